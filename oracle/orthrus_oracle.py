@@ -1,0 +1,248 @@
+"""Plain fp64 CPU oracle for one Orthrus dual-view decode step.
+
+TEST INFRASTRUCTURE ONLY.  This module is the slow, obviously correct
+definition that the HIP kernels are checked against.  Only the test suite,
+the smoke check and the benchmark's CPU-baseline leg may import it; the
+product path never does, and this module imports nothing from the product
+package (it shares no code, tables or helpers with it).
+
+Source of the definitions: the explainer page for "Orthrus: Memory-Efficient
+Parallel Token Generation via Dual-View Diffusion" (gist.science, arXiv
+2605.12825), technical summary:
+
+* §2.1 -- the frozen AR head and the diffusion head both read ONE shared
+  cache of AR keys/values (K_AR, V_AR); there is no second cache.
+* §2.2 -- the diffusion view's block mask M_diff: (rule 1) every position in
+  the block attends to the clean AR context that precedes the block anchor;
+  (rule 2) positions inside the same block attend to each other in both
+  directions.
+* §2.3 -- inference: the diffusion head projects K candidates from
+  [anchor, K-1 masks] in one pass; the frozen AR head then sees the filled
+  block and computes exact targets for all K positions in one (causal) pass;
+  drafts are accepted strictly left to right while they equal the AR greedy
+  prediction; at the first divergence j the prefix up to j-1 is committed
+  together with the AR correction token, and the cache is truncated to the
+  committed positions.
+
+Everything is written as the definition, in fp64, with numpy primitives
+(fancy indexing, matmul, exp) as steps and no blocking or fusion.
+
+Readings of points the pages leave open (each one is listed in the design doc):
+
+* rows of the two views are aligned by position: row i of either view is the
+  prediction for the token after block position i; drafts[i] is compared
+  with argmax(ar_logits[i]);
+* accept_len a counts accepted drafts (0..K); the step commits
+  n = min(a + 1, K) tokens (the correction exists only on a divergence; with
+  a == K no bonus token exists because no AR row past K-1 is computed);
+* next_token = g[min(a, K - 1)], the last committed token (next anchor);
+* the appended K/V are the AR verify pass's block rows 0..n-1 (anchor plus
+  accepted drafts), written at cache positions L .. L+n-1;
+* grouped-query attention maps query head h to KV head h * Hkv // Hq; the
+  softmax scale defaults to 1/sqrt(D); no soft-cap, window or bias;
+* argmax ties go to the lowest index; -0.0 equals +0.0 (IEEE compare).
+
+Pins: every function here is pinned in tests/test_oracle_pins.py against
+closed forms, invariants and brute force (see each docstring).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+DIFF_BIDIR = 0
+AR_CAUSAL = 1
+
+
+def _f64(x):
+    """Exact widening to fp64 (bf16/fp16/fp32 all embed exactly in fp64)."""
+    if hasattr(x, "detach"):  # a torch tensor: go through float32 exactly
+        x = x.detach().cpu()
+        if str(x.dtype) in ("torch.bfloat16", "torch.float16"):
+            x = x.float()
+        x = x.numpy()
+    return np.asarray(x, dtype=np.float64)
+
+
+def _i64(x):
+    if hasattr(x, "detach"):
+        x = x.detach().cpu().numpy()
+    return np.asarray(x, dtype=np.int64)
+
+
+def _raw(x):
+    """Element storage as numpy without any value conversion (bf16 tensors
+    are viewed as their int16 bit patterns), for bit-exact copies."""
+    if hasattr(x, "detach"):
+        x = x.detach().cpu()
+        if str(x.dtype) in ("torch.bfloat16", "torch.float16"):
+            import torch
+            x = x.view(torch.int16)
+        x = x.numpy()
+    return np.asarray(x)
+
+
+def gather_context(cache, page_table_row, n_tokens, kv_head, page_size):
+    """The cached key (or value) rows of one sequence and one KV head.
+
+    Cache layout [num_pages, Hkv, P, D]; logical position p of the sequence
+    lives in physical page page_table_row[p // P], slot p % P.  Returns the
+    [n_tokens, D] fp64 rows in logical order.
+    """
+    n_pages = -(-n_tokens // page_size)
+    pages = _i64(page_table_row)[:n_pages]
+    if hasattr(cache, "detach"):                  # index before widening a large cache
+        import torch
+        rows = _f64(cache[torch.as_tensor(pages, device=cache.device), kv_head])
+    else:
+        rows = _f64(np.asarray(cache)[pages, kv_head])   # [n_pages, P, D]
+    return rows.reshape(n_pages * page_size, rows.shape[-1])[:n_tokens]
+
+
+def visible_keys(mode, L, K, i):
+    """Logical key positions visible to block row i (0-based) of a block of K
+    rows placed after L cached tokens.
+
+    Cached context 0..L-1 is always visible (§2.2 rule 1).  Block key L+j is
+    visible for every j < K in DIFF_BIDIR (§2.2 rule 2, bidirectional block),
+    and only for j <= i in AR_CAUSAL (§2.3, the AR head's causal verify pass).
+    """
+    if mode == DIFF_BIDIR:
+        blk = list(range(K))
+    elif mode == AR_CAUSAL:
+        blk = list(range(i + 1))
+    else:
+        raise ValueError("mode must be DIFF_BIDIR or AR_CAUSAL")
+    return list(range(L)) + [L + j for j in blk]
+
+
+def block_attn(q, k_cache, v_cache, k_blk, v_blk, page_table, ctx_lens, mode,
+               softmax_scale=None, page_size=16, batches=None, heads=None):
+    """Block attention of one decode step over the shared paged KV cache.
+
+    Shapes: q [B, K, Hq, D]; k_cache/v_cache [num_pages, Hkv, P, D];
+    k_blk/v_blk [B, K, Hkv, D]; page_table [B, max_pages]; ctx_lens [B].
+    Returns fp64 [B, K, Hq, D]; rows/heads outside `batches`/`heads` (when
+    given) are left NaN.
+
+    For sequence b, query head h (KV head g = h*Hkv//Hq) and block row i:
+    keys are the L cached keys followed by the K block keys, the visible set
+    is visible_keys(mode, L, K, i), scores s_p = scale * <q, k_p>, and the
+    output is sum_p softmax(s)_p v_p over the visible set.  Every visible set
+    holds at least the row's own block key, so no softmax is empty.
+    """
+    q = _f64(q)
+    kb = _f64(k_blk)
+    vb = _f64(v_blk)
+    pt = _i64(page_table)
+    lens = _i64(ctx_lens)
+    B, K, Hq, D = q.shape
+    Hkv = kb.shape[2]
+    scale = 1.0 / np.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    out = np.full((B, K, Hq, D), np.nan)
+    for b in (range(B) if batches is None else batches):
+        L = int(lens[b])
+        ctx = {}
+        for h in (range(Hq) if heads is None else heads):
+            g = h * Hkv // Hq
+            if g not in ctx:
+                ctx[g] = (gather_context(k_cache, pt[b], L, g, page_size),
+                          gather_context(v_cache, pt[b], L, g, page_size))
+            keys_c, vals_c = ctx[g]
+            # scores of every block row against the cached keys and the block keys
+            s_c = scale * (keys_c @ q[b, :, h].T)           # [L, K]
+            s_b = scale * (kb[b, :, g] @ q[b, :, h].T)      # [K(keys), K(rows)]
+            for i in range(K):
+                vis_b = [p - L for p in visible_keys(mode, L, K, i) if p >= L]
+                s = np.concatenate([s_c[:, i], s_b[vis_b, i]])
+                w = np.exp(s - s.max())
+                num = w[:L] @ vals_c + w[L:] @ vb[b, vis_b, g]
+                out[b, i, h] = num / w.sum()
+    return out
+
+
+def greedy_argmax(logits):
+    """g[..., ] = the lowest vocabulary index attaining the row maximum.
+
+    The AR head's greedy prediction per block position (§2.3 "greedy
+    prediction"); ties resolve to the lowest index.  Written as its
+    definition: find the maximum, then the first position equal to it.
+    """
+    x = _f64(logits)
+    flat = x.reshape(-1, x.shape[-1])
+    g = np.empty(flat.shape[0], dtype=np.int64)
+    for r in range(flat.shape[0]):
+        m = flat[r].max()
+        g[r] = np.flatnonzero(flat[r] == m)[0]
+    return g.reshape(x.shape[:-1])
+
+
+def accept_prefix(draft_row, g_row):
+    """Number of leading positions where the draft equals the AR greedy token
+    (strict left-to-right evaluation, §2.3)."""
+    a = 0
+    for d, t in zip(draft_row, g_row):
+        if int(d) != int(t):
+            break
+        a += 1
+    return a
+
+
+def greedy_accept(ar_logits, draft_tokens):
+    """Greedy consensus of one step.
+
+    Returns (accept_len [B], next_token [B], g [B, K]) with
+    accept_len = accepted drafts a in [0, K] and next_token = g[min(a, K-1)],
+    the AR correction token on a divergence (or the last accepted token when
+    all K agree).  The committed tokens of the step are g[0 .. n-1] with
+    n = commit_count(a, K).
+    """
+    g = greedy_argmax(ar_logits)
+    drafts = _i64(draft_tokens)
+    B, K = g.shape
+    acc = np.array([accept_prefix(drafts[b], g[b]) for b in range(B)], dtype=np.int64)
+    nxt = np.array([g[b, min(acc[b], K - 1)] for b in range(B)], dtype=np.int64)
+    return acc, nxt, g
+
+
+def commit_count(accept_len, K):
+    """Tokens committed by one step: the accepted prefix plus the correction
+    token, capped at the block size (§2.3)."""
+    return min(int(accept_len) + 1, K)
+
+
+def kv_append(k_cache, v_cache, k_blk, v_blk, page_table, ctx_lens, accept_len, page_size=16):
+    """Commit the accepted block rows into the shared cache.
+
+    Rows r < n = commit_count(a_b, K) of the AR pass's block K/V go to
+    logical position L_b + r, i.e. physical page page_table[b][(L_b+r)//P],
+    slot (L_b+r) % P, for every KV head.  Nothing else in the cache changes
+    (the cache is "truncated" to the committed positions, §2.3).
+
+    Returns (k_cache', v_cache', new_ctx_lens [B], slots [B, K]) where the
+    caches are fresh numpy copies of the element storage (bf16 as int16 bit
+    patterns), new_ctx_lens = L + n, and
+    slots[b, r] = page * P + slot for the written rows and -1 otherwise.
+    """
+    kc = _raw(k_cache).copy()
+    vc = _raw(v_cache).copy()
+    kb = _raw(k_blk)
+    vb = _raw(v_blk)
+    pt = _i64(page_table)
+    lens = _i64(ctx_lens)
+    acc = _i64(accept_len)
+    B, K = kb.shape[0], kb.shape[1]
+    slots = np.full((B, K), -1, dtype=np.int64)
+    new_lens = np.empty(B, dtype=np.int64)
+    for b in range(B):
+        L = int(lens[b])
+        n = commit_count(acc[b], K)
+        for r in range(n):
+            pos = L + r
+            page = int(pt[b, pos // page_size])
+            slot = pos % page_size
+            kc[page, :, slot, :] = kb[b, r]
+            vc[page, :, slot, :] = vb[b, r]
+            slots[b, r] = page * page_size + slot
+        new_lens[b] = L + n
+    return kc, vc, new_lens, slots

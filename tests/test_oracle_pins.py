@@ -1,0 +1,514 @@
+"""Pins of the CPU oracle to facts fixed by the pages and by mathematics.
+
+None of these compares the oracle with itself: each check is a closed form,
+an invariant of the definition, a hand-built case with a known answer, or a
+brute force written along a different route (explicit dense mask, contiguous
+unpaged keys, library softmax).  Each is chosen so that a plausible mistake
+in the oracle (a dropped term, a wrong sign, index, page or mask, a
+transposed operand) fails at least one of them.
+
+Passages: the Orthrus explainer (gist.science, arXiv 2605.12825), technical
+summary §2.1 (one shared KV cache), §2.2 (M_diff: causal context +
+bidirectional block), §2.3 (single causal verify pass, greedy left-to-right
+consensus, correction token, cache truncation), §3/§4 (lossless output,
+acceptance length 11.7); the agentlenshq summary (K = 32, O(1) ~ 4.5 MiB KV
+overhead).
+"""
+
+import itertools
+import math
+
+import numpy as np
+import pytest
+from scipy.special import softmax
+
+from oracle import orthrus_oracle as O
+
+DIFF, AR = O.DIFF_BIDIR, O.AR_CAUSAL
+
+
+def contiguous_case(rng, B, K, Hq, Hkv, D, lens, P=16, shuffle=True):
+    """Random fp64 inputs in the paged layout plus the same keys/values as
+    contiguous per-sequence arrays built position by position."""
+    need = [-(-(L + K) // P) for L in lens]
+    total = sum(need)
+    perm = rng.permutation(total) if shuffle else np.arange(total)
+    pt = np.full((B, max(need)), -1, dtype=np.int64)
+    pos = 0
+    for b, n in enumerate(need):
+        pt[b, :n] = perm[pos:pos + n]
+        pos += n
+    kc = rng.standard_normal((total, Hkv, P, D))
+    vc = rng.standard_normal((total, Hkv, P, D))
+    q = rng.standard_normal((B, K, Hq, D))
+    kb = rng.standard_normal((B, K, Hkv, D))
+    vb = rng.standard_normal((B, K, Hkv, D))
+    return q, kc, vc, kb, vb, pt, np.array(lens)
+
+
+def brute_force(q, kc, vc, kb, vb, pt, lens, mode, scale=None, P=16):
+    """Dense reference: contiguous [L+K, D] keys copied slot by slot, an
+    explicit [K, L+K] additive 0/-inf mask, scipy softmax, one matmul."""
+    B, K, Hq, D = q.shape
+    Hkv = kb.shape[2]
+    sc = 1 / math.sqrt(D) if scale is None else scale
+    out = np.zeros(q.shape)
+    for b in range(B):
+        L = int(lens[b])
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            keys = np.zeros((L + K, D))
+            vals = np.zeros((L + K, D))
+            for p in range(L):
+                keys[p] = kc[pt[b, p // P], g, p % P]
+                vals[p] = vc[pt[b, p // P], g, p % P]
+            for j in range(K):
+                keys[L + j] = kb[b, j, g]
+                vals[L + j] = vb[b, j, g]
+            mask = np.zeros((K, L + K))
+            if mode == AR:
+                for i in range(K):
+                    mask[i, L + i + 1:] = -np.inf
+            s = sc * (q[b, :, h, :] @ keys.T) + mask
+            out[b, :, h, :] = softmax(s, axis=1) @ vals
+    return out
+
+
+# ---------------------------------------------------------------------------
+# block attention
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", [DIFF, AR])
+@pytest.mark.parametrize("lens,K,Hq,Hkv,D", [
+    ([0], 4, 2, 1, 8), ([1], 8, 4, 1, 16), ([15, 17], 5, 4, 2, 8), ([33, 64, 7], 8, 8, 2, 16),
+    ([16], 1, 2, 2, 4), ([40], 8, 4, 4, 8)])
+def test_brute_force_agrees(mode, lens, K, Hq, Hkv, D):
+    """P-6: dense explicit-mask brute force on tiny sizes agrees to 1e-12."""
+    rng = np.random.default_rng(hash((mode, tuple(lens), K, Hq)) % 2**32)
+    args = contiguous_case(rng, len(lens), K, Hq, Hkv, D, lens)
+    got = O.block_attn(*args, mode)
+    ref = brute_force(*args, mode)
+    assert np.max(np.abs(got - ref)) < 1e-12
+
+
+def test_two_key_closed_form():
+    """P-1 and the default scale: K = 1 after one cached token is a two-key
+    softmax, out = v0*sigmoid(s0-s1) + v1*sigmoid(s1-s0), s = <q,k>/sqrt(D)."""
+    D = 4
+    q = np.zeros((1, 1, 1, D)); q[0, 0, 0, 0] = 3.0
+    kc = np.zeros((1, 1, 16, D)); kc[0, 0, 0, 0] = 1.0          # s0 = 3 * 1 / 2 = 1.5
+    vc = np.zeros((1, 1, 16, D)); vc[0, 0, 0] = [1.0, -2.0, 0.5, 4.0]
+    kb = np.zeros((1, 1, 1, D)); kb[0, 0, 0, 0] = -0.5          # s1 = 3 * -0.5 / 2 = -0.75
+    vb = np.zeros((1, 1, 1, D)); vb[0, 0, 0] = [0.0, 2.0, -1.0, 8.0]
+    pt = np.zeros((1, 1), dtype=np.int64)
+    sig = lambda x: 1 / (1 + math.exp(-x))
+    expect = vc[0, 0, 0] * sig(1.5 - (-0.75)) + vb[0, 0, 0] * sig(-0.75 - 1.5)
+    for mode in (DIFF, AR):
+        got = O.block_attn(q, kc, vc, kb, vb, pt, [1], mode)[0, 0, 0]
+        assert np.max(np.abs(got - expect)) < 1e-14
+
+
+def test_k1_modes_identical():
+    """P-1: with K = 1 both masks see the same keys (ordinary causal decode)."""
+    rng = np.random.default_rng(1)
+    args = contiguous_case(rng, 2, 1, 4, 2, 16, [37, 64])
+    a = O.block_attn(*args, DIFF)
+    b = O.block_attn(*args, AR)
+    assert np.array_equal(a, b)
+
+
+def test_ar_is_the_sequential_decode_chain():
+    """P-2: the AR verify pass equals K one-token decode steps: row i is
+    ordinary decode at context L+i with block rows < i already cached."""
+    rng = np.random.default_rng(2)
+    K, Hq, Hkv, D, L = 6, 4, 2, 8, 21
+    q, kc, vc, kb, vb, pt, lens = contiguous_case(rng, 1, K, Hq, Hkv, D, [L])
+    full = O.block_attn(q, kc, vc, kb, vb, pt, lens, AR)
+    for i in range(K):
+        # a cache holding positions 0..L+i-1 (block rows < i written by hand)
+        P = 16
+        n_pages = -(-(L + i + 1) // P)
+        kc2 = np.zeros((n_pages, Hkv, P, D)); vc2 = np.zeros((n_pages, Hkv, P, D))
+        for p in range(L + i):
+            src_k = kc[pt[0, p // P], :, p % P] if p < L else kb[0, p - L]
+            src_v = vc[pt[0, p // P], :, p % P] if p < L else vb[0, p - L]
+            kc2[p // P, :, p % P] = src_k
+            vc2[p // P, :, p % P] = src_v
+        pt2 = np.arange(n_pages)[None]
+        one = O.block_attn(q[:, i:i + 1], kc2, vc2, kb[:, i:i + 1], vb[:, i:i + 1], pt2, [L + i], AR)
+        assert np.max(np.abs(one[0, 0] - full[0, i])) < 1e-12
+
+
+def test_last_row_same_in_both_modes():
+    """P-3: the last block row sees the whole block in both views."""
+    rng = np.random.default_rng(3)
+    args = contiguous_case(rng, 2, 8, 4, 1, 8, [5, 30])
+    a = O.block_attn(*args, DIFF)
+    b = O.block_attn(*args, AR)
+    assert np.max(np.abs(a[:, -1] - b[:, -1])) < 1e-15
+    assert np.max(np.abs(a[:, 0] - b[:, 0])) > 1e-3   # and the first row differs
+
+
+def test_diff_permutation_equivariance():
+    """P-4: in DIFF_BIDIR, permuting the block positions (q, k_blk, v_blk
+    jointly) permutes the outputs (§2.2 rule 2 is order-free)."""
+    rng = np.random.default_rng(4)
+    q, kc, vc, kb, vb, pt, lens = contiguous_case(rng, 2, 8, 4, 2, 8, [19, 3])
+    perm = rng.permutation(8)
+    a = O.block_attn(q, kc, vc, kb, vb, pt, lens, DIFF)
+    b = O.block_attn(q[:, perm], kc, vc, kb[:, perm], vb[:, perm], pt, lens, DIFF)
+    assert np.max(np.abs(a[:, perm] - b)) < 1e-13
+    # the causal view is not equivariant (guards against a mask that ignores mode)
+    c = O.block_attn(q, kc, vc, kb, vb, pt, lens, AR)
+    d = O.block_attn(q[:, perm], kc, vc, kb[:, perm], vb[:, perm], pt, lens, AR)
+    assert np.max(np.abs(c[:, perm] - d)) > 1e-3
+
+
+def test_identical_keys_uniform_mean():
+    """P-5: identical keys make every visible key equally weighted: DIFF rows
+    are the mean of all L+K values, AR row i the mean of the first L+i+1."""
+    rng = np.random.default_rng(5)
+    K, Hq, Hkv, D, L = 7, 2, 1, 8, 23
+    q, kc, vc, kb, vb, pt, lens = contiguous_case(rng, 1, K, Hq, Hkv, D, [L])
+    key = rng.standard_normal(D)
+    kc[:] = key
+    kb[:] = key
+    ctx_vals = [vc[pt[0, p // 16], 0, p % 16] for p in range(L)]
+    blk_vals = [vb[0, j, 0] for j in range(K)]
+    diff = O.block_attn(q, kc, vc, kb, vb, pt, lens, DIFF)
+    ar = O.block_attn(q, kc, vc, kb, vb, pt, lens, AR)
+    all_mean = np.mean(ctx_vals + blk_vals, axis=0)
+    for i in range(K):
+        for h in range(Hq):
+            assert np.max(np.abs(diff[0, i, h] - all_mean)) < 1e-13
+            assert np.max(np.abs(ar[0, i, h] - np.mean(ctx_vals + blk_vals[:i + 1], axis=0))) < 1e-13
+
+
+def test_sharp_scores_pick_the_designed_key():
+    """A query aligned with one key by a large margin returns that key's
+    value: checks page/slot addressing, block placement and the AR mask."""
+    rng = np.random.default_rng(6)
+    K, Hq, Hkv, D, L = 8, 2, 1, 64, 45
+    q, kc, vc, kb, vb, pt, lens = contiguous_case(rng, 1, K, Hq, Hkv, D, [L])
+    # orthonormal keys: every logical position gets its own basis direction
+    basis = np.linalg.qr(rng.standard_normal((D, D)))[0]
+    n_pos = L + K
+    assert n_pos <= D
+    dirs = [basis[p] for p in range(n_pos)]
+    for p in range(L):
+        kc[pt[0, p // 16], 0, p % 16] = dirs[p]
+    for j in range(K):
+        kb[0, j, 0] = dirs[L + j]
+    targets = {0: 3, 1: 17, 2: L - 1, 3: L + 2, 4: L + 6, 5: 31, 6: L + 6, 7: L}
+    for i, p in targets.items():
+        for h in range(Hq):
+            q[0, i, h] = 400.0 * dirs[p] / np.dot(dirs[p], dirs[p])
+    value = lambda p: vc[pt[0, p // 16], 0, p % 16] if p < L else vb[0, p - L, 0]
+    diff = O.block_attn(q, kc, vc, kb, vb, pt, lens, DIFF, softmax_scale=1.0)
+    ar = O.block_attn(q, kc, vc, kb, vb, pt, lens, AR, softmax_scale=1.0)
+    for i, p in targets.items():
+        for h in range(Hq):
+            assert np.max(np.abs(diff[0, i, h] - value(p))) < 1e-6
+            if p < L + i + 1:      # visible to the causal row
+                assert np.max(np.abs(ar[0, i, h] - value(p))) < 1e-6
+            else:                  # hidden from row i: the causal output must not be it
+                assert np.max(np.abs(ar[0, i, h] - value(p))) > 1e-2
+
+
+def test_page_permutation_invariance():
+    """P-7: relabelling physical pages (cache and table together) leaves the
+    output bit-identical."""
+    rng = np.random.default_rng(7)
+    q, kc, vc, kb, vb, pt, lens = contiguous_case(rng, 2, 4, 4, 2, 8, [50, 17])
+    a = O.block_attn(q, kc, vc, kb, vb, pt, lens, AR)
+    relabel = rng.permutation(kc.shape[0])        # new id of old page x is relabel[x]
+    kc2 = np.empty_like(kc); vc2 = np.empty_like(vc)
+    kc2[relabel] = kc; vc2[relabel] = vc
+    pt2 = np.where(pt >= 0, relabel[np.maximum(pt, 0)], -1)
+    b = O.block_attn(q, kc2, vc2, kb, vb, pt2, lens, AR)
+    assert np.array_equal(a, b)
+
+
+def test_convexity():
+    """P-8: outputs are convex combinations of the visible values."""
+    rng = np.random.default_rng(8)
+    K, L = 6, 13
+    q, kc, vc, kb, vb, pt, lens = contiguous_case(rng, 1, K, 2, 1, 8, [L])
+    ar = O.block_attn(q * 3, kc, vc, kb, vb, pt, lens, AR)
+    ctx_vals = np.array([vc[pt[0, p // 16], 0, p % 16] for p in range(L)])
+    for i in range(K):
+        vis = np.concatenate([ctx_vals, vb[0, :i + 1, 0]])
+        assert np.all(ar[0, i] <= vis.max(0) + 1e-12) and np.all(ar[0, i] >= vis.min(0) - 1e-12)
+
+
+def test_gqa_head_mapping():
+    """Query head h reads KV head h*Hkv//Hq: with each KV head's values set
+    to a constant equal to its index, head h returns exactly that index."""
+    rng = np.random.default_rng(9)
+    Hq, Hkv = 8, 2
+    q, kc, vc, kb, vb, pt, lens = contiguous_case(rng, 1, 4, Hq, Hkv, 8, [20])
+    for g in range(Hkv):
+        vc[:, g] = g + 1.0
+        vb[:, :, g] = g + 1.0
+    out = O.block_attn(q, kc, vc, kb, vb, pt, lens, DIFF)
+    for h in range(Hq):
+        assert np.allclose(out[0, :, h], h // (Hq // Hkv) + 1.0, atol=1e-13, rtol=0)
+
+
+def test_empty_context_block_only():
+    """L = 0: the rows attend to block keys only; AR row 0 is its own value."""
+    rng = np.random.default_rng(10)
+    q, kc, vc, kb, vb, pt, lens = contiguous_case(rng, 1, 4, 2, 1, 8, [0])
+    ar = O.block_attn(q, kc, vc, kb, vb, pt, lens, AR)
+    assert np.max(np.abs(ar[0, 0, 0] - vb[0, 0, 0])) < 1e-15
+
+
+# ---------------------------------------------------------------------------
+# greedy argmax and acceptance
+# ---------------------------------------------------------------------------
+
+def test_argmax_planted_cases():
+    """P-9: ties go to the lowest index; -0.0 ties with +0.0; -inf rows give
+    index 0; maxima at the first and last index."""
+    V = 37
+    rows, expect = [], []
+    r = -np.ones(V); r[9] = 5; r[21] = 5; r[30] = 5; rows.append(r); expect.append(9)
+    r = -np.ones(V); r[0] = 2; rows.append(r); expect.append(0)
+    r = -np.ones(V); r[V - 1] = 2; rows.append(r); expect.append(V - 1)
+    r = -np.ones(V); r[3] = 0.0; r[5] = -0.0; rows.append(r); expect.append(3)
+    r = -np.ones(V); r[2] = -0.0; r[7] = 0.0; rows.append(r); expect.append(2)
+    r = np.full(V, -np.inf); rows.append(r); expect.append(0)
+    r = np.full(V, -np.inf); r[11] = -1e30; rows.append(r); expect.append(11)
+    r = np.zeros(V); rows.append(r); expect.append(0)
+    x = np.array(rows, dtype=np.float32)[None]
+    assert list(O.greedy_argmax(x)[0]) == expect
+
+
+def test_argmax_brute_force_integer_logits():
+    """Lowest index v with x_v >= x_u for all u, by exhaustive comparison, on
+    small-integer logits full of ties."""
+    rng = np.random.default_rng(11)
+    x = rng.integers(-3, 3, size=(5, 7, 19)).astype(np.float32)
+    g = O.greedy_argmax(x)
+    for b in range(5):
+        for i in range(7):
+            row = list(x[b, i])
+            first = next(v for v in range(19) if all(row[v] >= u for u in row))
+            assert g[b, i] == first
+
+
+def test_accept_all_and_none():
+    """P-10: a draft equal to the AR greedy tokens accepts all K (n = K,
+    next = g[K-1]); a first-position miss accepts 0 and commits the AR
+    correction token g[0] (n = 1)."""
+    rng = np.random.default_rng(12)
+    K, V = 32, 50
+    logits = rng.standard_normal((2, K, V))
+    g = O.greedy_argmax(logits)
+    drafts = g.copy()
+    drafts[1, 0] = (g[1, 0] + 1) % V
+    acc, nxt, gg = O.greedy_accept(logits, drafts)
+    assert list(acc) == [K, 0]
+    assert nxt[0] == g[0, K - 1] and nxt[1] == g[1, 0]
+    assert O.commit_count(acc[0], K) == K and O.commit_count(acc[1], K) == 1
+
+
+def test_accept_exhaustive_tiny_vocab():
+    """All 3^3 drafts over a 3-token vocabulary against a fixed greedy row:
+    a is the length of the longest common prefix, n = min(a+1, K) >= 1 and
+    the committed tokens are the AR tokens g[0..n-1], which equal the
+    accepted drafts followed by the correction."""
+    V, K = 3, 3
+    logits = np.array([[[0.1, 0.9, 0.0], [2.0, 1.0, 2.0], [0.0, 0.0, 1.0]]])
+    g = [1, 0, 2]
+    for d in itertools.product(range(V), repeat=K):
+        acc, nxt, gg = O.greedy_accept(logits, np.array([d]))
+        lcp = 0
+        while lcp < K and d[lcp] == g[lcp]:
+            lcp += 1
+        assert list(gg[0]) == g
+        assert acc[0] == lcp
+        n = O.commit_count(acc[0], K)
+        assert n == min(lcp + 1, K) and n >= 1
+        committed = list(d[:lcp]) + ([g[lcp]] if lcp < K else [])
+        assert committed[:n] == g[:n] and nxt[0] == g[n - 1]
+
+
+def test_tiny_workload_accepts_twelve():
+    """The tiny fp32 workload's drafts agree with the AR greedy tokens on the
+    first 12 positions: 12 accepted, 13 committed, next = g[12]."""
+    from diffusion_drafted_verification_amd import inputs as I
+    logits, _ = I.make_logits(1, 32, 1024, seed=0, workload="tiny_fp32")
+    g = O.greedy_argmax(logits.numpy())
+    drafts = I.make_drafts(g, [12], 1024, seed=0, workload="tiny_fp32")
+    acc, nxt, _ = O.greedy_accept(logits.numpy(), drafts.numpy())
+    assert acc[0] == 12 and nxt[0] == g[0, 12] and O.commit_count(acc[0], 32) == 13
+
+
+# ---------------------------------------------------------------------------
+# KV append
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("L,a", [(0, 0), (15, 0), (15, 3), (16, 31), (31, 32), (47, 5)])
+def test_append_writes_exactly_the_committed_rows(L, a):
+    """P-11: n = min(a+1, K) rows land at positions L..L+n-1 (hand-computed
+    page/slot), bit-exact; every other cache entry keeps its sentinel."""
+    K, Hkv, D, P = 32, 2, 4, 16
+    n_pages = 6
+    pt = np.array([[4, 0, 5, 2, 1, 3]])                    # a scrambled table
+    kc = np.full((n_pages, Hkv, P, D), -7, dtype=np.int16)
+    vc = np.full((n_pages, Hkv, P, D), -9, dtype=np.int16)
+    rng = np.random.default_rng(L * 100 + a)
+    kb = rng.integers(0, 1000, size=(1, K, Hkv, D)).astype(np.int16)
+    vb = rng.integers(0, 1000, size=(1, K, Hkv, D)).astype(np.int16)
+    kc2, vc2, new_lens, slots = O.kv_append(kc, vc, kb, vb, pt, [L], [a])
+    n = min(a + 1, K)
+    assert new_lens[0] == L + n
+    changed = set()
+    for r in range(n):
+        pos = L + r
+        page, slot = [4, 0, 5, 2, 1, 3][pos // 16], pos % 16
+        assert slots[0, r] == page * 16 + slot
+        assert np.array_equal(kc2[page, :, slot], kb[0, r]) and np.array_equal(vc2[page, :, slot], vb[0, r])
+        changed.add((page, slot))
+    assert np.all(slots[0, n:] == -1)
+    for page in range(n_pages):
+        for slot in range(P):
+            if (page, slot) not in changed:
+                assert np.all(kc2[page, :, slot] == -7) and np.all(vc2[page, :, slot] == -9)
+
+
+# ---------------------------------------------------------------------------
+# the whole loop: losslessness (§3/§4: same tokens as plain greedy AR)
+# ---------------------------------------------------------------------------
+
+class ToyModel:
+    """One-layer fp64 toy language model used only to exercise the decode
+    loop: token + position embeddings, GQA attention through the oracle's
+    block_attn over a paged cache, output projection to V logits."""
+
+    def __init__(self, seed=0, V=64, dm=16, Hq=2, Hkv=1, D=8, P=16, max_pos=256):
+        r = np.random.default_rng(seed)
+        self.V, self.Hq, self.Hkv, self.D, self.P = V, Hq, Hkv, D, P
+        self.emb = r.standard_normal((V, dm))
+        self.pos = r.standard_normal((max_pos, dm)) * 0.5
+        self.wq = r.standard_normal((Hq, dm, D))
+        self.wk = r.standard_normal((Hkv, dm, D))
+        self.wv = r.standard_normal((Hkv, dm, D))
+        self.wo = r.standard_normal((Hq * D, V))
+        self.wu = r.standard_normal((dm, V))
+        self.mask_token = V - 1
+
+    def qkv(self, tokens, start):
+        x = np.array([self.emb[t] + self.pos[start + i] for i, t in enumerate(tokens)])
+        q = np.einsum("td,hde->the", x, self.wq)[None]
+        k = np.einsum("td,hde->the", x, self.wk)[None]
+        v = np.einsum("td,hde->the", x, self.wv)[None]
+        return x, q, k, v
+
+    def logits(self, x, attn):
+        return (attn.reshape(attn.shape[1], -1) @ self.wo + x @ self.wu)[None]
+
+    def new_cache(self, n_pages):
+        z = np.zeros((n_pages, self.Hkv, self.P, self.D))
+        return z, z.copy(), np.random.default_rng(1).permutation(n_pages)[None]
+
+
+def prefill(m, prompt, kc, vc, pt):
+    """Write the prompt's K/V one token at a time (K = 1 steps); returns the
+    context length and the last prompt token (the first anchor)."""
+    L = 0
+    for t in prompt[:-1]:
+        _, q, k, v = m.qkv([t], L)
+        kc, vc, nl, _ = O.kv_append(kc, vc, k, v, pt, [L], [0])
+        L = int(nl[0])
+    return L, prompt[-1], kc, vc
+
+
+def plain_greedy(m, prompt, n_new):
+    kc, vc, pt = m.new_cache(32)
+    L, anchor, kc, vc = prefill(m, prompt, kc, vc, pt)
+    out = []
+    while len(out) < n_new:
+        x, q, k, v = m.qkv([anchor], L)
+        att = O.block_attn(q, kc, vc, k, v, pt, [L], AR)
+        tok = int(O.greedy_argmax(m.logits(x, att))[0, 0])
+        kc, vc, nl, _ = O.kv_append(kc, vc, k, v, pt, [L], [0])
+        L, anchor = int(nl[0]), tok
+        out.append(tok)
+    return out
+
+
+def dual_view(m, prompt, n_new, K, drafter):
+    kc, vc, pt = m.new_cache(32)
+    L, anchor, kc, vc = prefill(m, prompt, kc, vc, pt)
+    out, steps = [], 0
+    while len(out) < n_new:
+        drafts = drafter(m, anchor, L, kc, vc, pt, K, len(out))
+        block = [anchor] + list(drafts[:K - 1])                # the filled block
+        x, q, k, v = m.qkv(block, L)
+        att = O.block_attn(q, kc, vc, k, v, pt, [L], AR)        # one causal verify pass
+        acc, nxt, g = O.greedy_accept(m.logits(x, att), np.array([drafts]))
+        n = O.commit_count(acc[0], K)
+        out.extend(int(t) for t in g[0, :n])
+        kc, vc, nl, _ = O.kv_append(kc, vc, k, v, pt, [L], acc)
+        L, anchor = int(nl[0]), int(nxt[0])
+        steps += 1
+    return out[:n_new], steps
+
+
+@pytest.mark.parametrize("source", ["perfect", "random", "adversarial", "diffusion_view"])
+def test_dual_view_loop_is_lossless(source):
+    """P-12: whatever the drafts, the committed stream equals plain greedy
+    decoding token for token; perfect drafts commit K tokens per step."""
+    m = ToyModel(seed=3)
+    prompt = [5, 9, 2, 33, 7, 1, 12]
+    n_new, K = 40, 8
+    ref = plain_greedy(m, prompt, n_new + K)
+    rng = np.random.default_rng(4)
+
+    def drafter(m, anchor, L, kc, vc, pt, K, done):
+        if source == "perfect":
+            return ref[done:done + K]
+        if source == "random":
+            return list(rng.integers(0, m.V, size=K))
+        if source == "adversarial":
+            return [(t + 1) % m.V for t in ref[done:done + K]]
+        # the diffusion view: [anchor, K-1 masks] through the same toy layer
+        # with the bidirectional block mask, greedy per position
+        x, q, k, v = m.qkv([anchor] + [m.mask_token] * (K - 1), L)
+        att = O.block_attn(q, kc, vc, k, v, pt, [L], DIFF)
+        return list(O.greedy_argmax(m.logits(x, att))[0])
+
+    got, steps = dual_view(m, prompt, n_new, K, drafter)
+    assert got == ref[:n_new]
+    if source == "perfect":
+        assert steps == n_new // K
+    if source == "adversarial":
+        assert steps == n_new
+
+
+# ---------------------------------------------------------------------------
+# workload arithmetic
+# ---------------------------------------------------------------------------
+
+def test_block_kv_overhead_is_4p5_mib():
+    """P-13: one K = 32 block of bf16 K/V over Qwen3-8B's 36 layers (8 KV
+    heads, D 128) is 4,718,592 B = 4.5 MiB, the O(1) overhead the pages
+    quote: the block K/V is a transient K-row buffer, not a second cache."""
+    from diffusion_drafted_verification_amd import inputs as I
+    n = I.block_kv_bytes_per_step(32, 36, 8, 128, 2)
+    assert n == 4718592 == int(4.5 * 2**20)
+
+
+def test_step_accounting_geometric_prefix():
+    """P-14: every step commits >= 1 token; with the Geometric(mean 11.7)
+    agreement prefix capped at 32, the mean commit is 1 + 11.7 (1 - (11.7/
+    12.7)^31) = 11.78 within sampling error."""
+    from diffusion_drafted_verification_amd import inputs as I
+    a = I.geometric_prefix(40000, 32, seed=5)
+    n = np.minimum(a + 1, 32)
+    assert n.min() >= 1 and a.max() <= 32
+    expect = 1 + 11.7 * (1 - (11.7 / 12.7) ** 31)
+    assert abs(expect - 11.78) < 0.01
+    assert abs(n.mean() - expect) < 4 * n.std() / math.sqrt(len(n))
