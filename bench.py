@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark of one Orthrus dual-view decode step on one MI355X.
+
+Workload (Qwen3-8B attention shape, batch 1, 8192 cached tokens, K = 32):
+one decode step of the whole 36-layer model's hot path =
+  36 x block attention in the diffusion view (DIFF_BIDIR)
+  36 x block attention in the AR verify view (AR_CAUSAL)
+   1 x greedy accept over 32 x 151936 fp32 logits
+  36 x KV append of the accepted rows
+Every layer has its own synthetic paged K/V (N(0,1) bf16, shuffled 16-token
+pages), so each attention call reads its 32 MiB of KV cold (1.2 GB per view
+per step, several times the 256 MB Infinity Cache).  The step is captured once
+in a HIP graph and replayed; inputs are resident in HBM before timing starts.
+
+Output: one JSON line.  `value` = block-attention KV bytes read per step /
+step time (GB/s).  `roofline` = the block-attention call (main + combine
+kernels) timed alone with HIP events on its stream, against the 8 TB/s HBM
+peak.  `cpu_baseline` = the fp64 oracle on a bounded sample of the same step
+on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+METRIC = "block-attn KV-read GB/s (% of HBM peak), Qwen3-8B K=32 ctx 8k, bs 1–16"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--batch", type=int, default=1)
+    p.add_argument("--ctx", type=int, default=8192)
+    p.add_argument("--layers", type=int, default=36)
+    p.add_argument("--split-tokens", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-sweep", action="store_true")
+    p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a graph")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    return p.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+class Step:
+    """Buffers and calls of one decode step (all layers)."""
+
+    def __init__(self, ob, I, torch, batch, ctx, layers, split_tokens, seed=0):
+        self.ob, self.torch = ob, torch
+        d = torch.device("cuda:0")
+        w = I.WORKLOADS["qwen3_8b_8k"]
+        self.B, self.K, self.Hq, self.Hkv, self.D = batch, w["block_k"], w["n_q_heads"], w["n_kv_heads"], w["head_dim"]
+        self.layers, self.split = layers, split_tokens
+        lens = [ctx] * batch
+        table, n_pages = I.make_page_table(lens, self.K, 16, shuffle=True, seed=seed)
+        self.page_table = torch.from_numpy(table).to(d)
+        self.ctx_lens = torch.tensor(lens, dtype=torch.int32, device=d)
+        self.max_ctx = ctx
+        self.L = []
+        for l in range(layers):
+            a = I.make_attn_inputs("qwen3_8b_8k", seed=seed, layer=l, device=d, ctx_lens=lens, batch=batch)
+            q_ar = I._randn(a.q.shape, torch.bfloat16, d, I._seed(seed + 1, "qwen3_8b_8k", l, "q"))
+            kb_ar = I._randn(a.k_blk.shape, torch.bfloat16, d, I._seed(seed + 1, "qwen3_8b_8k", l, "k_blk"))
+            vb_ar = I._randn(a.v_blk.shape, torch.bfloat16, d, I._seed(seed + 1, "qwen3_8b_8k", l, "v_blk"))
+            self.L.append(dict(k_cache=a.k_cache, v_cache=a.v_cache, q_diff=a.q, kb_diff=a.k_blk, vb_diff=a.v_blk,
+                               q_ar=q_ar, kb_ar=kb_ar, vb_ar=vb_ar, out_diff=torch.empty_like(a.q),
+                               out_ar=torch.empty_like(a.q)))
+        self.logits, t = I.make_logits(batch, self.K, I.QWEN3_VOCAB, seed=seed, workload="qwen3_8b_8k", plant=True,
+                                       device=d)
+        self.prefix = I.geometric_prefix(batch, self.K, seed=seed, workload="qwen3_8b_8k")
+        self.drafts = I.make_drafts(t.cpu(), self.prefix, I.QWEN3_VOCAB, seed=seed).to(d)
+        self.new_ctx = torch.empty(batch, dtype=torch.int32, device=d)
+        self.kv_bytes_call = I.kv_bytes(lens, self.Hkv, self.D, 2)
+
+    def attn(self, l, mode):
+        x = self.L[l]
+        q, kb, vb, out = ((x["q_diff"], x["kb_diff"], x["vb_diff"], x["out_diff"]) if mode == self.ob.DIFF_BIDIR
+                          else (x["q_ar"], x["kb_ar"], x["vb_ar"], x["out_ar"]))
+        self.ob.block_attn(q, x["k_cache"], x["v_cache"], kb, vb, self.page_table, self.ctx_lens, mode, out,
+                           max_ctx_len=self.max_ctx, split_tokens=self.split)
+
+    def run(self):
+        ob = self.ob
+        for l in range(self.layers):
+            self.attn(l, ob.DIFF_BIDIR)
+        for l in range(self.layers):
+            self.attn(l, ob.AR_CAUSAL)
+        self.acc, self.nxt, self.tok = ob.greedy_accept(self.logits, self.drafts)
+        for l in range(self.layers):
+            x = self.L[l]
+            last = l == self.layers - 1
+            ob.kv_append(x["k_cache"], x["v_cache"], x["kb_ar"], x["vb_ar"], self.page_table, self.ctx_lens,
+                         self.acc, new_ctx_lens=self.new_ctx if last else None, want_outputs=last,
+                         max_ctx_len=self.max_ctx)
+
+
+def capture(torch, fn):
+    """Capture fn() in a HIP graph on a side stream (after one eager run so
+    workspaces exist); returns a replay callable."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g.replay
+
+
+def time_region(torch, fn, iters, warmup):
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(iters):
+        fn()
+    e1.record(st)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / iters  # ms
+
+
+def attn_only_ms(torch, step, mode, use_graph, iters=20, warmup=3):
+    """Average time of one block-attention call (main + combine kernels),
+    cycling through the layers so every call reads its KV cold."""
+    fn = lambda: [step.attn(l, mode) for l in range(step.layers)]
+    rep = capture(torch, fn) if use_graph else fn
+    return time_region(torch, rep, iters, warmup) / step.layers
+
+
+def cpu_baseline(step, I, seconds):
+    """The fp64 oracle, as is, on one layer of the step (both views, accept,
+    append) at the same shapes; repeated for about `seconds`."""
+    import numpy as np
+    from oracle import orthrus_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    x = step.L[0]
+    cpu = {k: v.cpu() for k, v in x.items()}
+    pt, cl = step.page_table.cpu(), step.ctx_lens.cpu()
+    logits, drafts = step.logits.cpu().numpy(), step.drafts.cpu().numpy()
+    reps, t0 = 0, time.perf_counter()
+    kv = 0
+    while True:
+        O.block_attn(cpu["q_diff"], cpu["k_cache"], cpu["v_cache"], cpu["kb_diff"], cpu["vb_diff"], pt, cl, O.DIFF_BIDIR)
+        O.block_attn(cpu["q_ar"], cpu["k_cache"], cpu["v_cache"], cpu["kb_ar"], cpu["vb_ar"], pt, cl, O.AR_CAUSAL)
+        acc, nxt, g = O.greedy_accept(logits, drafts)
+        O.kv_append(cpu["k_cache"], cpu["v_cache"], cpu["kb_ar"], cpu["vb_ar"], pt, cl, acc)
+        kv += 2 * step.kv_bytes_call
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(kv / el / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{reps} x one layer of the step (DIFF + AR block attention over {step.max_ctx} cached "
+                      f"tokens x B{step.B}, accept over 32x151936, append) in {el:.1f} s; "
+                      f"same shapes and inputs as the GPU step",
+            "s_per_layer_step": round(el / reps, 4)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1", "n_gpus": args.gpus}))
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    ROOT = os.path.dirname(os.path.abspath(__file__))
+    sys.path.insert(0, ROOT)
+    from diffusion_drafted_verification_amd import inputs as I
+    from diffusion_drafted_verification_amd import orthrus as ob
+    ob.lib()
+    use_graph = not args.no_graph
+
+    log("building inputs")
+    step = Step(ob, I, torch, args.batch, args.ctx, args.layers, args.split_tokens)
+    split = ob.lib().orthrus_block_attn_split_tokens(
+        ob.make_desc(step.L[0]["q_diff"], step.L[0]["k_cache"], step.page_table, step.max_ctx, None,
+                     args.split_tokens))
+    step.run()
+    torch.cuda.synchronize()
+    rep = capture(torch, step.run) if use_graph else step.run
+    log("timing step")
+    ms = time_region(torch, rep, args.steps, args.warmup)
+    kv_step = 2 * args.layers * step.kv_bytes_call
+    value = kv_step / (ms * 1e-3) / 1e9
+
+    log("timing attention calls")
+    ms_diff = attn_only_ms(torch, step, ob.DIFF_BIDIR, use_graph)
+    ms_ar = attn_only_ms(torch, step, ob.AR_CAUSAL, use_graph)
+    ms_call = 0.5 * (ms_diff + ms_ar)
+    achieved = step.kv_bytes_call / (ms_call * 1e-3) / 1e9
+    flops = 2 * 2 * step.B * step.K * step.Hq * step.D * (args.ctx + step.K)
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "block_attn call (attn_main + attn_combine)", "us_per_call": round(ms_call * 1e3, 3),
+            "us_diff": round(ms_diff * 1e3, 3), "us_ar": round(ms_ar * 1e3, 3),
+            "bytes_per_call": step.kv_bytes_call, "split_tokens": split,
+            "mfma_tflops": round(flops / (ms_call * 1e-3) / 1e12, 1)}
+
+    sweep = {}
+    if not args.no_sweep:
+        log("batch sweep")
+        del step
+        torch.cuda.empty_cache()
+        for bs in (1, 2, 4, 8, 16):
+            layers = max(2, math.ceil(1.0 * 2**30 / (bs * args.ctx * 4096)))
+            s2 = Step(ob, I, torch, bs, args.ctx, layers, 0, seed=1)
+            t = 0.5 * (attn_only_ms(torch, s2, ob.DIFF_BIDIR, use_graph, iters=10) +
+                       attn_only_ms(torch, s2, ob.AR_CAUSAL, use_graph, iters=10))
+            gbs = s2.kv_bytes_call / (t * 1e-3) / 1e9
+            sweep[f"bs{bs}"] = {"us_per_call": round(t * 1e3, 2), "kv_gbs": round(gbs, 1),
+                                "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+            del s2
+            torch.cuda.empty_cache()
+        step = None
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline")
+        s1 = step if step is not None else Step(ob, I, torch, args.batch, args.ctx, 1, args.split_tokens)
+        cpu = cpu_baseline(s1, I, args.cpu_seconds)
+
+    line = {"metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": f"qwen3_8b_8k step: B{args.batch} Hq32/Hkv8 D128 ctx{args.ctx} K32, "
+                                   f"{args.layers} layers x (DIFF_BIDIR + AR_CAUSAL) + accept(V=151936) + "
+                                   f"{args.layers} x kv_append",
+                       "batch": args.batch, "ctx": args.ctx, "block_k": 32, "layers": args.layers,
+                       "graph": use_graph, "parallelism": "none (1 GPU)"},
+            "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+            "roofline": roof, "cpu_baseline": cpu, "sweep": sweep or None}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

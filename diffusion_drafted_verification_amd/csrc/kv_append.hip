@@ -1,0 +1,125 @@
+// Commit of one Orthrus decode step on gfx950 (Orthrus explainer,
+// gist.science arXiv 2605.12825, technical summary §2.3: the cache keeps only
+// the committed positions).  The AR verify pass's block K/V rows
+// 0 .. n-1, n = min(accept_len + 1, K), are scattered into the paged cache at
+// logical positions ctx_len .. ctx_len + n - 1.  One work-group per
+// (sequence, block row); 16-byte copies of the Hkv x D row of K and of V.
+//
+// Also the library's plain streaming copy, used as a measurement probe.
+#include "orthrus_device.h"
+#include "orthrus_host.h"
+
+namespace orthrus {
+
+struct AppendArgs {
+  char* k_cache;
+  char* v_cache;
+  const char* k_blk;
+  const char* v_blk;
+  const int32_t* page_table;
+  const int32_t* ctx_lens;
+  const int32_t* accept_len;
+  int32_t* new_ctx_lens;
+  int32_t* slots;
+  int B, K, Hkv, max_pages, num_pages, max_ctx, row_bytes, head_bytes;
+};
+
+__global__ void __launch_bounds__(256) kv_append_kernel(AppendArgs a) {
+  const int b = blockIdx.x / a.K, r = blockIdx.x % a.K;
+  int L = a.ctx_lens[b];
+  L = L < 0 ? 0 : (L > a.max_ctx ? a.max_ctx : L);
+  int acc = a.accept_len[b];
+  acc = acc < 0 ? 0 : (acc > a.K ? a.K : acc);
+  const int n = acc + 1 < a.K ? acc + 1 : a.K;
+  const int pos = L + r;
+  bool write = r < n;
+  int page = -1;
+  if (write) {
+    const int lp = pos / kPage;
+    page = lp < a.max_pages ? a.page_table[(size_t)b * a.max_pages + lp] : -1;
+    if (page < 0 || page >= a.num_pages) write = false;
+  }
+  if (threadIdx.x == 0) {
+    if (a.slots) a.slots[b * a.K + r] = write ? page * kPage + pos % kPage : -1;
+    if (r == 0 && a.new_ctx_lens) a.new_ctx_lens[b] = L + n;
+  }
+  if (!write) return;
+  const int units = a.row_bytes / 16;  // per tensor: Hkv heads x D elements
+  const size_t src_row = (size_t)(b * a.K + r) * a.row_bytes;
+  for (int u = threadIdx.x; u < 2 * units; u += blockDim.x) {
+    const int tensor = u / units, uu = u % units;
+    const int g = uu / (a.head_bytes / 16), cc = uu % (a.head_bytes / 16);
+    const size_t dst = ((size_t)(page * a.Hkv + g) * kPage + pos % kPage) * a.head_bytes + cc * 16;
+    if (tensor == 0)
+      st16(a.k_cache + dst, ld16(a.k_blk + src_row + uu * 16));
+    else
+      st16(a.v_cache + dst, ld16(a.v_blk + src_row + uu * 16));
+  }
+}
+
+__global__ void __launch_bounds__(256) copy_probe_kernel(u32x4* __restrict__ dst, const u32x4* __restrict__ src,
+                                                         size_t n) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t k = (size_t)blockIdx.x * blockDim.x + threadIdx.x; k < n; k += stride) dst[k] = src[k];
+}
+
+}  // namespace orthrus
+
+using namespace orthrus;
+
+extern "C" orthrus_status orthrus_kv_append(void* k_cache, void* v_cache, const void* k_blk, const void* v_blk,
+                                            const int32_t* page_table, const int32_t* ctx_lens,
+                                            const int32_t* accept_len, int32_t* new_ctx_lens, int32_t* slots,
+                                            const orthrus_attn_desc* desc, void* stream) {
+  orthrus_status st = validate_desc(desc);
+  if (st != ORTHRUS_OK) return st;
+  if (!k_cache || !v_cache || !k_blk || !v_blk || !page_table || !ctx_lens || !accept_len) return ORTHRUS_ERR_NULL;
+  const orthrus_attn_desc& d = *desc;
+  AppendArgs a;
+  a.k_cache = (char*)k_cache;
+  a.v_cache = (char*)v_cache;
+  a.k_blk = (const char*)k_blk;
+  a.v_blk = (const char*)v_blk;
+  a.page_table = page_table;
+  a.ctx_lens = ctx_lens;
+  a.accept_len = accept_len;
+  a.new_ctx_lens = new_ctx_lens;
+  a.slots = slots;
+  a.B = d.batch;
+  a.K = d.block_k;
+  a.Hkv = d.n_kv_heads;
+  a.max_pages = d.max_pages_per_seq;
+  a.num_pages = d.num_pages;
+  a.max_ctx = d.max_ctx_len;
+  const int esz = d.dtype == ORTHRUS_BF16 ? 2 : 4;
+  a.head_bytes = d.head_dim * esz;
+  a.row_bytes = d.n_kv_heads * a.head_bytes;
+  hipLaunchKernelGGL(kv_append_kernel, dim3(d.batch * d.block_k), dim3(256), 0, (hipStream_t)stream, a);
+  return hipGetLastError() == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_LAUNCH;
+}
+
+extern "C" orthrus_status orthrus_copy_probe(void* dst, const void* src, size_t bytes, void* stream) {
+  if (!dst || !src) return ORTHRUS_ERR_NULL;
+  if (bytes == 0 || bytes % 16 != 0) return ORTHRUS_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(dst) | reinterpret_cast<uintptr_t>(src)) & 15) return ORTHRUS_ERR_SHAPE;
+  const size_t n = bytes / 16;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(copy_probe_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream, (u32x4*)dst,
+                     (const u32x4*)src, n);
+  return hipGetLastError() == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_LAUNCH;
+}
+
+extern "C" int32_t orthrus_abi_version(void) { return ORTHRUS_ABI_VERSION; }
+
+extern "C" const char* orthrus_status_str(orthrus_status s) {
+  switch (s) {
+    case ORTHRUS_OK: return "ok";
+    case ORTHRUS_ERR_NULL: return "a required pointer is NULL";
+    case ORTHRUS_ERR_SHAPE: return "a size is out of range or sizes are inconsistent";
+    case ORTHRUS_ERR_UNSUPPORTED: return "dtype, head_dim, group size or page size not supported";
+    case ORTHRUS_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case ORTHRUS_ERR_LAUNCH: return "the HIP runtime reported a launch error";
+  }
+  return "unknown status";
+}

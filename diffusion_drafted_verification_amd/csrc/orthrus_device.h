@@ -1,0 +1,49 @@
+// Device-side building blocks shared by the gfx950 kernels: vector types,
+// 16-byte memory moves and the 32x32 MFMA step for bf16 and fp32 storage.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace orthrus {
+
+typedef __bf16 bf16;
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kPage = 16;  // tokens per cache page
+
+// Eight consecutive elements of the storage type: the per-lane A/B operand
+// of one 32x32 MFMA k-step of 16 (two lane halves x 8 elements).
+template <typename T> struct Vec8;
+template <> struct Vec8<bf16> { typedef bf16x8 type; static constexpr int bytes = 16; };
+template <> struct Vec8<float> { typedef f32x8 type; static constexpr int bytes = 32; };
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// D(32x32, fp32) += A(32 x 16) * B(16 x 32) for one lane's operands.  Lane l
+// supplies row (l % 32) of A / column (l % 32) of B, elements 8*(l/32)+e of
+// the contracted dimension.  Only the pairing of A's and B's k-slots matters
+// for the contraction, and it is the same for both operands by construction.
+__device__ __forceinline__ f32x16 mfma_step(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// fp32 storage: eight 32x32x2 steps, step e contracting element e of both halves.
+__device__ __forceinline__ f32x16 mfma_step(f32x8 a, f32x8 b, f32x16 c) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], b[e], c, 0, 0, 0);
+  return c;
+}
+
+__device__ __forceinline__ float wave_max_xor32(float x) {
+  return fmaxf(x, __shfl_xor(x, 32, kWave));
+}
+
+}  // namespace orthrus

@@ -1,0 +1,30 @@
+// Host-side argument checks shared by the C entry points.  They run before
+// any HIP call, so every error status can be produced without a GPU.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "orthrus.h"
+
+namespace orthrus {
+
+inline orthrus_status validate_desc(const orthrus_attn_desc* d) {
+  if (!d) return ORTHRUS_ERR_NULL;
+  if (d->batch < 1 || d->block_k < 1 || d->block_k > 32 || d->n_q_heads < 1 || d->n_kv_heads < 1 ||
+      d->max_pages_per_seq < 1 || d->num_pages < 1 || d->max_ctx_len < 0)
+    return ORTHRUS_ERR_SHAPE;
+  if (d->n_q_heads % d->n_kv_heads != 0) return ORTHRUS_ERR_SHAPE;
+  const int G = d->n_q_heads / d->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return ORTHRUS_ERR_UNSUPPORTED;
+  if (d->head_dim != 64 && d->head_dim != 128) return ORTHRUS_ERR_UNSUPPORTED;
+  if (d->page_size != 16) return ORTHRUS_ERR_UNSUPPORTED;
+  if (d->dtype != ORTHRUS_BF16 && d->dtype != ORTHRUS_F32) return ORTHRUS_ERR_UNSUPPORTED;
+  if ((long)d->max_ctx_len + d->block_k > (long)d->max_pages_per_seq * d->page_size) return ORTHRUS_ERR_SHAPE;
+  if ((long)d->max_ctx_len + d->block_k > (1L << 30)) return ORTHRUS_ERR_SHAPE;
+  if (d->split_tokens < 0 || d->split_tokens % 64 != 0 || d->split_tokens > 8192) return ORTHRUS_ERR_SHAPE;
+  if (d->softmax_scale != d->softmax_scale) return ORTHRUS_ERR_SHAPE;  // NaN
+  return ORTHRUS_OK;
+}
+
+}  // namespace orthrus

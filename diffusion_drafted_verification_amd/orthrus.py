@@ -1,0 +1,219 @@
+"""Python binding of the gfx950 C-ABI library (include/orthrus.h).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels of liborthrus_gfx950.so.  PyTorch provides device memory and the
+current stream.  There is no CPU fallback: if the library is missing or the
+tensors are not on a GPU, the calls raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch  # imported before the library so both share torch's HIP runtime
+
+DIFF_BIDIR = 0
+AR_CAUSAL = 1
+BF16 = 0
+F32 = 1
+PAGE_SIZE = 16
+
+LIB_NAME = "liborthrus_gfx950.so"
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
+
+STATUS = {0: "ok", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_UNSUPPORTED", 4: "ERR_WORKSPACE", 5: "ERR_LAUNCH"}
+
+# every entry point include/orthrus.h declares, with its ctypes signature
+_vp, _i32, _sz, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float
+
+
+class AttnDesc(ctypes.Structure):
+    """orthrus_attn_desc"""
+    _fields_ = [("batch", _i32), ("block_k", _i32), ("n_q_heads", _i32), ("n_kv_heads", _i32),
+                ("head_dim", _i32), ("page_size", _i32), ("max_pages_per_seq", _i32), ("num_pages", _i32),
+                ("max_ctx_len", _i32), ("dtype", _i32), ("softmax_scale", _f32), ("split_tokens", _i32)]
+
+
+_DESC_P = ctypes.POINTER(AttnDesc)
+SIGNATURES = {
+    "orthrus_abi_version": (_i32, []),
+    "orthrus_status_str": (ctypes.c_char_p, [_i32]),
+    "orthrus_block_attn_workspace_bytes": (_sz, [_DESC_P]),
+    "orthrus_block_attn_split_tokens": (_i32, [_DESC_P]),
+    "orthrus_block_attn": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _DESC_P, _vp, _sz, _vp]),
+    "orthrus_greedy_accept_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "orthrus_greedy_accept": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
+    "orthrus_kv_append": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _DESC_P, _vp]),
+    "orthrus_copy_probe": (_i32, [_vp, _vp, _sz, _vp]),
+}
+
+_lib = None
+_lock = threading.Lock()
+
+
+class OrthrusError(RuntimeError):
+    pass
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        with _lock:
+            if _lib is None:
+                if not os.path.exists(LIB_PATH):
+                    raise OrthrusError(f"{LIB_PATH} is missing: build it with "
+                                       "`python -m diffusion_drafted_verification_amd.build`")
+                handle = ctypes.CDLL(LIB_PATH)
+                for name, (res, args) in SIGNATURES.items():
+                    fn = getattr(handle, name)
+                    fn.restype = res
+                    fn.argtypes = args
+                _lib = handle
+    return _lib
+
+
+def _check(status, what):
+    if status != 0:
+        msg = lib().orthrus_status_str(status).decode()
+        raise OrthrusError(f"{what}: {STATUS.get(status, status)} ({msg})")
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _gpu(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise OrthrusError("tensors must be on a GPU (there is no CPU path)")
+        if not t.is_contiguous():
+            raise OrthrusError("tensors must be contiguous")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise OrthrusError("tensors must be on one device")
+    return dev
+
+
+_DTYPES = {torch.bfloat16: BF16, torch.float32: F32}
+
+
+def make_desc(q, k_cache, page_table, max_ctx_len=None, softmax_scale=None, split_tokens=0):
+    """orthrus_attn_desc for tensors q [B,K,Hq,D], k_cache [pages,Hkv,P,D] and
+    page_table [B, max_pages].  max_ctx_len defaults to the table capacity
+    minus K (always a valid bound; pass the true maximum to size the launch
+    tightly)."""
+    B, K, Hq, D = q.shape
+    n_pages, Hkv, P, D2 = k_cache.shape
+    if D2 != D or P != PAGE_SIZE:
+        raise OrthrusError("k_cache must be [num_pages, Hkv, 16, D]")
+    if q.dtype not in _DTYPES:
+        raise OrthrusError(f"unsupported dtype {q.dtype}")
+    max_pages = page_table.shape[1]
+    if max_ctx_len is None:
+        max_ctx_len = max_pages * P - K
+    return AttnDesc(B, K, Hq, Hkv, D, P, max_pages, n_pages, int(max_ctx_len), _DTYPES[q.dtype],
+                    float(softmax_scale) if softmax_scale else 0.0, int(split_tokens))
+
+
+_workspaces = {}
+
+
+def workspace(device, nbytes, kind):
+    """A cached per-(device, kind) workspace of at least nbytes, zero-filled
+    when first allocated (the accept kernel leaves its workspace zeroed)."""
+    key = (str(device), kind)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def block_attn_workspace_bytes(desc):
+    return lib().orthrus_block_attn_workspace_bytes(ctypes.byref(desc))
+
+
+def block_attn(q, k_cache, v_cache, k_blk, v_blk, page_table, ctx_lens, mode, out=None, *, max_ctx_len=None,
+               softmax_scale=None, split_tokens=0, ws=None, stream=None):
+    """orthrus_block_attn: out [B, K, Hq, D] in q's dtype."""
+    dev = _gpu(q, k_cache, v_cache, k_blk, v_blk, page_table, ctx_lens, out)
+    if not (q.dtype == k_cache.dtype == v_cache.dtype == k_blk.dtype == v_blk.dtype):
+        raise OrthrusError("q, caches and block K/V must share one dtype")
+    if page_table.dtype != torch.int32 or ctx_lens.dtype != torch.int32:
+        raise OrthrusError("page_table and ctx_lens must be int32")
+    B, K, Hq, D = q.shape
+    if tuple(k_blk.shape) != (B, K, k_cache.shape[1], D) or v_blk.shape != k_blk.shape \
+            or v_cache.shape != k_cache.shape or tuple(ctx_lens.shape) != (B,) or page_table.shape[0] != B:
+        raise OrthrusError("inconsistent shapes")
+    desc = make_desc(q, k_cache, page_table, max_ctx_len, softmax_scale, split_tokens)
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise OrthrusError("out must match q")
+    need = lib().orthrus_block_attn_workspace_bytes(ctypes.byref(desc))
+    if ws is None and need:
+        ws = workspace(dev, need, "attn")
+    st = lib().orthrus_block_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_blk), _ptr(v_blk),
+                                  _ptr(page_table), _ptr(ctx_lens), int(mode), _ptr(out), ctypes.byref(desc),
+                                  _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream))
+    _check(st, "orthrus_block_attn")
+    return out
+
+
+def greedy_accept(ar_logits, draft_tokens, *, want_ar_tokens=True, ws=None, stream=None):
+    """orthrus_greedy_accept: returns (accept_len [B], next_token [B],
+    ar_tokens [B, K] or None), int32 on the logits' device."""
+    dev = _gpu(ar_logits, draft_tokens)
+    if ar_logits.dtype != torch.float32 or draft_tokens.dtype != torch.int32:
+        raise OrthrusError("ar_logits must be fp32 and draft_tokens int32")
+    B, K, V = ar_logits.shape
+    if tuple(draft_tokens.shape) != (B, K):
+        raise OrthrusError("draft_tokens must be [B, K]")
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    nxt = torch.empty(B, dtype=torch.int32, device=dev)
+    g = torch.empty((B, K), dtype=torch.int32, device=dev) if want_ar_tokens else None
+    need = lib().orthrus_greedy_accept_workspace_bytes(B, K, V)
+    if ws is None:
+        ws = workspace(dev, need, "accept")
+    st = lib().orthrus_greedy_accept(_ptr(ar_logits), _ptr(draft_tokens), _ptr(acc), _ptr(nxt), _ptr(g),
+                                     B, K, V, _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "orthrus_greedy_accept")
+    return acc, nxt, g
+
+
+def kv_append(k_cache, v_cache, k_blk, v_blk, page_table, ctx_lens, accept_len, *, new_ctx_lens=None,
+              slots=None, want_outputs=True, max_ctx_len=None, stream=None):
+    """orthrus_kv_append (in place on the caches): returns (new_ctx_lens [B],
+    slots [B, K]) or (None, None) when want_outputs is False."""
+    dev = _gpu(k_cache, v_cache, k_blk, v_blk, page_table, ctx_lens, accept_len)
+    B, K, Hkv, D = k_blk.shape
+    if want_outputs:
+        if new_ctx_lens is None:
+            new_ctx_lens = torch.empty(B, dtype=torch.int32, device=dev)
+        if slots is None:
+            slots = torch.empty((B, K), dtype=torch.int32, device=dev)
+    qlike = torch.empty((B, K, Hkv, D), dtype=k_blk.dtype, device="meta")
+    desc = make_desc(qlike, k_cache, page_table, max_ctx_len)
+    st = lib().orthrus_kv_append(_ptr(k_cache), _ptr(v_cache), _ptr(k_blk), _ptr(v_blk), _ptr(page_table),
+                                 _ptr(ctx_lens), _ptr(accept_len), _ptr(new_ctx_lens), _ptr(slots),
+                                 ctypes.byref(desc), _stream(stream))
+    _check(st, "orthrus_kv_append")
+    return new_ctx_lens, slots
+
+
+def copy_probe(dst, src, stream=None):
+    _gpu(dst, src)
+    n = src.numel() * src.element_size()
+    _check(lib().orthrus_copy_probe(_ptr(dst), _ptr(src), n, _stream(stream)), "orthrus_copy_probe")

@@ -1,0 +1,171 @@
+/*
+ * orthrus.h -- C ABI of the MI355X (gfx950) hot path of one Orthrus
+ * dual-view decode step: block attention over a shared paged KV cache,
+ * greedy consensus (argmax + longest-prefix accept) and KV append.
+ *
+ * Semantics follow the Orthrus explainer page for "Orthrus: Memory-Efficient
+ * Parallel Token Generation via Dual-View Diffusion" (gist.science, arXiv
+ * 2605.12825), technical summary §2.1-§2.3.
+ *
+ * Conventions shared by every call
+ *   - Every tensor pointer is a DEVICE pointer (hipMalloc / torch CUDA
+ *     memory) owned by the caller.  The library never allocates, frees or
+ *     retains caller memory and keeps no mutable global state.
+ *   - Work is only enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream); no call synchronises.  Results are ready when the stream is.
+ *   - Errors are synchronous and host-detectable only: a non-OK status means
+ *     nothing was enqueued.  ORTHRUS_ERR_LAUNCH means a launch was attempted
+ *     and the HIP runtime reported an error right after it.
+ *   - Device-resident values (ctx_lens, page ids, accept_len) are checked by
+ *     the kernels: an out-of-range context length or page id never faults; it
+ *     makes the affected rows' results unspecified (cache rows are not
+ *     written through an invalid page id).
+ *   - For a fixed descriptor every output is bit-identical from run to run.
+ *   - Calls are reentrant; calls that share a workspace must be ordered on
+ *     one stream.
+ *
+ * Layouts (row-major, innermost last)
+ *   q, out          [B, K, Hq, D]            storage dtype
+ *   k_blk, v_blk    [B, K, Hkv, D]           storage dtype
+ *   k_cache, v_cache[num_pages, Hkv, P, D]   storage dtype (one (page, head)
+ *                                            is P*D contiguous elements)
+ *   page_table      [B, max_pages_per_seq]   int32 physical page ids
+ *   ctx_lens        [B]                      int32 cached tokens per sequence
+ *   ar_logits       [B, K, V]                fp32
+ *   draft_tokens    [B, K]                   int32
+ *   accept_len, next_token, new_ctx_lens [B] int32
+ *   ar_tokens, slots[B, K]                   int32
+ * Logical position p of sequence b lives in page page_table[b][p / P], slot
+ * p % P.  Query head h reads KV head h * Hkv / Hq (grouped-query attention).
+ */
+#ifndef ORTHRUS_H
+#define ORTHRUS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ORTHRUS_ABI_VERSION 1
+
+/* Which view's mask the block rows use inside the block (explainer §2.2,
+ * §2.3).  Both views see the whole cached context. */
+typedef enum {
+  ORTHRUS_DIFF_BIDIR = 0, /* diffusion view, M_diff: block rows attend to each other both ways */
+  ORTHRUS_AR_CAUSAL = 1   /* frozen AR head's verify pass: block row i sees block rows j <= i   */
+} orthrus_mode;
+
+typedef enum { ORTHRUS_BF16 = 0, ORTHRUS_F32 = 1 } orthrus_dtype;
+
+typedef enum {
+  ORTHRUS_OK = 0,
+  ORTHRUS_ERR_NULL = 1,        /* a required pointer is NULL                          */
+  ORTHRUS_ERR_SHAPE = 2,       /* a size is out of range or sizes are inconsistent    */
+  ORTHRUS_ERR_UNSUPPORTED = 3, /* dtype / head_dim / group / page size not supported  */
+  ORTHRUS_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required          */
+  ORTHRUS_ERR_LAUNCH = 5       /* the HIP runtime reported an error after a launch    */
+} orthrus_status;
+
+/* Shape of one block-attention / append call.
+ *   batch               B >= 1
+ *   block_k             K, 1 <= K <= 32 (the pages use K = 32: anchor + 31 masks)
+ *   n_q_heads, n_kv_heads  Hq, Hkv; Hq % Hkv == 0, Hq / Hkv in {1, 2, 4, 8}
+ *   head_dim            D in {64, 128}
+ *   page_size           P, must be 16
+ *   max_pages_per_seq   row length of page_table
+ *   num_pages           physical pages in k_cache / v_cache
+ *   max_ctx_len         upper bound on every ctx_lens[b] (sizes the launch);
+ *                       max_ctx_len + K <= max_pages_per_seq * P
+ *   dtype               storage type of q, out, caches and block K/V
+ *   softmax_scale       <= 0 selects 1 / sqrt(D)
+ *   split_tokens        context positions per work-group; 0 = automatic,
+ *                       otherwise a multiple of 64 in [64, 8192]          */
+typedef struct {
+  int32_t batch;
+  int32_t block_k;
+  int32_t n_q_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t max_pages_per_seq;
+  int32_t num_pages;
+  int32_t max_ctx_len;
+  int32_t dtype;
+  float softmax_scale;
+  int32_t split_tokens;
+} orthrus_attn_desc;
+
+int32_t orthrus_abi_version(void);
+const char* orthrus_status_str(orthrus_status s);
+
+/* Bytes of caller-provided scratch orthrus_block_attn needs for `desc`
+ * (split-context partial results).  0 for an invalid descriptor.  The
+ * workspace needs no initialisation. */
+size_t orthrus_block_attn_workspace_bytes(const orthrus_attn_desc* desc);
+
+/* Context positions per work-group that orthrus_block_attn will use for
+ * `desc` (the split length), or 0 for an invalid descriptor. */
+int32_t orthrus_block_attn_split_tokens(const orthrus_attn_desc* desc);
+
+/* Block attention of one decode step (explainer §2.1-§2.3).
+ *
+ * For every sequence b (L = ctx_lens[b]), query head h and block row i < K:
+ *   keys/values = the L cached rows of KV head h*Hkv/Hq followed by the K
+ *   block rows k_blk/v_blk[b, :, h*Hkv/Hq]; row i sees all L cached keys and
+ *   block key j when mode == DIFF_BIDIR (any j) or AR_CAUSAL (j <= i);
+ *   out[b, i, h] = softmax(scale * q . k) . v over the visible keys.
+ * Accumulation is fp32; bf16 outputs are rounded to nearest even once.
+ * k_cache/v_cache are read only (the cache holds the AR keys/values that both
+ * views share).  `out` must not alias any input.  workspace may be NULL only
+ * when orthrus_block_attn_workspace_bytes(desc) == 0. */
+orthrus_status orthrus_block_attn(const void* q, const void* k_cache, const void* v_cache,
+                                  const void* k_blk, const void* v_blk, const int32_t* page_table,
+                                  const int32_t* ctx_lens, orthrus_mode mode, void* out,
+                                  const orthrus_attn_desc* desc, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* Bytes of the workspace orthrus_greedy_accept needs.  The workspace must be
+ * zero-filled before its first use; every call leaves it zero-filled again. */
+size_t orthrus_greedy_accept_workspace_bytes(int32_t batch, int32_t block_k, int32_t vocab);
+
+/* Greedy consensus of one step (explainer §2.3).
+ *   g[b, i]       = lowest index of the maximum of ar_logits[b, i, :]
+ *                   (fp32 compare; -0.0 ties with +0.0; logits must not be NaN)
+ *   accept_len[b] = number of leading i with draft_tokens[b, i] == g[b, i], in [0, K]
+ *   next_token[b] = g[b, min(accept_len[b], K-1)]  (the AR correction token, or
+ *                   the last accepted token when all K drafts agree)
+ *   ar_tokens     = g when non-NULL.
+ * The step commits min(accept_len + 1, K) tokens: g[b, 0 .. n-1].
+ * 1 <= K <= 32, 1 <= V < 2^31. */
+orthrus_status orthrus_greedy_accept(const float* ar_logits, const int32_t* draft_tokens,
+                                     int32_t* accept_len, int32_t* next_token, int32_t* ar_tokens,
+                                     int32_t batch, int32_t block_k, int32_t vocab, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+/* Commit the accepted block rows to the shared cache (explainer §2.3: the
+ * cache keeps only the committed positions).
+ *   n_b = min(max(accept_len[b], 0) + 1, K); for r < n_b and every KV head,
+ *   k_blk/v_blk[b, r] is copied bit-exactly to logical position
+ *   L_b + r = ctx_lens[b] + r of k_cache/v_cache.  Nothing else is written.
+ *   new_ctx_lens[b] = L_b + n_b            (optional, may be NULL)
+ *   slots[b, r] = page * P + slot written, -1 for r >= n_b (optional)
+ * ctx_lens is read only: in a multi-layer step pass new_ctx_lens only on
+ * the last layer so every layer appends at the same positions.  Neither
+ * output may alias ctx_lens, accept_len or page_table. */
+orthrus_status orthrus_kv_append(void* k_cache, void* v_cache, const void* k_blk, const void* v_blk,
+                                 const int32_t* page_table, const int32_t* ctx_lens,
+                                 const int32_t* accept_len, int32_t* new_ctx_lens, int32_t* slots,
+                                 const orthrus_attn_desc* desc, void* stream);
+
+/* Measurement helper: streams `bytes` (a multiple of 16) from src to dst with
+ * plain 16-byte loads and stores.  Used to calibrate hardware counters and to
+ * measure the achievable HBM rate; not part of the decode step. */
+orthrus_status orthrus_copy_probe(void* dst, const void* src, size_t bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ORTHRUS_H */

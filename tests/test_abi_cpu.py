@@ -1,0 +1,117 @@
+"""The C-ABI library loads, exports every entry point the header declares,
+and rejects invalid arguments on the host (no GPU needed: every call here
+fails validation before any HIP call)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from diffusion_drafted_verification_amd import orthrus as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "orthrus.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="library not built")
+
+
+def declared_entry_points():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(orthrus_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_entry_points()
+    assert len(names) == 9
+    assert set(names) == set(B.SIGNATURES)
+    lib = B.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_one_hip_runtime_in_process():
+    B.lib()
+    maps = open("/proc/self/maps").read()
+    runtimes = {l.split()[-1] for l in maps.splitlines() if "libamdhip64" in l}
+    assert len(runtimes) == 1, runtimes
+
+
+def test_version_and_status_strings():
+    lib = B.lib()
+    assert lib.orthrus_abi_version() == 1
+    for s in range(6):
+        assert lib.orthrus_status_str(s)
+
+
+def good_desc(**kw):
+    d = dict(batch=1, block_k=32, n_q_heads=32, n_kv_heads=8, head_dim=128, page_size=16,
+             max_pages_per_seq=514, num_pages=514, max_ctx_len=8192, dtype=0, softmax_scale=0.0, split_tokens=0)
+    d.update(kw)
+    return B.AttnDesc(**d)
+
+
+FAKE = ctypes.c_void_p(4096)   # never dereferenced: validation fails first
+
+
+def attn(desc, ws=None, ws_bytes=0, mode=0, null_q=False):
+    return B.lib().orthrus_block_attn(None if null_q else FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, mode, FAKE,
+                                      ctypes.byref(desc), ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(block_k=0), 2), (dict(block_k=33), 2), (dict(batch=0), 2), (dict(n_q_heads=12), 2),
+    (dict(n_q_heads=48), 3), (dict(head_dim=96), 3), (dict(page_size=32), 3), (dict(dtype=7), 3),
+    (dict(max_ctx_len=8193 - 32 + 16 * 514), 2), (dict(split_tokens=100), 2), (dict(split_tokens=16384), 2),
+    (dict(num_pages=0), 2), (dict(max_ctx_len=-1), 2)])
+def test_block_attn_rejects_bad_descriptors(kw, status):
+    assert attn(good_desc(**kw)) == status
+    assert B.lib().orthrus_block_attn_workspace_bytes(ctypes.byref(good_desc(**kw))) == 0
+
+
+def test_block_attn_rejects_null_mode_and_workspace():
+    d = good_desc()
+    assert attn(d, null_q=True) == 1
+    need = B.lib().orthrus_block_attn_workspace_bytes(ctypes.byref(d))
+    assert need > 0
+    assert attn(d, mode=2, ws=FAKE, ws_bytes=need) == 2
+    assert attn(d) == 4                                   # workspace missing
+    assert attn(d, ws=FAKE, ws_bytes=need - 1) == 4       # too small
+    assert attn(d, ws=ctypes.c_void_p(4100), ws_bytes=need) == 4   # misaligned
+
+
+def test_split_and_workspace_arithmetic():
+    lib = B.lib()
+    d = good_desc()
+    split = lib.orthrus_block_attn_split_tokens(ctypes.byref(d))
+    assert split % 64 == 0 and 64 <= split <= 8192
+    s_max = -(-(8192 + 32) // split)
+    rows = 1 * 32 * s_max * 32
+    assert lib.orthrus_block_attn_workspace_bytes(ctypes.byref(d)) == rows * 128 * 4 + rows * 8
+    d1 = good_desc(split_tokens=8192, max_ctx_len=100)      # one split: no workspace
+    assert lib.orthrus_block_attn_workspace_bytes(ctypes.byref(d1)) == 0
+
+
+def test_accept_and_append_validation():
+    lib = B.lib()
+    assert lib.orthrus_greedy_accept(None, FAKE, FAKE, FAKE, None, 1, 32, 100, FAKE, 1 << 20, None) == 1
+    assert lib.orthrus_greedy_accept(FAKE, FAKE, FAKE, FAKE, None, 1, 33, 100, FAKE, 1 << 20, None) == 2
+    assert lib.orthrus_greedy_accept(FAKE, FAKE, FAKE, FAKE, None, 1, 32, 0, FAKE, 1 << 20, None) == 2
+    need = lib.orthrus_greedy_accept_workspace_bytes(2, 32, 151936)
+    assert need == 2 * 32 * 8 + 16
+    assert lib.orthrus_greedy_accept(FAKE, FAKE, FAKE, FAKE, None, 2, 32, 151936, FAKE, need - 1, None) == 4
+    assert lib.orthrus_greedy_accept(FAKE, FAKE, FAKE, FAKE, None, 2, 32, 151936, None, need, None) == 4
+    d = good_desc()
+    assert lib.orthrus_kv_append(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, ctypes.byref(d), None) == 1
+    assert lib.orthrus_kv_append(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+                                 ctypes.byref(good_desc(head_dim=80)), None) == 3
+    assert lib.orthrus_copy_probe(FAKE, FAKE, 17, None) == 2
+    assert lib.orthrus_copy_probe(None, FAKE, 16, None) == 1
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 32, 4, 64)
+    with pytest.raises(B.OrthrusError):
+        B.block_attn(q, q, q, q, q, torch.zeros(1, 1, dtype=torch.int32), torch.zeros(1, dtype=torch.int32), 0)

@@ -1,0 +1,419 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 CPU oracle.
+
+Bars: bit-exact for argmax tokens, accept lengths, next tokens, slots,
+context lengths and appended cache bytes; for attention outputs
+max|gpu - oracle| <= 2e-2 * max|V| over the call (the stated tolerance) and,
+because that bound alone is loose at N(0,1) inputs, also <= 2e-2 * the largest
+|oracle output| of each (sequence, head) slice, plus sharp-softmax and
+block-dominant variants where a wrong key, page or mask gives an O(1) error.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from diffusion_drafted_verification_amd import inputs as I
+from oracle import orthrus_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+DIFF, AR = O.DIFF_BIDIR, O.AR_CAUSAL
+TOL = 2e-2
+
+
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def K_():
+    from diffusion_drafted_verification_amd import orthrus
+    return orthrus
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def max_abs_v(inp):
+    return max(inp.v_cache.float().abs().max().item(), inp.v_blk.float().abs().max().item())
+
+
+def check_attn(inp, mode, *, scale=None, split=0, batches=None, heads=None, tight=None, max_ctx=None):
+    """Run the GPU call and compare with the oracle on the selected slices."""
+    d = dev()
+    g = inp.to(d)
+    out = K_().block_attn(g.q, g.k_cache, g.v_cache, g.k_blk, g.v_blk, g.page_table, g.ctx_lens, mode,
+                          max_ctx_len=inp.max_ctx_len if max_ctx is None else max_ctx,
+                          softmax_scale=scale, split_tokens=split)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().astype(np.float64)
+    ref = O.block_attn(inp.q, inp.k_cache, inp.v_cache, inp.k_blk, inp.v_blk, inp.page_table, inp.ctx_lens,
+                       mode, softmax_scale=scale, batches=batches, heads=heads)
+    sel = ~np.isnan(ref)
+    err = np.abs(got - ref)
+    err[~sel] = 0
+    vmax = max_abs_v(inp)
+    assert np.isfinite(got[sel]).all()
+    assert err.max() <= TOL * vmax, (err.max(), vmax)
+    Bn, K, Hq, D = ref.shape
+    for b in (range(Bn) if batches is None else batches):
+        for h in (range(Hq) if heads is None else heads):
+            sl = ref[b, :, h]
+            assert err[b, :, h].max() <= TOL * np.abs(sl).max(), (b, h, err[b, :, h].max(), np.abs(sl).max())
+    if tight is not None:
+        assert err.max() <= tight * vmax, (err.max(), vmax)
+    return out, err.max() / vmax
+
+
+# ---------------------------------------------------------------------------
+# block attention
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", [DIFF, AR])
+def test_tiny_fp32(mode):
+    say("tiny_fp32", mode)
+    inp = I.make_attn_inputs("tiny_fp32")
+    _, rel = check_attn(inp, mode, tight=1e-4)
+
+
+@pytest.mark.parametrize("mode", [DIFF, AR])
+def test_qwen3_1p7b_2k(mode):
+    say("qwen3_1p7b_2k", mode)
+    check_attn(I.make_attn_inputs("qwen3_1p7b_2k"), mode)
+
+
+@pytest.mark.parametrize("mode", [DIFF, AR])
+def test_qwen3_8b_8k(mode):
+    say("qwen3_8b_8k", mode)
+    check_attn(I.make_attn_inputs("qwen3_8b_8k"), mode)
+
+
+@pytest.mark.parametrize("mode", [DIFF, AR])
+def test_qwen3_8b_ragged16_sampled(mode):
+    say("qwen3_8b_ragged16", mode)
+    inp = I.make_attn_inputs("qwen3_8b_ragged16")
+    lens = inp.ctx_lens.numpy()
+    pick = [int(np.argmin(lens)), int(np.argmax(lens)), 7]
+    check_attn(inp, mode, batches=pick)
+
+
+def test_qwen3_8b_32k_sampled():
+    say("qwen3_8b_32k_b4 layer 0 sampled heads")
+    inp = I.make_attn_inputs("qwen3_8b_32k_b4")
+    for mode in (DIFF, AR):
+        check_attn(inp, mode, batches=[0, 3], heads=[0, 5, 31])
+
+
+@pytest.mark.parametrize("mode", [DIFF, AR])
+@pytest.mark.parametrize("split", [64, 128, 256, 1024, 8192])
+def test_split_lengths_agree(mode, split):
+    """Every context split length (and thus every partial-combine path) meets
+    the bar; 8192 means one work-group per (sequence, KV head)."""
+    say("split", split, mode)
+    inp = I.make_attn_inputs("qwen3_8b_8k", ctx_lens=[3001])
+    check_attn(inp, mode, split=split)
+
+
+@pytest.mark.parametrize("mode", [DIFF, AR])
+@pytest.mark.parametrize("workload,dtype", [("qwen3_8b_8k", torch.bfloat16), ("qwen3_1p7b_2k", torch.bfloat16),
+                                            ("tiny_fp32", torch.float32)])
+def test_sharp_softmax(mode, workload, dtype):
+    """Scale 1 (score std ~ sqrt(D)): outputs are close to single value rows,
+    so a wrong page, key or mask is an O(1) error."""
+    say("sharp", workload, mode)
+    inp = I.make_attn_inputs(workload, ctx_lens=[517])
+    check_attn(inp, mode, scale=1.0)
+
+
+@pytest.mark.parametrize("mode", [DIFF, AR])
+@pytest.mark.parametrize("L", [0, 1, 15, 16, 17, 63, 64, 65, 200])
+@pytest.mark.parametrize("K", [1, 7, 32])
+def test_block_dominant(mode, L, K):
+    """Short contexts with distinct block values (8 + r on row r): the block
+    rows dominate, so the mode mask and block placement are checked hard."""
+    say("block_dominant", mode, L, K)
+    inp = I.make_attn_inputs("qwen3_8b_8k", ctx_lens=[L])
+    inp.q = inp.q[:, :K].contiguous()
+    inp.k_blk = inp.k_blk[:, :K].contiguous()
+    inp.v_blk = (inp.v_blk[:, :K].float() + 8.0 + torch.arange(K).view(1, K, 1, 1)).to(torch.bfloat16)
+    check_attn(inp, mode)
+    check_attn(inp, mode, scale=1.0)
+
+
+@pytest.mark.parametrize("G,D,dtype", [(1, 64, torch.bfloat16), (2, 64, torch.bfloat16), (8, 128, torch.bfloat16),
+                                       (1, 128, torch.bfloat16), (4, 64, torch.float32), (2, 128, torch.float32)])
+def test_group_sizes_and_head_dims(G, D, dtype):
+    say("group/dim", G, D, dtype)
+    Hkv = 2
+    torch.manual_seed(G * 1000 + D)
+    B, K, L = 2, 32, [300, 77]
+    table, n_pages = I.make_page_table(L, K, 16, shuffle=True, seed=G + D)
+    inp = I.AttnInputs(torch.randn(B, K, G * Hkv, D).to(dtype), torch.randn(n_pages, Hkv, 16, D).to(dtype),
+                       torch.randn(n_pages, Hkv, 16, D).to(dtype), torch.randn(B, K, Hkv, D).to(dtype),
+                       torch.randn(B, K, Hkv, D).to(dtype), torch.from_numpy(table),
+                       torch.tensor(L, dtype=torch.int32), max(L))
+    for mode in (DIFF, AR):
+        check_attn(inp, mode)
+        check_attn(inp, mode, scale=1.0)
+
+
+def test_gpu_invariants():
+    """K = 1: both modes give identical bits; page relabelling gives identical
+    bits; the last row agrees between modes; two runs give identical bits."""
+    say("invariants")
+    d = dev()
+    ob = K_()
+    inp = I.make_attn_inputs("qwen3_8b_8k", ctx_lens=[2500]).to(d)
+    run = lambda x, mode, **kw: ob.block_attn(x.q, x.k_cache, x.v_cache, x.k_blk, x.v_blk, x.page_table,
+                                               x.ctx_lens, mode, max_ctx_len=x.max_ctx_len, **kw)
+    a1 = run(inp, AR)
+    a2 = run(inp, AR)
+    assert torch.equal(a1, a2)
+    df = run(inp, DIFF)
+    assert (a1[:, -1].float() - df[:, -1].float()).abs().max().item() <= 2e-3
+    # K = 1
+    k1 = I.AttnInputs(inp.q[:, :1].contiguous(), inp.k_cache, inp.v_cache, inp.k_blk[:, :1].contiguous(),
+                      inp.v_blk[:, :1].contiguous(), inp.page_table, inp.ctx_lens, inp.max_ctx_len)
+    assert torch.equal(run(k1, AR), run(k1, DIFF))
+    # relabel the physical pages
+    n = inp.k_cache.shape[0]
+    relabel = torch.randperm(n, generator=torch.Generator().manual_seed(5)).to(d)
+    kc2 = torch.empty_like(inp.k_cache); kc2[relabel] = inp.k_cache
+    vc2 = torch.empty_like(inp.v_cache); vc2[relabel] = inp.v_cache
+    pt = inp.page_table.long()
+    pt2 = torch.where(pt >= 0, relabel[pt.clamp(min=0)], pt).int()
+    moved = I.AttnInputs(inp.q, kc2, vc2, inp.k_blk, inp.v_blk, pt2, inp.ctx_lens, inp.max_ctx_len)
+    assert torch.equal(run(moved, AR), a1)
+
+
+def test_ragged_with_loose_max_ctx():
+    """max_ctx_len larger than every real context (grid sized by the bound,
+    splits past a sequence's end exit early)."""
+    say("loose max_ctx")
+    inp = I.make_attn_inputs("qwen3_8b_8k", ctx_lens=[100], batch=1)
+    check_attn(inp, AR, max_ctx=inp.page_table.shape[1] * 16 - 32)
+
+
+# ---------------------------------------------------------------------------
+# greedy accept
+# ---------------------------------------------------------------------------
+
+def check_accept(logits, drafts):
+    d = dev()
+    acc, nxt, g = K_().greedy_accept(logits.to(d), drafts.to(d))
+    torch.cuda.synchronize()
+    ra, rn, rg = O.greedy_accept(logits.numpy(), drafts.numpy())
+    assert np.array_equal(g.cpu().numpy(), rg)
+    assert np.array_equal(acc.cpu().numpy(), ra)
+    assert np.array_equal(nxt.cpu().numpy(), rn)
+    return ra
+
+
+def test_accept_tiny_twelve():
+    say("accept tiny")
+    logits, _ = I.make_logits(1, 32, 1024, seed=0, workload="tiny_fp32")
+    g = O.greedy_argmax(logits.numpy())
+    drafts = I.make_drafts(g, [12], 1024, seed=0, workload="tiny_fp32")
+    ra = check_accept(logits, drafts)
+    assert ra[0] == 12
+
+
+@pytest.mark.parametrize("B,plant", [(1, False), (1, True), (16, True), (4, False)])
+def test_accept_qwen_vocab(B, plant):
+    say("accept qwen", B, plant)
+    logits, t = I.make_logits(B, 32, I.QWEN3_VOCAB, seed=B, workload="qwen3_8b_8k", plant=plant)
+    if t is None:
+        t = torch.from_numpy(O.greedy_argmax(logits.numpy()))
+    pre = I.geometric_prefix(B, 32, seed=B)
+    drafts = I.make_drafts(t, pre, I.QWEN3_VOCAB, seed=B)
+    ra = check_accept(logits, drafts)
+    assert np.array_equal(ra, pre)
+
+
+def test_accept_planted_ties_and_zeros():
+    say("accept ties")
+    V = 151936
+    x = torch.randn(2, 32, V) * 4
+    x[0, 0, [5, 70000, V - 1]] = 1e3             # ties across chunks -> 5
+    x[0, 1, :] = -torch.inf                      # all -inf -> 0
+    x[0, 2, V - 1] = 1e3                         # max at the end
+    x[0, 3, 0] = 1e3                             # max at the start
+    x[0, 4, :] = 0.0
+    x[0, 4, 100:] = -1.0
+    x[0, 4, 17] = -0.0                           # -0.0 ties with +0.0: lowest index 0
+    x[0, 5, :] = -1.0
+    x[0, 5, [9000, 9001]] = torch.tensor([-0.0, 0.0])   # -> 9000
+    x[0, 6, :] = -1.0
+    x[0, 6, [20000, 3]] = torch.tensor([0.0, -0.0])     # -> 3
+    x[1, :, 12345] = 1e3
+    x[1, :, 12344] = 1e3                         # -> 12344 on every row
+    g = torch.from_numpy(O.greedy_argmax(x.numpy()))
+    assert g[0, 0] == 5 and g[0, 1] == 0 and g[0, 2] == V - 1 and g[0, 3] == 0 and g[0, 4] == 0
+    assert g[0, 5] == 9000 and g[0, 6] == 3 and bool((g[1] == 12344).all())
+    for drafts in (g.int(), torch.where(torch.arange(32) == 9, g + 1, g).int(), (g + 1).int()):
+        check_accept(x, drafts)
+
+
+@pytest.mark.parametrize("V", [1, 3, 1023, 1025, 151937, 262147])
+def test_accept_unaligned_vocab(V):
+    say("accept V", V)
+    x = torch.randn(3, 5, V)
+    g = torch.from_numpy(O.greedy_argmax(x.numpy()))
+    drafts = g.clone().int()
+    drafts[1, 2] += 1
+    drafts[2, 0] += 1
+    check_accept(x, drafts)
+
+
+def test_accept_workspace_is_reset_between_calls():
+    say("accept repeat")
+    for s in range(4):
+        x = torch.randn(2, 32, 5000, generator=torch.Generator().manual_seed(s))
+        g = torch.from_numpy(O.greedy_argmax(x.numpy())).int()
+        d = g.clone()
+        d[0, s * 7] += 1
+        check_accept(x, d)
+
+
+# ---------------------------------------------------------------------------
+# KV append
+# ---------------------------------------------------------------------------
+
+def check_append(inp, acc):
+    d = dev()
+    g = inp.to(d)
+    accg = torch.tensor(acc, dtype=torch.int32, device=d)
+    # sentinel-filled caches
+    kc = torch.full_like(g.k_cache, -3.0)
+    vc = torch.full_like(g.v_cache, 5.0)
+    new_lens, slots = K_().kv_append(kc, vc, g.k_blk, g.v_blk, g.page_table, g.ctx_lens, accg,
+                                     max_ctx_len=inp.max_ctx_len)
+    torch.cuda.synchronize()
+    rk, rv, rl, rs = O.kv_append(kc.cpu(), vc.cpu(), inp.k_blk, inp.v_blk, inp.page_table, inp.ctx_lens, acc)
+    view = (lambda t: t.cpu().view(torch.int16).numpy()) if kc.dtype == torch.bfloat16 else \
+        (lambda t: t.cpu().numpy())
+    assert np.array_equal(view(kc), rk)
+    assert np.array_equal(view(vc), rv)
+    assert np.array_equal(new_lens.cpu().numpy(), rl)
+    assert np.array_equal(slots.cpu().numpy(), rs)
+
+
+@pytest.mark.parametrize("L,a", [(0, 0), (15, 0), (15, 3), (16, 31), (31, 32), (2047, 11), (8192, 32)])
+def test_append_cases(L, a):
+    say("append", L, a)
+    inp = I.make_attn_inputs("qwen3_8b_8k", ctx_lens=[L])
+    check_append(inp, [a])
+
+
+def test_append_ragged_batch():
+    say("append ragged16")
+    inp = I.make_attn_inputs("qwen3_8b_ragged16")
+    acc = list(I.geometric_prefix(16, 32, seed=3))
+    check_append(inp, acc)
+
+
+def test_append_fp32():
+    say("append fp32")
+    inp = I.make_attn_inputs("tiny_fp32")
+    check_append(inp, [12])
+
+
+# ---------------------------------------------------------------------------
+# whole step and lossless loop
+# ---------------------------------------------------------------------------
+
+def test_full_step_qwen3_8b():
+    """DIFF attention, AR attention, accept and append of one step at the
+    Qwen3-8B 8k shape, each output checked against the oracle."""
+    say("full step 8b")
+    d = dev()
+    ob = K_()
+    inp = I.make_attn_inputs("qwen3_8b_8k")
+    g = inp.to(d)
+    for mode in (DIFF, AR):
+        check_attn(inp, mode)
+    logits, t = I.make_logits(1, 32, I.QWEN3_VOCAB, seed=0, workload="qwen3_8b_8k", plant=True)
+    pre = I.geometric_prefix(1, 32, seed=0, workload="qwen3_8b_8k")
+    drafts = I.make_drafts(t, pre, I.QWEN3_VOCAB, seed=0)
+    acc, nxt, tok = ob.greedy_accept(logits.to(d), drafts.to(d))
+    ra, rn, rg = O.greedy_accept(logits.numpy(), drafts.numpy())
+    assert acc.cpu().numpy()[0] == ra[0] == pre[0] and nxt.cpu().numpy()[0] == rn[0]
+    kc, vc = g.k_cache.clone(), g.v_cache.clone()
+    nl, sl = ob.kv_append(kc, vc, g.k_blk, g.v_blk, g.page_table, g.ctx_lens, acc, max_ctx_len=inp.max_ctx_len)
+    rk, rv, rl, rs = O.kv_append(inp.k_cache, inp.v_cache, inp.k_blk, inp.v_blk, inp.page_table, inp.ctx_lens, ra)
+    assert np.array_equal(kc.cpu().view(torch.int16).numpy(), rk)
+    assert np.array_equal(vc.cpu().view(torch.int16).numpy(), rv)
+    assert nl.cpu().numpy()[0] == rl[0] == 8192 + min(ra[0] + 1, 32)
+
+
+def test_lossless_loop_on_gpu():
+    """The dual-view loop driven by the GPU calls commits exactly the tokens
+    of one-token-at-a-time greedy decoding driven by the same GPU calls
+    (toy fp32 one-layer model; projections are test scaffolding)."""
+    say("lossless loop")
+    d = dev()
+    ob = K_()
+    r = torch.Generator().manual_seed(7)
+    V, dm, Hq, Hkv, D, K = 64, 32, 4, 1, 64, 8
+    emb = torch.randn(V, dm, generator=r).to(d)
+    pos = (torch.randn(512, dm, generator=r) * 0.5).to(d)
+    wq = torch.randn(dm, Hq * D, generator=r).to(d) / math.sqrt(dm)
+    wk = torch.randn(dm, Hkv * D, generator=r).to(d) / math.sqrt(dm)
+    wv = torch.randn(dm, Hkv * D, generator=r).to(d) / math.sqrt(dm)
+    wo = torch.randn(Hq * D, V, generator=r).to(d)
+    wu = torch.randn(dm, V, generator=r).to(d)
+    n_pages = 32
+    table = torch.randperm(n_pages, generator=r).int().view(1, -1).to(d)
+
+    def qkv(tokens, start):
+        x = emb[tokens] + pos[start:start + len(tokens)]
+        T = len(tokens)
+        return (x, (x @ wq).view(1, T, Hq, D).contiguous(), (x @ wk).view(1, T, Hkv, D).contiguous(),
+                (x @ wv).view(1, T, Hkv, D).contiguous())
+
+    def run(prompt, n_new, Kb, drafter):
+        kc = torch.zeros(n_pages, Hkv, 16, D, device=d)
+        vc = torch.zeros_like(kc)
+        L = torch.zeros(1, dtype=torch.int32, device=d)
+        for i, t in enumerate(prompt[:-1]):
+            _, q, k, v = qkv(torch.tensor([t], device=d), i)
+            L, _ = ob.kv_append(kc, vc, k, v, table, L, torch.zeros(1, dtype=torch.int32, device=d),
+                                max_ctx_len=n_pages * 16 - 1)
+        anchor, out, steps = prompt[-1], [], 0
+        while len(out) < n_new:
+            Lh = int(L.item())
+            drafts = drafter(out, Kb)
+            block = torch.tensor([anchor] + drafts[:Kb - 1], device=d)
+            x, q, k, v = qkv(block, Lh)
+            att = ob.block_attn(q, kc, vc, k, v, table, L, AR, max_ctx_len=n_pages * 16 - Kb)
+            logits = (att.view(Kb, Hq * D) @ wo + x @ wu).view(1, Kb, V).contiguous()
+            acc, nxt, g = ob.greedy_accept(logits, torch.tensor([drafts], dtype=torch.int32, device=d))
+            n = min(int(acc.item()) + 1, Kb)
+            out.extend(g[0, :n].tolist())
+            L, _ = ob.kv_append(kc, vc, k, v, table, L, acc, max_ctx_len=n_pages * 16 - Kb)
+            anchor = int(nxt.item())
+            steps += 1
+        return out[:n_new], steps
+
+    prompt = [3, 17, 5, 60, 2]
+    ref, s1 = run(prompt, 60, 1, lambda out, Kb: [0] * Kb)
+    assert s1 == 60
+    perfect, s2 = run(prompt, 48, K, lambda out, Kb: (ref + [0] * 64)[len(out):len(out) + Kb])
+    assert perfect == ref[:48] and s2 == 48 // K
+    rnd = np.random.default_rng(1)
+    noisy, _ = run(prompt, 48, K, lambda out, Kb: [t if rnd.random() < 0.7 else int(rnd.integers(V))
+                                                    for t in (ref + [0] * 64)[len(out):len(out) + Kb]])
+    assert noisy == ref[:48]
+
+
+def test_copy_probe():
+    say("copy probe")
+    d = dev()
+    src = torch.randn(1 << 20, device=d)
+    dst = torch.empty_like(src)
+    K_().copy_probe(dst, src)
+    assert torch.equal(dst, src)
