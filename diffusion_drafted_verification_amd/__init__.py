@@ -8,8 +8,10 @@ this package holds those sources (csrc/), their build script and a thin
 ctypes binding.
 """
 
-from .orthrus import (AR_CAUSAL, DIFF_BIDIR, AttnDesc, OrthrusError, block_attn, block_attn_workspace_bytes,
-                      copy_probe, greedy_accept, kv_append, lib, make_desc)
+from .orthrus import (AR_CAUSAL, DIFF_BIDIR, AttnDesc, LayerPointers, OrthrusError, block_attn,
+                      block_attn_workspace_bytes, copy_probe, greedy_accept, kv_append, kv_append_layers, lib,
+                      make_desc)
 
-__all__ = ["AR_CAUSAL", "DIFF_BIDIR", "AttnDesc", "OrthrusError", "block_attn", "block_attn_workspace_bytes",
-           "copy_probe", "greedy_accept", "kv_append", "lib", "make_desc"]
+__all__ = ["AR_CAUSAL", "DIFF_BIDIR", "AttnDesc", "LayerPointers", "OrthrusError", "block_attn",
+           "block_attn_workspace_bytes", "copy_probe", "greedy_accept", "kv_append", "kv_append_layers", "lib",
+           "make_desc"]

@@ -27,6 +27,8 @@
 //     partials (unnormalised O, running max, sum) and a combine kernel merges
 //     them; the work-group order puts all splits of one (b, g) on one XCD so
 //     the partials stay in that XCD's L2.
+#include <type_traits>
+
 #include "orthrus_device.h"
 #include "orthrus_host.h"
 
@@ -97,170 +99,184 @@ __device__ __forceinline__ typename Vec8<T>::type pack_p(const f32x16& s, int j)
   return r;
 }
 
-// Global -> register staging of one 64-position stage.  Unit u covers four
+// Global -> register staging of one 64-position stage.  Half of the
+// work-group's waves stage K, the other half V.  Unit u covers four
 // consecutive positions (one token quad, never crossing a page) and one
-// 16-byte chunk of the head dimension, for both K and V.
+// 16-byte chunk of the head dimension.
 template <typename T, int D, int NT>
 struct Stage {
   typedef AttnLayout<T, D> Lay;
-  static constexpr int UPT = (Lay::UNITS + NT - 1) / NT;
-  u32x4 k[UPT][4];
-  u32x4 v[UPT][4];
+  static constexpr int LT = NT / 2;                          // loader threads per tensor
+  static constexpr int UPT = (Lay::UNITS + LT - 1) / LT;     // units per loader thread
+  u32x4 r[UPT][4];
+  uint32_t valid;  // bit 4j+t: r[j][t] holds data (else it is stored as zeros)
 
-  __device__ void load(const AttnArgs& a, const int* pages, int page_base, int b, int g, int L, int N,
-                       int p0, int tid) {
+  // Issue the loads of one stage without consuming them: every load reads a
+  // valid address (the block K/V base stands in for unused positions) and the
+  // zeroing of unused positions waits until store time, so the loads of
+  // several stages stay in flight together.  cache / blk: the tensor this
+  // thread stages (K or V).
+  // Positions at or past p_end (the split's end, <= N) are never read: the
+  // page-id table only covers the split.
+  __device__ void load(const char* cache, const char* blk, const AttnArgs& a, const int* pages, int page_base,
+                       int b, int g, int L, int p_end, int p0, int ltid) {
+    valid = 0;
+    // a stage entirely inside the cached context (the common case): one page
+    // id per thread and four loads at fixed offsets from one address
+    const bool all_cached = p0 + kTile <= L && p0 + kTile <= p_end;
 #pragma unroll
     for (int j = 0; j < UPT; ++j) {
-      const int u = tid + j * NT;
-      if (Lay::UNITS % NT != 0 && u >= Lay::UNITS) break;
+      const int u = ltid + j * LT;
+      if (Lay::UNITS % LT != 0 && u >= Lay::UNITS) break;
       const int tq = u / Lay::KCH, c = u % Lay::KCH;
-      const int pos0 = p0 + 4 * tq;
-      if (pos0 + 4 <= L) {  // four cached positions of one page
-        const int page = pages[(pos0 >> 4) - page_base];
-        if (page >= 0) {
-          const size_t off = ((size_t)(page * a.Hkv + g) * kPage + (pos0 & 15)) * Lay::KROW + c * 16;
+      const int pos0 = p0 + 4 * tq;  // four positions of one page
+      const int pidx = (pos0 >> 4) - page_base;  // padded stages run past the split: clamp
+      const int page = pages[pidx < kMaxSplit / kPage ? pidx : kMaxSplit / kPage - 1];
+      const size_t coff =
+          ((size_t)((page > 0 ? page : 0) * a.Hkv + g) * kPage + (pos0 & 15)) * Lay::KROW + c * 16;
+      if (all_cached) {
+        const bool ok = page >= 0;
+        const char* src = ok ? cache + coff : blk;
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            k[j][t] = ld16(a.k_cache + off + t * Lay::KROW);
-            v[j][t] = ld16(a.v_cache + off + t * Lay::KROW);
-          }
-        } else {
+        for (int t = 0; t < 4; ++t) r[j][t] = ld16(src + (ok ? t * Lay::KROW : 0));
+        valid |= (ok ? 15u : 0u) << (4 * j);
+        continue;
+      }
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            k[j][t] = u32x4{0, 0, 0, 0};
-            v[j][t] = u32x4{0, 0, 0, 0};
-          }
-        }
-      } else {
-        // tail of the context, the block rows, or past the end: every load is
-        // issued from a valid address and zeroed afterwards when unused
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int pos = pos0 + t;
-          const char* kp = a.k_blk;
-          const char* vp = a.v_blk;
-          bool ok = false;
-          if (pos < L) {
-            const int page = pages[(pos >> 4) - page_base];
-            if (page >= 0) {
-              const size_t off = ((size_t)(page * a.Hkv + g) * kPage + (pos & 15)) * Lay::KROW + c * 16;
-              kp = a.k_cache + off;
-              vp = a.v_cache + off;
-              ok = true;
-            }
-          } else if (pos < N) {
-            const size_t off = ((size_t)(b * a.K + (pos - L)) * a.Hkv + g) * Lay::KROW + c * 16;
-            kp = a.k_blk + off;
-            vp = a.v_blk + off;
-            ok = true;
-          }
-          const u32x4 kk = ld16(kp), vv = ld16(vp);
-          const u32x4 z{0, 0, 0, 0};
-          k[j][t] = ok ? kk : z;
-          v[j][t] = ok ? vv : z;
-        }
+      for (int t = 0; t < 4; ++t) {
+        const int pos = pos0 + t;
+        const bool in_cache = pos < L && pos < p_end && page >= 0;
+        const bool in_blk = pos >= L && pos < p_end;
+        const size_t boff = ((size_t)(b * a.K + (in_blk ? pos - L : 0)) * a.Hkv + g) * Lay::KROW + c * 16;
+        const char* src = in_cache ? cache + coff + t * Lay::KROW : blk + boff;
+        r[j][t] = ld16(src);
+        valid |= (uint32_t)(in_cache || in_blk) << (4 * j + t);
       }
     }
   }
 
+  __device__ u32x4 get(int j, int t) const {
+    return ((valid >> (4 * j + t)) & 1) ? r[j][t] : u32x4{0, 0, 0, 0};
+  }
+
   // K rows go to LDS row swap_bits23(token) (so the score accumulator holds
-  // eight consecutive tokens per lane half); V is written transposed.
-  __device__ void store(char* stage, int tid) const {
-    char* ks = stage;
-    char* vs = stage + Lay::KBYTES;
+  // eight consecutive tokens per lane half), XOR-swizzled by 16-byte chunk.
+  __device__ void store_k(char* ks, int ltid) const {
 #pragma unroll
     for (int j = 0; j < UPT; ++j) {
-      const int u = tid + j * NT;
-      if (Lay::UNITS % NT != 0 && u >= Lay::UNITS) break;
+      const int u = ltid + j * LT;
+      if (Lay::UNITS % LT != 0 && u >= Lay::UNITS) break;
       const int tq = u / Lay::KCH, c = u % Lay::KCH;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int row = swap_bits23(4 * tq + t);
-        st16(ks + Lay::kslot(row, c), k[j][t]);
-      }
+      for (int t = 0; t < 4; ++t) st16(ks + Lay::kslot(swap_bits23(4 * tq + t), c), get(j, t));
+    }
+  }
+
+  // V is written transposed: row d holds the 64 positions of element d.
+  __device__ void store_v(char* vs, int ltid) const {
+#pragma unroll
+    for (int j = 0; j < UPT; ++j) {
+      const int u = ltid + j * LT;
+      if (Lay::UNITS % LT != 0 && u >= Lay::UNITS) break;
+      const int tq = u / Lay::KCH, c = u % Lay::KCH;
+      const u32x4 x0 = get(j, 0), x1 = get(j, 1), x2 = get(j, 2), x3 = get(j, 3);
       if constexpr (sizeof(T) == 2) {
-        // element e of the chunk is d = c*8 + e; four tokens -> 8 bytes of row d
+        // element e of the chunk is d = c*8 + e; four positions -> 8 bytes of row d
         const int tch = tq >> 1, half = (tq & 1) * 8;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int w = e >> 1;
           u32x2 pk;
           if (e & 1) {
-            pk[0] = (v[j][0][w] >> 16) | (v[j][1][w] & 0xffff0000u);
-            pk[1] = (v[j][2][w] >> 16) | (v[j][3][w] & 0xffff0000u);
+            pk[0] = (x0[w] >> 16) | (x1[w] & 0xffff0000u);
+            pk[1] = (x2[w] >> 16) | (x3[w] & 0xffff0000u);
           } else {
-            pk[0] = (v[j][0][w] & 0xffffu) | (v[j][1][w] << 16);
-            pk[1] = (v[j][2][w] & 0xffffu) | (v[j][3][w] << 16);
+            pk[0] = (x0[w] & 0xffffu) | (x1[w] << 16);
+            pk[1] = (x2[w] & 0xffffu) | (x3[w] << 16);
           }
-          const int d = c * 8 + e;
-          *reinterpret_cast<u32x2*>(vs + Lay::vslot(d, tch) + half) = pk;
+          *reinterpret_cast<u32x2*>(vs + Lay::vslot(c * 8 + e, tch) + half) = pk;
         }
       } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int d = c * 4 + e;
-          st16(vs + Lay::vslot(d, tq), u32x4{v[j][0][e], v[j][1][e], v[j][2][e], v[j][3][e]});
-        }
+        for (int e = 0; e < 4; ++e) st16(vs + Lay::vslot(c * 4 + e, tq), u32x4{x0[e], x1[e], x2[e], x3[e]});
       }
     }
   }
 };
 
+// One work-group per (sequence b, KV head g, context split s); 2G waves:
+// wave w serves query head g*G + w%G on the 32-position half w/G of every
+// 64-position stage.  The two halves of a head keep separate softmax states
+// and are merged through LDS at the end.
 template <typename T, int D, int G, int MODE>
-__global__ void __launch_bounds__(kWave * G) attn_main(AttnArgs a) {
+__global__ void __launch_bounds__(2 * kWave * G) attn_main(AttnArgs a) {
   typedef AttnLayout<T, D> Lay;
   typedef typename Vec8<T>::type V8;
-  constexpr int NT = kWave * G;
+  constexpr int NT = 2 * kWave * G;
   constexpr int KS = D / 16;   // MFMA k-steps over the head dimension
   constexpr int MB = D / 32;   // 32-wide blocks of the head dimension in O^T
+  typedef Stage<T, D, NT> St;
+  // stages kept in flight in registers (about 64 staging registers at most)
+  constexpr int PD = (St::UPT * 16 <= 16) ? 3 : ((St::UPT * 16 <= 32) ? 2 : 1);
+  constexpr int MERGE = G * (MB * 16 + 2) * kWave * 4;
+  constexpr int SMEM = (2 * Lay::STAGE > MERGE) ? 2 * Lay::STAGE : MERGE;
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * Lay::STAGE];
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
   __shared__ int pages[kMaxSplit / kPage];
 
   const int BH = a.B * a.Hkv;
   const int bg = blockIdx.x % BH;
   const int s = blockIdx.x / BH;
   const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int tid = threadIdx.x;
+  const int p_begin = s * a.split;
+  const int page_base = p_begin >> 4;
+  // page ids of this split (loaded before the context length is known, so
+  // the two loads overlap); ids outside [0, num_pages) become -1
+  int pg[(kMaxSplit / kPage + NT - 1) / NT];
+#pragma unroll
+  for (int k = 0; k < (kMaxSplit / kPage + NT - 1) / NT; ++k) {
+    const int x = tid + k * NT, lp = page_base + x;
+    pg[k] = (x < a.split / kPage && lp < a.max_pages) ? a.page_table[(size_t)b * a.max_pages + lp] : -1;
+  }
   int L = a.ctx_lens[b];
   L = L < 0 ? 0 : (L > a.max_ctx ? a.max_ctx : L);
   const int N = L + a.K;
-  const int S_b = (N + a.split - 1) / a.split;
+  // splits partition the cached context; the last one also takes the K block keys
+  const int S_b = L > 0 ? (L + a.split - 1) / a.split : 1;
   if (s >= S_b) return;
-  const int p_begin = s * a.split;
-  const int p_end = min(p_begin + a.split, N);
+  const int p_end = s == S_b - 1 ? N : p_begin + a.split;
   const int ntiles = (p_end - p_begin + kTile - 1) / kTile;
-  const int tid = threadIdx.x;
   const int wave = tid / kWave, lane = tid % kWave;
   const int i = lane & 31, hi = lane >> 5;
-  const int h = g * G + wave;
+  const int hw = wave % G, sub = wave / G;
+  const int h = g * G + hw;
+  // loader role: the first half of the threads stages V, the second K
+  const bool v_loader = tid < NT / 2;
+  const int ltid = v_loader ? tid : tid - NT / 2;
+  const char* src_cache = v_loader ? a.v_cache : a.k_cache;
+  const char* src_blk = v_loader ? a.v_blk : a.k_blk;
 
-  // page ids of this split's cached positions (invalid ids become -1)
-  const int page_base = p_begin >> 4;
-  for (int x = tid; x < a.split / kPage; x += NT) {
-    const int lp = page_base + x;
-    int id = -1;
-    if (lp * kPage < L && lp < a.max_pages) {
-      id = a.page_table[(size_t)b * a.max_pages + lp];
-      if (id < 0 || id >= a.num_pages) id = -1;
-    }
-    pages[x] = id;
+#pragma unroll
+  for (int k = 0; k < (kMaxSplit / kPage + NT - 1) / NT; ++k) {
+    const int x = tid + k * NT;
+    if (x < kMaxSplit / kPage) pages[x] = (pg[k] >= 0 && pg[k] < a.num_pages) ? pg[k] : -1;
   }
 
   // this wave's query rows as the B operand of S^T = K Q^T (one 16-wide k-step each)
   V8 qf[KS];
   {
-    const char* qrow = a.q + ((size_t)(b * a.K + i) * a.Hq + h) * D * sizeof(T);
+    const char* qrow = a.q + ((size_t)(b * a.K + (i < a.K ? i : 0)) * a.Hq + h) * D * sizeof(T);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      if (i < a.K) {
-        const int off = (16 * ks + 8 * hi) * sizeof(T);
-        if constexpr (sizeof(T) == 2) {
-          qf[ks] = __builtin_bit_cast(V8, ld16(qrow + off));
-        } else {
-          struct P { u32x4 x, y; } pr{ld16(qrow + off), ld16(qrow + off + 16)};
-          qf[ks] = __builtin_bit_cast(V8, pr);
-        }
+      const int off = (16 * ks + 8 * hi) * sizeof(T);
+      if constexpr (sizeof(T) == 2) {
+        qf[ks] = __builtin_bit_cast(V8, ld16(qrow + off));
       } else {
+        struct P { u32x4 x, y; } pr{ld16(qrow + off), ld16(qrow + off + 16)};
+        qf[ks] = __builtin_bit_cast(V8, pr);
+      }
+      if (i >= a.K) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) qf[ks][e] = (T)0.f;
       }
@@ -274,79 +290,116 @@ __global__ void __launch_bounds__(kWave * G) attn_main(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[m][r] = 0.f;
   float m_c = -INFINITY;  // running max of this lane's row, log2 units
-  float l = 0.f;          // this lane half's share of the row sum
+  float l = 0.f;          // this lane's share of the row sum
   const float c = a.c;
 
-  Stage<T, D, NT> st;
-  st.load(a, pages, page_base, b, g, L, N, p_begin, tid);
+  // Register ring of PD stages.  The stage count is padded to a multiple of
+  // PD and every load is issued unconditionally (stages past the split read
+  // valid addresses and are masked), so the ring body is straight-line code
+  // and the compiler's wait counts keep PD stages in flight.
+  St st[PD];
+#pragma unroll
+  for (int p = 0; p < PD; ++p)
+    st[p].load(src_cache, src_blk, a, pages, page_base, b, g, L, p_end, p_begin + p * kTile, ltid);
 
-  for (int t = 0; t < ntiles; ++t) {
-    char* buf = smem + (t & 1) * Lay::STAGE;
-    st.store(buf, tid);
-    __syncthreads();
-    const int p0 = p_begin + t * kTile;
-    if (t + 1 < ntiles) st.load(a, pages, page_base, b, g, L, N, p0 + kTile, tid);
+  const int nt_pad = ((ntiles + PD - 1) / PD) * PD;
+  for (int t0 = 0; t0 < nt_pad; t0 += PD) {
+#pragma unroll
+    for (int p = 0; p < PD; ++p) {
+      const int t = t0 + p;
+      char* buf = smem + (t & 1) * Lay::STAGE;
+      if (v_loader) st[p].store_v(buf + Lay::KBYTES, ltid);
+      else st[p].store_k(buf, ltid);
+      __syncthreads();
+      st[p].load(src_cache, src_blk, a, pages, page_base, b, g, L, p_end, p_begin + (t + PD) * kTile, ltid);
 
-    const char* ks_lds = buf;
-    const char* vs_lds = buf + Lay::KBYTES;
+      const int pbase = p_begin + t * kTile + 32 * sub;
+      if (pbase < p_end) {
+        const char* ks_lds = buf;
+        const char* vs_lds = buf + Lay::KBYTES;
+        f32x16 acc;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int pbase = p0 + 32 * sub;
-      if (pbase >= p_end) break;
-      f32x16 acc;
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+        const int row = 32 * sub + i;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-      const int row = 32 * sub + i;
+        for (int ks = 0; ks < KS; ++ks) {
+          const int e0 = (16 * ks + 8 * hi) * sizeof(T) / 16;  // first chunk of the operand
+          const V8 av = lds_vec8<T>(ks_lds, Lay::kslot(row, e0), Lay::kslot(row, e0 + 1));
+          acc = mfma_step(av, qf[ks], acc);
+        }
+        // acc[r] is the score of position pbase + 16*(r/8) + 8*hi + r%8 for row i
+        if (pbase + 32 > L) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int e0 = (16 * ks + 8 * hi) * sizeof(T) / 16;  // first chunk of the operand
-        const V8 av = lds_vec8<T>(ks_lds, Lay::kslot(row, e0), Lay::kslot(row, e0 + 1));
-        acc = mfma_step(av, qf[ks], acc);
-      }
-      // acc[r] is the score of position pbase + 16*(r/8) + 8*hi + r%8 for row i
-      if (pbase + 32 > L) {
+          for (int r = 0; r < 16; ++r) {
+            const int pos = pbase + 16 * (r >> 3) + 8 * hi + (r & 7);
+            bool vis;
+            if (MODE == ORTHRUS_DIFF_BIDIR) vis = pos < N;
+            else vis = pos < L || (pos < N && pos - L <= i);
+            if (!vis) acc[r] = -INFINITY;
+          }
+        }
+        float mx = acc[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, acc[r]);
+        mx = wave_max_xor32(mx);
+        const bool need = mx * c > m_c + kRescaleLog2;
+        if (__any(need)) {
+          const float new_mc = need ? mx * c : m_c;
+          const float sc = (new_mc == m_c) ? 1.f : __builtin_amdgcn_exp2f(m_c - new_mc);
+#pragma unroll
+          for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[m][r] *= sc;
+          l *= sc;
+          m_c = new_mc;
+        }
+        const float mref = (m_c == -INFINITY) ? 0.f : m_c;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int pos = pbase + 16 * (r >> 3) + 8 * hi + (r & 7);
-          bool vis;
-          if (MODE == ORTHRUS_DIFF_BIDIR) vis = pos < N;
-          else vis = pos < L || (pos < N && pos - L <= i);
-          if (!vis) acc[r] = -INFINITY;
+          acc[r] = __builtin_amdgcn_exp2f(fmaf(acc[r], c, -mref));
+          l += acc[r];
         }
-      }
-      float mx = acc[0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, acc[r]);
-      mx = wave_max_xor32(mx);
-      const bool need = mx * c > m_c + kRescaleLog2;
-      if (__any(need)) {
-        const float new_mc = need ? mx * c : m_c;
-        const float sc = (new_mc == m_c) ? 1.f : __builtin_amdgcn_exp2f(m_c - new_mc);
+        for (int j = 0; j < 2; ++j) {
+          const V8 pv = pack_p<T>(acc, j);
+          const int e0 = (32 * sub + 16 * j + 8 * hi) * sizeof(T) / 16;
 #pragma unroll
-        for (int m = 0; m < MB; ++m)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[m][r] *= sc;
-        l *= sc;
-        m_c = new_mc;
-      }
-      const float mref = (m_c == -INFINITY) ? 0.f : m_c;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        acc[r] = __builtin_amdgcn_exp2f(fmaf(acc[r], c, -mref));
-        l += acc[r];
-      }
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const V8 pv = pack_p<T>(acc, j);
-        const int e0 = (32 * sub + 16 * j + 8 * hi) * sizeof(T) / 16;
-#pragma unroll
-        for (int m = 0; m < MB; ++m) {
-          const int d = 32 * m + i;
-          const V8 vv = lds_vec8<T>(vs_lds, Lay::vslot(d, e0), Lay::vslot(d, e0 + 1));
-          o[m] = mfma_step(vv, pv, o[m]);
+          for (int m = 0; m < MB; ++m) {
+            const int d = 32 * m + i;
+            const V8 vv = lds_vec8<T>(vs_lds, Lay::vslot(d, e0), Lay::vslot(d, e0 + 1));
+            o[m] = mfma_step(vv, pv, o[m]);
+          }
         }
       }
     }
+  }
+
+  // merge the two position halves of each head: the second-half wave hands
+  // its (max, sum, O) to the first-half wave through LDS
+  __syncthreads();  // every wave is done with the stage buffers
+  float* mo = reinterpret_cast<float*>(smem) + hw * (MB * 16 + 2) * kWave;
+  if (sub == 1) {
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mo[(m * 16 + r) * kWave + lane] = o[m][r];
+    mo[(MB * 16) * kWave + lane] = m_c;
+    mo[(MB * 16 + 1) * kWave + lane] = l;
+  }
+  __syncthreads();
+  if (sub == 1) return;
+  {
+    const float m1 = mo[(MB * 16) * kWave + lane];
+    const float l1 = mo[(MB * 16 + 1) * kWave + lane];
+    const float mm = fmaxf(m_c, m1);
+    const float w0 = (m_c == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_c - mm);
+    const float w1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[m][r] = w0 * o[m][r] + w1 * mo[(m * 16 + r) * kWave + lane];
+    l = w0 * l + w1 * l1;
+    m_c = mm;
   }
 
   const float l_row = l + __shfl_xor(l, 32, kWave);
@@ -389,35 +442,101 @@ __global__ void __launch_bounds__(kWave * G) attn_main(AttnArgs a) {
 
 // Merge the split partials of sequences whose context spans several
 // work-groups: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
-template <typename T, int D>
-__global__ void __launch_bounds__(256) attn_combine(AttnArgs a, int G) {
-  constexpr int TPR = D / 4;          // threads per row (4 outputs each)
-  constexpr int RPW = 256 / TPR;      // rows per work-group
-  const int id = blockIdx.x;
-  const int g = id % a.Hkv;
-  const int b = (id / a.Hkv) % a.B;
-  const int rest = id / (a.Hkv * a.B);  // = rg * G + w
-  const int w = rest % G, rg = rest / G;
+// A row (b, i, h) is served by SG groups of D/4 lanes (4 outputs per lane);
+// group q takes splits q, q+SG, ... and issues all of its loads before
+// reducing; the groups of a row then merge (shuffles within a wave, LDS
+// otherwise).  A work-group covers 256 / (SG D/4) consecutive rows of one
+// (b, g); block id = chunk * (B Hkv) + b Hkv + g, so the rows of one (b, g)
+// run on the XCD that wrote its partials (when B Hkv % 8 == 0).
+template <typename T, int D, int SG>
+__global__ void __launch_bounds__(256) attn_combine(AttnArgs a) {
+  constexpr int TPR = D / 4;          // lanes per group
+  constexpr int LPR = TPR * SG;       // lanes per row
+  constexpr int RPB = 256 / LPR;      // rows per work-group
+  constexpr int PER = 4;              // splits per group in flight at once
+  __shared__ float red_m[256 / kWave];
+  __shared__ f32x4 red_o[SG > 2 ? SG : 1][TPR];
+  __shared__ float red_l[SG > 2 ? SG : 1];
+
+  const int BH = a.B * a.Hkv, G = a.Hq / a.Hkv;
+  const int bg = blockIdx.x % BH, chunk = blockIdx.x / BH;
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int tid = threadIdx.x;
+  const int rl = chunk * RPB + tid / LPR;         // row within (b, g): w * K + i
+  const bool live = rl < G * a.K;
+  const int w = rl / a.K, i = rl % a.K;
   const int h = g * G + w;
-  const int i = rg * RPW + threadIdx.x / TPR;
-  if (i >= a.K) return;
   int L = a.ctx_lens[b];
   L = L < 0 ? 0 : (L > a.max_ctx ? a.max_ctx : L);
-  const int S_b = (L + a.K + a.split - 1) / a.split;
-  if (S_b <= 1) return;
-  const int d0 = 4 * (threadIdx.x % TPR);
-  const size_t base = (size_t)(b * a.Hq + h) * a.s_max * kRows + i;
+  const int S_b = L > 0 ? (L + a.split - 1) / a.split : 1;
+  if (S_b <= 1) return;                             // uniform over the work-group
+  const int x = tid % LPR, sg = x / TPR, d0 = 4 * (x % TPR);
+  const size_t base = (size_t)(b * a.Hq + (live ? h : 0)) * a.s_max * kRows + (live ? i : 0);
+
   float M = -INFINITY;
-  for (int s = 0; s < S_b; ++s) M = fmaxf(M, a.ws_ml[base + (size_t)s * kRows].x);
   f32x4 acc{0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
-  for (int s = 0; s < S_b; ++s) {
-    const float2 ml = a.ws_ml[base + (size_t)s * kRows];
-    const float w8 = (ml.x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
-    const f32x4 x = *reinterpret_cast<const f32x4*>(a.ws_o + (base + (size_t)s * kRows) * D + d0);
-    acc += w8 * x;
-    den += w8 * ml.y;
+  for (int s0 = sg; s0 < S_b; s0 += SG * PER) {
+    float2 ml[PER];
+    f32x4 xo[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int s = s0 + k * SG;
+      const size_t r = base + (size_t)(s < S_b ? s : 0) * kRows;
+      ml[k] = a.ws_ml[r];
+      xo[k] = *reinterpret_cast<const f32x4*>(a.ws_o + r * D + d0);
+      if (s >= S_b) ml[k].x = -INFINITY;
+    }
+    float mnew = M;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) mnew = fmaxf(mnew, ml[k].x);
+    if (mnew != -INFINITY) {
+      const float sc = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - mnew);
+      acc *= sc;
+      den *= sc;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) {
+        const float w8 = (ml[k].x == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(ml[k].x - mnew);
+        acc += w8 * xo[k];
+        den += w8 * ml[k].y;
+      }
+      M = mnew;
+    }
   }
+  if constexpr (SG == 2) {
+    // the two groups of a row are adjacent TPR-lane blocks of one wave
+    const float Mo = __shfl_xor(M, TPR, kWave);
+    const float Mall = fmaxf(M, Mo);
+    const float sc = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - Mall);
+    acc *= sc;
+    den *= sc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], TPR, kWave);
+    den += __shfl_xor(den, TPR, kWave);
+  } else if constexpr (SG > 2) {
+    // one row per work-group: merge the groups through LDS
+    float Mw = M;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) Mw = fmaxf(Mw, __shfl_xor(Mw, off, kWave));
+    if (tid % kWave == 0) red_m[tid / kWave] = Mw;
+    __syncthreads();
+    float Mall = red_m[0];
+#pragma unroll
+    for (int k = 1; k < 256 / kWave; ++k) Mall = fmaxf(Mall, red_m[k]);
+    const float sc = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - Mall);
+    red_o[sg][x % TPR] = acc * sc;
+    if (x % TPR == 0) red_l[sg] = den * sc;
+    __syncthreads();
+    if (sg != 0) return;
+    acc = red_o[0][x];
+    den = red_l[0];
+#pragma unroll
+    for (int q = 1; q < SG; ++q) {
+      acc += red_o[q][x];
+      den += red_l[q];
+    }
+  }
+  if (!live || sg != 0) return;
   const float inv = 1.f / den;
   char* orow = a.out + ((size_t)(b * a.K + i) * a.Hq + h) * D * sizeof(T);
   if constexpr (sizeof(T) == 2) {
@@ -430,6 +549,418 @@ __global__ void __launch_bounds__(256) attn_combine(AttnArgs a, int G) {
   }
 }
 
+template <typename T, int D>
+static hipError_t launch_combine(const AttnArgs& a, hipStream_t stream) {
+  const int rows = (a.Hq / a.Hkv) * a.K;  // per (b, g)
+  auto go = [&](auto sg_tag) {
+    constexpr int SG = decltype(sg_tag)::value;
+    constexpr int RPB = 256 / ((D / 4) * SG);
+    const int chunks = (rows + RPB - 1) / RPB;
+    hipLaunchKernelGGL((attn_combine<T, D, SG>), dim3(chunks * a.B * a.Hkv), dim3(256), 0, stream, a);
+  };
+  if (a.s_max >= 16) go(std::integral_constant<int, 256 / (D / 4)>());
+  else if (a.s_max >= 3) go(std::integral_constant<int, 2>());
+  else go(std::integral_constant<int, 1>());
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// bf16 streaming kernel.  Same work decomposition, masks and softmax as
+// attn_main, but the K/V stages go HBM -> LDS through the LDS-DMA path
+// (global_load_lds_dwordx4: no staging registers, no LDS store instructions)
+// and V stays token-major in LDS, read back transposed by ds_read_b64_tr_b16.
+// A ring of kRing 64-position stages (distinct LDS arrays, so the compiler's
+// wait tracking stays per buffer) keeps kRing - 1 stages of DMA in flight:
+// at stage t every wave waits for its own loads of stage t (vmcnt), one
+// barrier publishes the stage, then the DMA of stage t + kRing - 1 is issued
+// into the buffer stage t - 1 just released.  Work-group = 2G waves; wave w
+// serves query head g*G + w%G on the 32-position half w/G of each stage.
+constexpr int kRing = 4;
+
+template <int D>
+struct StreamLayout {
+  static constexpr int ROWB = D * 2;         // bytes per K/V row
+  static constexpr int CPR = ROWB / 16;      // 16-byte chunks per row (16 or 8)
+  static constexpr int TILEB = kTile * ROWB; // one tensor's 64-row tile
+  static constexpr int STAGE = 2 * TILEB;    // K tile then V tile
+  static constexpr int RPI = 1024 / ROWB;    // rows per wave DMA instruction (4 or 8)
+  static constexpr int IPT = kTile / RPI;    // DMA instructions per tensor tile
+  static constexpr int KSW = CPR - 1;        // K: chunk ^= row & KSW
+  __device__ static int kswz(int row) { return row & KSW; }
+  __device__ static int vswz(int row) { return (row & 3) << 1; }  // V: chunk ^= 2 (row & 3)
+};
+
+#define ORTHRUS_LDS __attribute__((address_space(3)))
+
+// One wave instruction of the LDS-DMA path: lane l copies 16 bytes from its
+// global address to LDS address (dst + 16 l).  Written as inline assembly so
+// that the compiler does not track these LDS writes: the kernel orders them
+// itself (s_waitcnt vmcnt + barrier before any wave reads a stage).  The
+// instruction has no register result; M0 holds the wave-uniform LDS base
+// (one wait state after writing M0 before the load reads it).
+__device__ __forceinline__ void dma16(const void* src, char* dst) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)reinterpret_cast<uintptr_t>((ORTHRUS_LDS char*)dst));
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+}
+
+// DMA of one stage (positions p0 .. p0 + 63).  Lane l of a wave instruction
+// writes 16 bytes at the instruction's LDS base + 16 l, i.e. row (base row +
+// l / CPR), chunk slot l % CPR, and therefore loads the chunk the slot's
+// swizzle assigns there.  The stage's instructions are dealt round-robin to
+// the waves (wave w owns q = w + NW k).  A lane's offset inside its (page,
+// head) block depends only on (lane, slot): loop invariant.
+template <int D, int NW>
+struct DmaPlan {
+  typedef StreamLayout<D> Lay;
+  static constexpr int NI = 2 * Lay::IPT;       // instructions per stage
+  static constexpr int NS = (NI + NW - 1) / NW; // per wave
+
+  __device__ static int voff(int wave, int lane, int k) {
+    const int q = wave + NW * k;
+    const int ten = q / Lay::IPT, ii = q % Lay::IPT;
+    const int row = ii * Lay::RPI + lane / Lay::CPR;
+    const int tok = ten == 0 ? swap_bits23(row) : row;
+    const int chunk = (lane % Lay::CPR) ^ (ten == 0 ? Lay::kswz(row) : Lay::vswz(row));
+    return (tok & 15) * Lay::ROWB + chunk * 16;
+  }
+
+  // the whole stage lies in the cached context (invalid page ids were
+  // replaced by page 0)
+  __device__ static void issue_cached(char* st, const AttnArgs& a, const int* pages, int page_base, int g, int p0,
+                                      int wave, int lane) {
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      const int q = wave + NW * k;
+      if (NI % NW != 0 && q >= NI) break;
+      const int ten = q / Lay::IPT, ii = q % Lay::IPT;
+      const int tok0 = ten == 0 ? swap_bits23(ii * Lay::RPI) : ii * Lay::RPI;  // rows share one page
+      const int page = __builtin_amdgcn_readfirstlane(pages[((p0 + tok0) >> 4) - page_base]);
+      const char* base = (ten == 0 ? a.k_cache : a.v_cache) + (size_t)(page * a.Hkv + g) * (kPage * Lay::ROWB);
+      char* dst = st + ten * Lay::TILEB + ii * 1024;
+      dma16(base + voff(wave, lane, k), dst);
+    }
+  }
+
+  // the stage reaches the context tail, the block rows or the split end:
+  // per-lane source selection (positions past the split end read a valid
+  // block K/V address; their scores are masked)
+  __device__ static void issue_tail(char* st, const AttnArgs& a, const int* pages, int page_base, int b, int g,
+                                    int L, int p_end, int p0, int wave, int lane) {
+    const int lrow = lane / Lay::CPR, cs = lane % Lay::CPR;
+#pragma unroll
+    for (int k = 0; k < NS; ++k) {
+      const int q = wave + NW * k;
+      if (NI % NW != 0 && q >= NI) break;
+      const int ten = q / Lay::IPT, ii = q % Lay::IPT;
+      const int row = ii * Lay::RPI + lrow;
+      const int tok = ten == 0 ? swap_bits23(row) : row;
+      const int chunk = cs ^ (ten == 0 ? Lay::kswz(row) : Lay::vswz(row));
+      const char* cache = ten == 0 ? a.k_cache : a.v_cache;
+      const char* blk = ten == 0 ? a.k_blk : a.v_blk;
+      const int pos = p0 + tok;
+      const char* src = blk + chunk * 16;
+      if (pos < L && pos < p_end)
+        src = cache + ((size_t)(pages[(pos >> 4) - page_base] * a.Hkv + g) * kPage + (pos & 15)) * Lay::ROWB +
+              chunk * 16;
+      else if (pos >= L && pos < p_end)
+        src = blk + ((size_t)(b * a.K + (pos - L)) * a.Hkv + g) * Lay::ROWB + chunk * 16;
+      char* dst = st + ten * Lay::TILEB + ii * 1024;
+      dma16(src, dst);
+    }
+  }
+
+  __device__ static void issue(char* st, const AttnArgs& a, const int* pages, int page_base, int b, int g, int L,
+                               int p_end, int p0, int wave, int lane) {
+    if (p0 >= p_end) return;
+    if (p0 + kTile <= L && p0 + kTile <= p_end)
+      issue_cached(st, a, pages, page_base, g, p0, wave, lane);
+    else
+      issue_tail(st, a, pages, page_base, b, g, L, p_end, p0, wave, lane);
+  }
+};
+
+// wait until at most N of this wave's vector loads are outstanding; issued
+// through the builtin so the compiler's own wait tracking knows about it
+// (gfx9 encoding: vmcnt low bits [3:0], high bits [15:14]; expcnt and
+// lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if constexpr (N == 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
+  else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+  else if constexpr (N == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
+  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+  else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  else if constexpr (N == 24) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+  else if constexpr (N == 32) asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+  else if constexpr (N == 48) asm volatile("s_waitcnt vmcnt(48)" ::: "memory");
+  else static_assert(N < 0, "unsupported wait count");
+}
+
+__device__ __forceinline__ void barrier_no_fence() {
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int D, int G, int MODE>
+__global__ void __launch_bounds__(2 * kWave * G) attn_stream(AttnArgs a) {
+  typedef StreamLayout<D> Lay;
+  typedef DmaPlan<D, 2 * G> Plan;
+  constexpr int NW = 2 * G;
+  constexpr int NT = kWave * NW;
+  constexpr int KS = D / 16;
+  constexpr int MB = D / 32;
+  static_assert(MB * 16 * kWave * 4 * 2 <= Lay::STAGE, "merge area: two heads per stage buffer");
+  static_assert(G <= 4, "merge area covers four heads");
+
+  __shared__ __attribute__((aligned(1024))) char st0[Lay::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[Lay::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st2[Lay::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st3[Lay::STAGE];
+  __shared__ int pages[kMaxSplit / kPage];
+
+  const int BH = a.B * a.Hkv;
+  const int bg = blockIdx.x % BH;
+  const int s = blockIdx.x / BH;
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int tid = threadIdx.x;
+  const int p_begin = s * a.split;
+  const int page_base = p_begin >> 4;
+  int pg[(kMaxSplit / kPage + NT - 1) / NT];
+#pragma unroll
+  for (int k = 0; k < (kMaxSplit / kPage + NT - 1) / NT; ++k) {
+    const int x = tid + k * NT, lp = page_base + x;
+    pg[k] = (x < a.split / kPage && lp < a.max_pages) ? a.page_table[(size_t)b * a.max_pages + lp] : -1;
+  }
+  int L = __builtin_amdgcn_readfirstlane(a.ctx_lens[b]);
+  L = L < 0 ? 0 : (L > a.max_ctx ? a.max_ctx : L);
+  const int N = L + a.K;
+  const int S_b = L > 0 ? (L + a.split - 1) / a.split : 1;
+  if (s >= S_b) return;
+  const int p_end = s == S_b - 1 ? N : p_begin + a.split;
+  const int ntiles = (p_end - p_begin + kTile - 1) / kTile;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int i = lane & 31, hi = lane >> 5;
+  const int hw = wave % G, sub = wave / G;
+  const int h = g * G + hw;
+
+  // ids outside [0, num_pages) read page 0 instead (results for such
+  // positions are unspecified, but every access stays in bounds)
+#pragma unroll
+  for (int k = 0; k < (kMaxSplit / kPage + NT - 1) / NT; ++k) {
+    const int x = tid + k * NT;
+    if (x < kMaxSplit / kPage) pages[x] = (pg[k] >= 0 && pg[k] < a.num_pages) ? pg[k] : 0;
+  }
+
+  typedef bf16x8 V8;
+  V8 qf[KS];
+  {
+    const char* qrow = a.q + ((size_t)(b * a.K + (i < a.K ? i : 0)) * a.Hq + h) * D * 2;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[ks] = __builtin_bit_cast(V8, ld16(qrow + (16 * ks + 8 * hi) * 2));
+      if (i >= a.K) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[ks][e] = (bf16)0.f;
+      }
+    }
+  }
+  __syncthreads();  // page ids visible (this also waits for the q loads)
+
+  f32x16 o[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[m][r] = 0.f;
+  float m_c = -INFINITY;
+  float l = 0.f;
+  const float c = a.c;
+
+  // lane constants of the LDS reads
+  // K, this wave's score tile, k-step ks: row 32 sub + i, chunk (2 ks + hi) ^ (row & KSW)
+  //   = ((32 sub + i) * ROWB + ((hi ^ (i & KSW)) << 4)) ^ (ks << 5)
+  const int kofs = (32 * sub + i) * Lay::ROWB + ((hi ^ (i & Lay::KSW)) << 4);
+  // V^T operand, 16-position step j, d block m, half hh: the lane supplies
+  // row 32 sub + 16 j + 8 hi + 4 hh + s16/4 and the 8 bytes at element
+  // 32 m + 16 ((lane/16) & 1) + 4 (s16 & 3); with the V swizzle this is
+  //   (32 sub + 16 j + 4 hh) * ROWB + (vofs ^ (m << 6))
+  const int s16 = lane & 15, g2 = (lane >> 4) & 1;
+  const int vrow = s16 >> 2;
+  const int vchunk = (2 * g2 + ((s16 >> 1) & 1)) ^ Lay::vswz(vrow);
+  const int vofs = (8 * hi + vrow) * Lay::ROWB + (vchunk << 4) + 8 * (s16 & 1);
+
+  // One stage = QK (scores of this wave's 32 positions), softmax, PV.  The
+  // scores of stage t+1 are computed during iteration t (software
+  // pipelining), and the two waves sharing a SIMD (the two halves of one
+  // head) run the phases in opposite orders, so one wave's MFMAs overlap the
+  // other's softmax VALU work.
+  auto qk = [&](const char* stage, f32x16& sc) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const V8 av = __builtin_bit_cast(V8, ld16(stage + (kofs ^ (ks << 5))));
+      sc = mfma_step(av, qf[ks], sc);
+    }
+  };
+  // scores -> probabilities (as the two 16-position B operands of PV)
+  auto softmax = [&](f32x16& sc, int pbase, V8& p0, V8& p1) {
+    // sc[r]: score of position pbase + 16(r/8) + 8hi + r%8 for row i
+    if (pbase + 32 > L) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int pos = pbase + 16 * (r >> 3) + 8 * hi + (r & 7);
+        bool vis;
+        if (MODE == ORTHRUS_DIFF_BIDIR) vis = pos < N;
+        else vis = pos < L || (pos < N && pos - L <= i);
+        if (!vis) sc[r] = -INFINITY;
+      }
+    }
+    float mx = sc[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+    mx = wave_max_xor32(mx);
+    const bool need = mx * c > m_c + kRescaleLog2;
+    if (__any(need)) {
+      const float new_mc = need ? mx * c : m_c;
+      const float f = (new_mc == m_c) ? 1.f : __builtin_amdgcn_exp2f(m_c - new_mc);
+#pragma unroll
+      for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[m][r] *= f;
+      l *= f;
+      m_c = new_mc;
+    }
+    const float mref = (m_c == -INFINITY) ? 0.f : m_c;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sc[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -mref));
+      l += sc[r];
+    }
+    p0 = pack_p<bf16>(sc, 0);
+    p1 = pack_p<bf16>(sc, 1);
+  };
+  auto pv = [&](const char* stage, const V8& p0, const V8& p1) {
+    const char* vt = stage + Lay::TILEB + 32 * sub * Lay::ROWB;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const char* vb = vt + 16 * j * Lay::ROWB;
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        const int off = vofs ^ (m << 6);
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((ORTHRUS_LDS bf16x4*)(vb + off));
+        const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((ORTHRUS_LDS bf16x4*)(vb + 4 * Lay::ROWB + off));
+        V8 av;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          av[e] = lo[e];
+          av[4 + e] = hi4[e];
+        }
+        o[m] = mfma_step(av, j == 0 ? p0 : p1, o[m]);
+      }
+    }
+  };
+
+  char* const ring[kRing] = {st0, st1, st2, st3};
+  // prologue: stages 0 .. kRing-2 in flight; scores of stage 0
+#pragma unroll
+  for (int u = 0; u < kRing - 1; ++u)
+    Plan::issue(ring[u], a, pages, page_base, b, g, L, p_end, p_begin + u * kTile, wave, lane);
+  if (ntiles > 2) wait_vmcnt<2 * Plan::NS>();
+  else wait_vmcnt<0>();
+  barrier_no_fence();
+  f32x16 s_cur;
+  qk(ring[0], s_cur);
+  const int my_lo = p_begin + 32 * sub;  // this wave's first position in a stage
+  for (int t0 = 0; t0 < ntiles; t0 += kRing) {
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) {
+      const int t = t0 + u;
+      if (t >= ntiles) break;
+      // stage t+1 must have landed (the loads of stage t+2 may still fly)
+      if (t + 2 < ntiles) wait_vmcnt<Plan::NS>();
+      else wait_vmcnt<0>();
+      barrier_no_fence();
+      Plan::issue(ring[(u + kRing - 1) % kRing], a, pages, page_base, b, g, L, p_end,
+                  p_begin + (t + kRing - 1) * kTile, wave, lane);
+      const char* cur = ring[u];
+      const char* nxt = ring[(u + 1) % kRing];
+      const bool has_next = t + 1 < ntiles;
+      const int pbase = my_lo + t * kTile;
+      const bool mine = pbase < p_end;  // this wave's half of stage t holds positions
+      f32x16 s_next = s_cur;  // overwritten by qk when a next stage exists
+      V8 p0, p1;
+      if (has_next) qk(nxt, s_next);
+      if (mine) {
+        softmax(s_cur, pbase, p0, p1);
+        pv(cur, p0, p1);
+      }
+      s_cur = s_next;
+    }
+  }
+
+  // merge the two halves of each head through LDS (O of heads 0,1 in st0,
+  // heads 2,3 in st1; max and sum in st2)
+  wait_vmcnt<0>();
+  __syncthreads();
+  float* mo = reinterpret_cast<float*>(hw < 2 ? st0 : st1) + (hw & 1) * (MB * 16) * kWave;
+  float* ml = reinterpret_cast<float*>(st2) + hw * 2 * kWave;
+  if (sub == 1) {
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mo[(m * 16 + r) * kWave + lane] = o[m][r];
+    ml[lane] = m_c;
+    ml[kWave + lane] = l;
+  }
+  __syncthreads();
+  if (sub == 1) return;
+  {
+    const float m1 = ml[lane], l1 = ml[kWave + lane];
+    const float mm = fmaxf(m_c, m1);
+    const float w0 = (m_c == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_c - mm);
+    const float w1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[m][r] = w0 * o[m][r] + w1 * mo[(m * 16 + r) * kWave + lane];
+    l = w0 * l + w1 * l1;
+    m_c = mm;
+  }
+  const float l_row = l + __shfl_xor(l, 32, kWave);
+  if (i >= a.K) return;
+  if (S_b == 1) {
+    const float inv = 1.f / l_row;
+    char* orow = a.out + ((size_t)(b * a.K + i) * a.Hq + h) * D * 2;
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d0 = 32 * m + 8 * rg + 4 * hi;
+        bf16x4 y;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = (bf16)(o[m][4 * rg + e] * inv);
+        *reinterpret_cast<bf16x4*>(orow + d0 * 2) = y;
+      }
+  } else {
+    const size_t prow = ((size_t)(b * a.Hq + h) * a.s_max + s) * kRows + i;
+    float* po = a.ws_o + prow * D;
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int d0 = 32 * m + 8 * rg + 4 * hi;
+        *reinterpret_cast<f32x4*>(po + d0) =
+            f32x4{o[m][4 * rg], o[m][4 * rg + 1], o[m][4 * rg + 2], o[m][4 * rg + 3]};
+      }
+    if (hi == 0) a.ws_ml[prow] = make_float2(m_c, l_row);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
@@ -437,23 +968,29 @@ __global__ void __launch_bounds__(256) attn_combine(AttnArgs a, int G) {
 static int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 
 int attn_split_tokens(const orthrus_attn_desc& d) {
-  const long N = (long)d.max_ctx_len + d.block_k;
-  const long n64 = ((N + kTile - 1) / kTile) * kTile;
-  if (d.split_tokens > 0) return (int)(d.split_tokens < n64 ? d.split_tokens : n64);
-  // aim for ~1024 work-groups at the longest context; keep splits >= 256
-  // positions so partial results stay small next to the KV bytes they cover
+  // splits partition the cached context (the last split also takes the K
+  // block keys)
+  const long Lm = d.max_ctx_len > 0 ? d.max_ctx_len : 1;
+  const long l64 = ((Lm + kTile - 1) / kTile) * kTile;
+  if (d.split_tokens > 0) return (int)(d.split_tokens < l64 ? d.split_tokens : l64);
+  // one work-group per CU and (b, g, split) unit at the longest context (one
+  // round of 256 work-groups), splits of 256..4096 positions
   const int units = d.batch * d.n_kv_heads;
-  const int s_target = units >= 1024 ? 1 : ceil_div(1024, units);
-  long split = ((ceil_div(N, s_target) + kTile - 1) / kTile) * kTile;
+  const int s_target = units >= 256 ? 1 : ceil_div(256, units);
+  long split = ((ceil_div(Lm, s_target) + kTile - 1) / kTile) * kTile;
   if (split < 256) split = 256;
-  if (split > kMaxSplit) split = kMaxSplit;
-  if (split > n64) split = n64;
+  if (split > 4096) split = 4096;
+  if (split > l64) split = l64;
   return (int)split;
+}
+
+static int attn_s_max(const orthrus_attn_desc& d, int split) {
+  return d.max_ctx_len > 0 ? ceil_div(d.max_ctx_len, split) : 1;
 }
 
 size_t attn_workspace_bytes(const orthrus_attn_desc& d) {
   const int split = attn_split_tokens(d);
-  const int s_max = ceil_div((long)d.max_ctx_len + d.block_k, split);
+  const int s_max = attn_s_max(d, split);
   if (s_max <= 1) return 0;
   const size_t rows = (size_t)d.batch * d.n_q_heads * s_max * kRows;
   return rows * d.head_dim * sizeof(float) + rows * sizeof(float2);
@@ -462,16 +999,23 @@ size_t attn_workspace_bytes(const orthrus_attn_desc& d) {
 template <typename T, int D, int G>
 static hipError_t launch_attn(const AttnArgs& a, int mode, hipStream_t stream) {
   const int grid = a.s_max * a.B * a.Hkv;
-  if (mode == ORTHRUS_DIFF_BIDIR)
-    hipLaunchKernelGGL((attn_main<T, D, G, ORTHRUS_DIFF_BIDIR>), dim3(grid), dim3(kWave * G), 0, stream, a);
-  else
-    hipLaunchKernelGGL((attn_main<T, D, G, ORTHRUS_AR_CAUSAL>), dim3(grid), dim3(kWave * G), 0, stream, a);
+  // bf16 with up to 4 query heads per KV head: the LDS-DMA streaming kernel;
+  // otherwise the register-staged kernel
+  constexpr bool stream_path = sizeof(T) == 2 && G <= 4;
+  if constexpr (stream_path) {
+    if (mode == ORTHRUS_DIFF_BIDIR)
+      hipLaunchKernelGGL((attn_stream<D, G, ORTHRUS_DIFF_BIDIR>), dim3(grid), dim3(2 * kWave * G), 0, stream, a);
+    else
+      hipLaunchKernelGGL((attn_stream<D, G, ORTHRUS_AR_CAUSAL>), dim3(grid), dim3(2 * kWave * G), 0, stream, a);
+  } else {
+    if (mode == ORTHRUS_DIFF_BIDIR)
+      hipLaunchKernelGGL((attn_main<T, D, G, ORTHRUS_DIFF_BIDIR>), dim3(grid), dim3(2 * kWave * G), 0, stream, a);
+    else
+      hipLaunchKernelGGL((attn_main<T, D, G, ORTHRUS_AR_CAUSAL>), dim3(grid), dim3(2 * kWave * G), 0, stream, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.s_max <= 1) return e;
-  constexpr int RPW = 256 / (D / 4);
-  const int cgrid = ((a.K + RPW - 1) / RPW) * G * a.B * a.Hkv;
-  hipLaunchKernelGGL((attn_combine<T, D>), dim3(cgrid), dim3(256), 0, stream, a, G);
-  return hipGetLastError();
+  return launch_combine<T, D>(a, stream);
 }
 
 template <typename T, int D>
@@ -530,7 +1074,7 @@ extern "C" orthrus_status orthrus_block_attn(const void* q, const void* k_cache,
   a.num_pages = d.num_pages;
   a.max_ctx = d.max_ctx_len;
   a.split = attn_split_tokens(d);
-  a.s_max = ceil_div((long)d.max_ctx_len + d.block_k, a.split);
+  a.s_max = attn_s_max(d, a.split);
   const size_t rows = (size_t)d.batch * d.n_q_heads * a.s_max * kRows;
   a.ws_o = need ? (float*)workspace : nullptr;
   a.ws_ml = need ? (float2*)((char*)workspace + rows * d.head_dim * sizeof(float)) : nullptr;

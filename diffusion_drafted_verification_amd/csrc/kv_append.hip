@@ -12,10 +12,14 @@
 namespace orthrus {
 
 struct AppendArgs {
-  char* k_cache;
+  char* k_cache;            // single layer: the tensors themselves
   char* v_cache;
   const char* k_blk;
   const char* v_blk;
+  const uint64_t* k_cache_list;  // several layers: device arrays of per-layer pointers
+  const uint64_t* v_cache_list;
+  const uint64_t* k_blk_list;
+  const uint64_t* v_blk_list;
   const int32_t* page_table;
   const int32_t* ctx_lens;
   const int32_t* accept_len;
@@ -25,7 +29,9 @@ struct AppendArgs {
 };
 
 __global__ void __launch_bounds__(256) kv_append_kernel(AppendArgs a) {
-  const int b = blockIdx.x / a.K, r = blockIdx.x % a.K;
+  const int layer = blockIdx.x / (a.B * a.K);
+  const int br = blockIdx.x % (a.B * a.K);
+  const int b = br / a.K, r = br % a.K;
   int L = a.ctx_lens[b];
   L = L < 0 ? 0 : (L > a.max_ctx ? a.max_ctx : L);
   int acc = a.accept_len[b];
@@ -39,11 +45,15 @@ __global__ void __launch_bounds__(256) kv_append_kernel(AppendArgs a) {
     page = lp < a.max_pages ? a.page_table[(size_t)b * a.max_pages + lp] : -1;
     if (page < 0 || page >= a.num_pages) write = false;
   }
-  if (threadIdx.x == 0) {
+  if (threadIdx.x == 0 && layer == 0) {
     if (a.slots) a.slots[b * a.K + r] = write ? page * kPage + pos % kPage : -1;
     if (r == 0 && a.new_ctx_lens) a.new_ctx_lens[b] = L + n;
   }
   if (!write) return;
+  char* k_cache = a.k_cache_list ? reinterpret_cast<char*>(a.k_cache_list[layer]) : a.k_cache;
+  char* v_cache = a.v_cache_list ? reinterpret_cast<char*>(a.v_cache_list[layer]) : a.v_cache;
+  const char* k_blk = a.k_blk_list ? reinterpret_cast<const char*>(a.k_blk_list[layer]) : a.k_blk;
+  const char* v_blk = a.v_blk_list ? reinterpret_cast<const char*>(a.v_blk_list[layer]) : a.v_blk;
   const int units = a.row_bytes / 16;  // per tensor: Hkv heads x D elements
   const size_t src_row = (size_t)(b * a.K + r) * a.row_bytes;
   for (int u = threadIdx.x; u < 2 * units; u += blockDim.x) {
@@ -51,9 +61,9 @@ __global__ void __launch_bounds__(256) kv_append_kernel(AppendArgs a) {
     const int g = uu / (a.head_bytes / 16), cc = uu % (a.head_bytes / 16);
     const size_t dst = ((size_t)(page * a.Hkv + g) * kPage + pos % kPage) * a.head_bytes + cc * 16;
     if (tensor == 0)
-      st16(a.k_cache + dst, ld16(a.k_blk + src_row + uu * 16));
+      st16(k_cache + dst, ld16(k_blk + src_row + uu * 16));
     else
-      st16(a.v_cache + dst, ld16(a.v_blk + src_row + uu * 16));
+      st16(v_cache + dst, ld16(v_blk + src_row + uu * 16));
   }
 }
 
@@ -63,23 +73,9 @@ __global__ void __launch_bounds__(256) copy_probe_kernel(u32x4* __restrict__ dst
   for (size_t k = (size_t)blockIdx.x * blockDim.x + threadIdx.x; k < n; k += stride) dst[k] = src[k];
 }
 
-}  // namespace orthrus
-
-using namespace orthrus;
-
-extern "C" orthrus_status orthrus_kv_append(void* k_cache, void* v_cache, const void* k_blk, const void* v_blk,
-                                            const int32_t* page_table, const int32_t* ctx_lens,
-                                            const int32_t* accept_len, int32_t* new_ctx_lens, int32_t* slots,
-                                            const orthrus_attn_desc* desc, void* stream) {
-  orthrus_status st = validate_desc(desc);
-  if (st != ORTHRUS_OK) return st;
-  if (!k_cache || !v_cache || !k_blk || !v_blk || !page_table || !ctx_lens || !accept_len) return ORTHRUS_ERR_NULL;
-  const orthrus_attn_desc& d = *desc;
-  AppendArgs a;
-  a.k_cache = (char*)k_cache;
-  a.v_cache = (char*)v_cache;
-  a.k_blk = (const char*)k_blk;
-  a.v_blk = (const char*)v_blk;
+static orthrus_status append_launch(AppendArgs& a, const orthrus_attn_desc& d, int n_layers,
+                                     const int32_t* page_table, const int32_t* ctx_lens, const int32_t* accept_len,
+                                     int32_t* new_ctx_lens, int32_t* slots, void* stream) {
   a.page_table = page_table;
   a.ctx_lens = ctx_lens;
   a.accept_len = accept_len;
@@ -94,8 +90,48 @@ extern "C" orthrus_status orthrus_kv_append(void* k_cache, void* v_cache, const 
   const int esz = d.dtype == ORTHRUS_BF16 ? 2 : 4;
   a.head_bytes = d.head_dim * esz;
   a.row_bytes = d.n_kv_heads * a.head_bytes;
-  hipLaunchKernelGGL(kv_append_kernel, dim3(d.batch * d.block_k), dim3(256), 0, (hipStream_t)stream, a);
+  const long grid = (long)n_layers * d.batch * d.block_k;
+  if (grid > 0x7fffffffL) return ORTHRUS_ERR_SHAPE;
+  hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)grid), dim3(256), 0, (hipStream_t)stream, a);
   return hipGetLastError() == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_LAUNCH;
+}
+
+}  // namespace orthrus
+
+using namespace orthrus;
+
+extern "C" orthrus_status orthrus_kv_append(void* k_cache, void* v_cache, const void* k_blk, const void* v_blk,
+                                            const int32_t* page_table, const int32_t* ctx_lens,
+                                            const int32_t* accept_len, int32_t* new_ctx_lens, int32_t* slots,
+                                            const orthrus_attn_desc* desc, void* stream) {
+  orthrus_status st = validate_desc(desc);
+  if (st != ORTHRUS_OK) return st;
+  if (!k_cache || !v_cache || !k_blk || !v_blk || !page_table || !ctx_lens || !accept_len) return ORTHRUS_ERR_NULL;
+  AppendArgs a = {};
+  a.k_cache = (char*)k_cache;
+  a.v_cache = (char*)v_cache;
+  a.k_blk = (const char*)k_blk;
+  a.v_blk = (const char*)v_blk;
+  return append_launch(a, *desc, 1, page_table, ctx_lens, accept_len, new_ctx_lens, slots, stream);
+}
+
+extern "C" orthrus_status orthrus_kv_append_layers(const uint64_t* k_cache_ptrs, const uint64_t* v_cache_ptrs,
+                                                   const uint64_t* k_blk_ptrs, const uint64_t* v_blk_ptrs,
+                                                   int32_t n_layers, const int32_t* page_table,
+                                                   const int32_t* ctx_lens, const int32_t* accept_len,
+                                                   int32_t* new_ctx_lens, int32_t* slots,
+                                                   const orthrus_attn_desc* desc, void* stream) {
+  orthrus_status st = validate_desc(desc);
+  if (st != ORTHRUS_OK) return st;
+  if (!k_cache_ptrs || !v_cache_ptrs || !k_blk_ptrs || !v_blk_ptrs || !page_table || !ctx_lens || !accept_len)
+    return ORTHRUS_ERR_NULL;
+  if (n_layers < 1 || n_layers > 4096) return ORTHRUS_ERR_SHAPE;
+  AppendArgs a = {};
+  a.k_cache_list = k_cache_ptrs;
+  a.v_cache_list = v_cache_ptrs;
+  a.k_blk_list = k_blk_ptrs;
+  a.v_blk_list = v_blk_ptrs;
+  return append_launch(a, *desc, n_layers, page_table, ctx_lens, accept_len, new_ctx_lens, slots, stream);
 }
 
 extern "C" orthrus_status orthrus_copy_probe(void* dst, const void* src, size_t bytes, void* stream) {

@@ -46,6 +46,7 @@ SIGNATURES = {
     "orthrus_greedy_accept_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "orthrus_greedy_accept": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
     "orthrus_kv_append": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _DESC_P, _vp]),
+    "orthrus_kv_append_layers": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _DESC_P, _vp]),
     "orthrus_copy_probe": (_i32, [_vp, _vp, _sz, _vp]),
 }
 
@@ -210,6 +211,51 @@ def kv_append(k_cache, v_cache, k_blk, v_blk, page_table, ctx_lens, accept_len, 
                                  _ptr(ctx_lens), _ptr(accept_len), _ptr(new_ctx_lens), _ptr(slots),
                                  ctypes.byref(desc), _stream(stream))
     _check(st, "orthrus_kv_append")
+    return new_ctx_lens, slots
+
+
+class LayerPointers:
+    """Device arrays of per-layer cache and block K/V addresses for
+    kv_append_layers (built once per set of tensors)."""
+
+    def __init__(self, k_caches, v_caches, k_blks, v_blks):
+        self.tensors = (list(k_caches), list(v_caches), list(k_blks), list(v_blks))
+        n = len(self.tensors[0])
+        if not all(len(t) == n for t in self.tensors) or n == 0:
+            raise OrthrusError("one tensor of each kind per layer")
+        dev = _gpu(*[t for ts in self.tensors for t in ts])
+        ref = self.tensors[0][0]
+        for ts in self.tensors[:2]:
+            if any(t.shape != ref.shape or t.dtype != ref.dtype for t in ts):
+                raise OrthrusError("all layer caches must share one shape and dtype")
+        kb = self.tensors[2][0]
+        for ts in self.tensors[2:]:
+            if any(t.shape != kb.shape or t.dtype != ref.dtype for t in ts):
+                raise OrthrusError("all layer block K/V must share one shape and the cache dtype")
+        self.n_layers = n
+        self.ptrs = [torch.tensor([t.data_ptr() for t in ts], dtype=torch.int64, device=dev)
+                     for ts in self.tensors]
+
+
+def kv_append_layers(layers, page_table, ctx_lens, accept_len, *, new_ctx_lens=None, slots=None,
+                     want_outputs=True, max_ctx_len=None, stream=None):
+    """orthrus_kv_append_layers over a LayerPointers set: one launch appends
+    the accepted rows of every layer."""
+    k0, kb0 = layers.tensors[0][0], layers.tensors[2][0]
+    dev = _gpu(k0, page_table, ctx_lens, accept_len)
+    B, K, Hkv, D = kb0.shape
+    if want_outputs:
+        if new_ctx_lens is None:
+            new_ctx_lens = torch.empty(B, dtype=torch.int32, device=dev)
+        if slots is None:
+            slots = torch.empty((B, K), dtype=torch.int32, device=dev)
+    qlike = torch.empty((B, K, Hkv, D), dtype=kb0.dtype, device="meta")
+    desc = make_desc(qlike, k0, page_table, max_ctx_len)
+    kp, vp, kbp, vbp = layers.ptrs
+    st = lib().orthrus_kv_append_layers(_ptr(kp), _ptr(vp), _ptr(kbp), _ptr(vbp), layers.n_layers, _ptr(page_table),
+                                        _ptr(ctx_lens), _ptr(accept_len), _ptr(new_ctx_lens), _ptr(slots),
+                                        ctypes.byref(desc), _stream(stream))
+    _check(st, "orthrus_kv_append_layers")
     return new_ctx_lens, slots
 
 

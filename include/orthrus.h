@@ -159,6 +159,17 @@ orthrus_status orthrus_kv_append(void* k_cache, void* v_cache, const void* k_blk
                                  const int32_t* accept_len, int32_t* new_ctx_lens, int32_t* slots,
                                  const orthrus_attn_desc* desc, void* stream);
 
+/* orthrus_kv_append for n_layers layers in one launch.  The four arguments
+ * *_ptrs are DEVICE arrays of n_layers device addresses (layer l's k_cache,
+ * v_cache, k_blk, v_blk); every layer shares page_table, ctx_lens and
+ * accept_len (one step commits the same positions in every layer).
+ * new_ctx_lens and slots are written once.  1 <= n_layers <= 4096. */
+orthrus_status orthrus_kv_append_layers(const uint64_t* k_cache_ptrs, const uint64_t* v_cache_ptrs,
+                                        const uint64_t* k_blk_ptrs, const uint64_t* v_blk_ptrs, int32_t n_layers,
+                                        const int32_t* page_table, const int32_t* ctx_lens,
+                                        const int32_t* accept_len, int32_t* new_ctx_lens, int32_t* slots,
+                                        const orthrus_attn_desc* desc, void* stream);
+
 /* Measurement helper: streams `bytes` (a multiple of 16) from src to dst with
  * plain 16-byte loads and stores.  Used to calibrate hardware counters and to
  * measure the achievable HBM rate; not part of the decode step. */

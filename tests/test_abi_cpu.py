@@ -24,7 +24,7 @@ def declared_entry_points():
 
 def test_exports_every_declared_symbol():
     names = declared_entry_points()
-    assert len(names) == 9
+    assert len(names) == 10
     assert set(names) == set(B.SIGNATURES)
     lib = B.lib()
     for n in names:
@@ -86,7 +86,7 @@ def test_split_and_workspace_arithmetic():
     d = good_desc()
     split = lib.orthrus_block_attn_split_tokens(ctypes.byref(d))
     assert split % 64 == 0 and 64 <= split <= 8192
-    s_max = -(-(8192 + 32) // split)
+    s_max = -(-8192 // split)           # splits partition the cached context
     rows = 1 * 32 * s_max * 32
     assert lib.orthrus_block_attn_workspace_bytes(ctypes.byref(d)) == rows * 128 * 4 + rows * 8
     d1 = good_desc(split_tokens=8192, max_ctx_len=100)      # one split: no workspace
@@ -99,13 +99,18 @@ def test_accept_and_append_validation():
     assert lib.orthrus_greedy_accept(FAKE, FAKE, FAKE, FAKE, None, 1, 33, 100, FAKE, 1 << 20, None) == 2
     assert lib.orthrus_greedy_accept(FAKE, FAKE, FAKE, FAKE, None, 1, 32, 0, FAKE, 1 << 20, None) == 2
     need = lib.orthrus_greedy_accept_workspace_bytes(2, 32, 151936)
-    assert need == 2 * 32 * 8 + 16
+    # chunk keys (64 rows x 19 chunks x 8 B), tokens, row and sequence tickets, 256-B aligned
+    assert need == 9728 + 256 + 256 + 256
     assert lib.orthrus_greedy_accept(FAKE, FAKE, FAKE, FAKE, None, 2, 32, 151936, FAKE, need - 1, None) == 4
     assert lib.orthrus_greedy_accept(FAKE, FAKE, FAKE, FAKE, None, 2, 32, 151936, None, need, None) == 4
     d = good_desc()
     assert lib.orthrus_kv_append(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, None, ctypes.byref(d), None) == 1
     assert lib.orthrus_kv_append(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
                                  ctypes.byref(good_desc(head_dim=80)), None) == 3
+    assert lib.orthrus_kv_append_layers(FAKE, FAKE, FAKE, None, 36, FAKE, FAKE, FAKE, None, None,
+                                        ctypes.byref(d), None) == 1
+    assert lib.orthrus_kv_append_layers(FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, None, None,
+                                        ctypes.byref(d), None) == 2
     assert lib.orthrus_copy_probe(FAKE, FAKE, 17, None) == 2
     assert lib.orthrus_copy_probe(None, FAKE, 16, None) == 1
 

@@ -269,6 +269,26 @@ def test_accept_unaligned_vocab(V):
     check_accept(x, drafts)
 
 
+def test_accept_workspace_reused_across_shapes():
+    """A workspace used by a large call serves a smaller call of another
+    shape (the kernel leaves every workspace word zero)."""
+    say("accept shapes")
+    from diffusion_drafted_verification_amd import orthrus as ob
+    d = dev()
+    ws = torch.zeros(ob.lib().orthrus_greedy_accept_workspace_bytes(16, 32, 151936), dtype=torch.uint8, device=d)
+    for (B, K, V) in [(16, 32, 151936), (4, 32, 151936), (1, 1, 64), (3, 7, 20000), (16, 32, 151936)]:
+        x = torch.randn(B, K, V, generator=torch.Generator().manual_seed(B * K))
+        g = torch.from_numpy(O.greedy_argmax(x.numpy())).int()
+        dr = g.clone()
+        dr[:, K // 2] += 1
+        acc, nxt, tok = ob.greedy_accept(x.to(d), dr.to(d), ws=ws)
+        ra, rn, rg = O.greedy_accept(x.numpy(), dr.numpy())
+        assert np.array_equal(tok.cpu().numpy(), rg) and np.array_equal(acc.cpu().numpy(), ra)
+        assert np.array_equal(nxt.cpu().numpy(), rn)
+        torch.cuda.synchronize()
+        assert int(ws.count_nonzero().item()) == 0
+
+
 def test_accept_workspace_is_reset_between_calls():
     say("accept repeat")
     for s in range(4):
@@ -320,6 +340,34 @@ def test_append_fp32():
     say("append fp32")
     inp = I.make_attn_inputs("tiny_fp32")
     check_append(inp, [12])
+
+
+def test_append_layers_matches_per_layer_oracle():
+    """One multi-layer launch writes every layer's accepted rows exactly like
+    the per-layer definition; context lengths and slots are written once."""
+    say("append layers")
+    d = dev()
+    ob = K_()
+    n_layers = 5
+    base = I.make_attn_inputs("qwen3_8b_ragged16", batch=4)
+    acc = torch.tensor([0, 31, 32, 7], dtype=torch.int32)
+    kcs, vcs, kbs, vbs = [], [], [], []
+    for l in range(n_layers):
+        x = I.make_attn_inputs("qwen3_8b_ragged16", batch=4, layer=l, ctx_lens=base.ctx_lens.numpy())
+        kcs.append(torch.full_like(x.k_cache, float(l)).to(d))
+        vcs.append(torch.full_like(x.v_cache, -float(l)).to(d))
+        kbs.append(x.k_blk.to(d))
+        vbs.append(x.v_blk.to(d))
+    lp = ob.LayerPointers(kcs, vcs, kbs, vbs)
+    nl, sl = ob.kv_append_layers(lp, base.page_table.to(d), base.ctx_lens.to(d), acc.to(d),
+                                 max_ctx_len=base.max_ctx_len)
+    torch.cuda.synchronize()
+    for l in range(n_layers):
+        rk, rv, rl, rs = O.kv_append(torch.full_like(base.k_cache, float(l)), torch.full_like(base.v_cache, -float(l)),
+                                     kbs[l].cpu(), vbs[l].cpu(), base.page_table, base.ctx_lens, acc.numpy())
+        assert np.array_equal(kcs[l].cpu().view(torch.int16).numpy(), rk)
+        assert np.array_equal(vcs[l].cpu().view(torch.int16).numpy(), rv)
+        assert np.array_equal(nl.cpu().numpy(), rl) and np.array_equal(sl.cpu().numpy(), rs)
 
 
 # ---------------------------------------------------------------------------
@@ -392,10 +440,13 @@ def test_lossless_loop_on_gpu():
             att = ob.block_attn(q, kc, vc, k, v, table, L, AR, max_ctx_len=n_pages * 16 - Kb)
             logits = (att.view(Kb, Hq * D) @ wo + x @ wu).view(1, Kb, V).contiguous()
             acc, nxt, g = ob.greedy_accept(logits, torch.tensor([drafts], dtype=torch.int32, device=d))
-            n = min(int(acc.item()) + 1, Kb)
-            out.extend(g[0, :n].tolist())
+            a_h, nxt_h, g_h = int(acc.item()), int(nxt.item()), g[0].tolist()
+            # range-check before any value is used as an index
+            assert 0 <= a_h <= Kb and 0 <= nxt_h < V and all(0 <= t < V for t in g_h)
+            n = min(a_h + 1, Kb)
+            out.extend(g_h[:n])
             L, _ = ob.kv_append(kc, vc, k, v, table, L, acc, max_ctx_len=n_pages * 16 - Kb)
-            anchor = int(nxt.item())
+            anchor = nxt_h
             steps += 1
         return out[:n_new], steps
 
