@@ -22,6 +22,7 @@ on the host cores.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -46,6 +47,8 @@ def parse():
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a graph")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="run one plain device copy of this size first (calibrates HBM byte counters)")
     return p.parse_args()
 
 
@@ -141,6 +144,33 @@ def attn_only_ms(torch, step, mode, use_graph, iters=20, warmup=3):
     return time_region(torch, rep, iters, warmup) / step.layers
 
 
+TRAFFIC_FILE = os.path.join("diffusion_drafted_verification_amd", "traffic_counters.json")
+ATTN_SOURCES = ("block_attn.hip", "orthrus_device.h", "orthrus_host.h")
+
+
+def attn_source_sha(root):
+    h = hashlib.sha256()
+    for f in ATTN_SOURCES:
+        with open(os.path.join(root, "diffusion_drafted_verification_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(root, batch, ctx):
+    """HBM bytes per block-attention call from the committed FETCH_SIZE /
+    WRITE_SIZE counter runs, if they were taken on the current kernel
+    sources at this workload; else None."""
+    path = os.path.join(root, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        d = json.load(fh)
+    if d.get("attn_source_sha256") != attn_source_sha(root):
+        return None
+    w = d.get("workloads", {}).get(f"b{batch}_ctx{ctx}")
+    return None if w is None else int(w["hbm_bytes_per_call"])
+
+
 def cpu_baseline(step, I, seconds):
     """The fp64 oracle, as is, on one layer of the step (both views, accept,
     append) at the same shapes; repeated for about `seconds`."""
@@ -195,6 +225,13 @@ def main():
     split = ob.lib().orthrus_block_attn_split_tokens(
         ob.make_desc(step.L[0]["q_diff"], step.L[0]["k_cache"], step.page_table, step.max_ctx, None,
                      args.split_tokens))
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n // 4, dtype=torch.int32, device="cuda:0")
+        dst = torch.empty_like(src)
+        ob.copy_probe(dst, src)
+        torch.cuda.synchronize()
+        del src, dst
     step.run()
     torch.cuda.synchronize()
     rep = capture(torch, step.run) if use_graph else step.run
@@ -210,7 +247,8 @@ def main():
     achieved = step.kv_bytes_call / (ms_call * 1e-3) / 1e9
     flops = 2 * 2 * step.B * step.K * step.Hq * step.D * (args.ctx + step.K)
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(ROOT, args.batch, args.ctx),
             "kernel": "block_attn call (attn_main + attn_combine)", "us_per_call": round(ms_call * 1e3, 3),
             "us_diff": round(ms_diff * 1e3, 3), "us_ar": round(ms_ar * 1e3, 3),
             "bytes_per_call": step.kv_bytes_call, "split_tokens": split,

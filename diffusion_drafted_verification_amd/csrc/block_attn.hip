@@ -8,14 +8,16 @@
 //
 // How (MI355X-first; the flash-attention dependency the pages name is prior
 // art for other hardware, not the blueprint):
-//   * one work-group per (sequence b, KV head g, context split s); its G waves
-//     are the G query heads sharing KV head g, so each KV byte is read from HBM
-//     once and feeds a (G x 32)-row tile;
-//   * context positions stream through LDS in 64-token stages (double
-//     buffered, register-staged prefetch of the next stage); K is kept
-//     token-major with an XOR chunk swizzle, V is stored transposed so both
-//     MFMA operands are single 16-byte LDS reads;
-//   * S^T = K Q^T and O^T = V^T P^T on v_mfma_f32_32x32x16_bf16 with fp32
+//   * one work-group per (sequence b, KV head g, context split s) with 2G
+//     waves: the G query heads sharing KV head g times the two 32-position
+//     halves of each 64-position stage, so each KV byte is read from HBM once
+//     and feeds a (G x 32)-row tile;
+//   * bf16 with G <= 4 (attn_stream): context stages go HBM -> LDS by LDS-DMA
+//     (no staging registers) through a ring of kRing stages; K and V both stay
+//     token-major with XOR chunk swizzles, V is read back transposed by
+//     ds_read_b64_tr_b16.  fp32 and G = 8 (attn_main): a register-staged
+//     double buffer, V transposed when it is written to LDS;
+//   * S^T = K Q^T and O^T = V^T P^T on MFMA 32x32 tiles with fp32
 //     accumulation: the score tile's accumulator layout is directly the B
 //     operand of the PV product (no shuffles), and every lane owns one query
 //     row, so row rescales are per-lane multiplies;
@@ -680,10 +682,10 @@ struct DmaPlan {
   }
 };
 
-// wait until at most N of this wave's vector loads are outstanding; issued
-// through the builtin so the compiler's own wait tracking knows about it
-// (gfx9 encoding: vmcnt low bits [3:0], high bits [15:14]; expcnt and
-// lgkmcnt left at their maxima)
+// wait until at most N of this wave's vector loads are outstanding.  Inline
+// assembly, like the DMA itself: the compiler does not count the DMA loads, so
+// the kernel places these waits by hand (only LDS-DMA loads are in flight
+// where they are used).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
