@@ -25,10 +25,11 @@
 //     only the row max needs one cross-lane exchange per 32 keys;
 //   * the block tile and the ragged context tail are the only masked tiles;
 //     the mask mode is a template parameter;
-//   * when a sequence is split over several work-groups each writes fp32
-//     partials (unnormalised O, running max, sum) and a combine kernel merges
-//     them; the work-group order puts all splits of one (b, g) on one XCD so
-//     the partials stay in that XCD's L2.
+//   * when a sequence is split over several work-groups each writes a
+//     partial (bf16 O / l on the streaming path, fp32 O otherwise, plus the
+//     row's max and sum) and a combine kernel merges them; the work-group
+//     order puts all splits of one (b, g) on one XCD so the partials stay in
+//     that XCD's L2.
 #include <type_traits>
 
 #include "orthrus_device.h"
@@ -51,7 +52,9 @@ struct AttnArgs {
   const int32_t* page_table;
   const int32_t* ctx_lens;
   char* out;
-  float* ws_o;      // [B, Hq, s_max, 32, D]  unnormalised partial outputs
+  // split partials for attn_combine, one slot per (b, h, split, row):
+  float* ws_o;      // [B, Hq, s_max, 32, D]  register-staged kernel: unnormalised O (fp32)
+  bf16* ws_p;       // [B, Hq, s_max, 32, D]  streaming kernel: normalised O / l (bf16)
   float2* ws_ml;    // [B, Hq, s_max, 32]     (running max in log2 units, row sum)
   int B, K, Hq, Hkv, max_pages, num_pages, max_ctx, split, s_max;
   float c;          // softmax scale * log2(e)
@@ -443,14 +446,15 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_main(AttnArgs a) {
 }
 
 // Merge the split partials of sequences whose context spans several
-// work-groups: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// work-groups: out = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, where
+// O_s is stored unnormalised (fp32) or as O_s / l_s (bf16, NORM).
 // A row (b, i, h) is served by SG groups of D/4 lanes (4 outputs per lane);
 // group q takes splits q, q+SG, ... and issues all of its loads before
 // reducing; the groups of a row then merge (shuffles within a wave, LDS
 // otherwise).  A work-group covers 256 / (SG D/4) consecutive rows of one
 // (b, g); block id = chunk * (B Hkv) + b Hkv + g, so the rows of one (b, g)
 // run on the XCD that wrote its partials (when B Hkv % 8 == 0).
-template <typename T, int D, int SG>
+template <typename T, int D, int SG, bool NORM>
 __global__ void __launch_bounds__(256) attn_combine(AttnArgs a) {
   constexpr int TPR = D / 4;          // lanes per group
   constexpr int LPR = TPR * SG;       // lanes per row
@@ -486,7 +490,13 @@ __global__ void __launch_bounds__(256) attn_combine(AttnArgs a) {
       const int s = s0 + k * SG;
       const size_t r = base + (size_t)(s < S_b ? s : 0) * kRows;
       ml[k] = a.ws_ml[r];
-      xo[k] = *reinterpret_cast<const f32x4*>(a.ws_o + r * D + d0);
+      if constexpr (NORM) {  // bf16 O / l: weight by the split's row sum
+        const bf16x4 y = *reinterpret_cast<const bf16x4*>(a.ws_p + r * D + d0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xo[k][e] = (float)y[e] * ml[k].y;
+      } else {
+        xo[k] = *reinterpret_cast<const f32x4*>(a.ws_o + r * D + d0);
+      }
       if (s >= S_b) ml[k].x = -INFINITY;
     }
     float mnew = M;
@@ -551,14 +561,14 @@ __global__ void __launch_bounds__(256) attn_combine(AttnArgs a) {
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool NORM>
 static hipError_t launch_combine(const AttnArgs& a, hipStream_t stream) {
   const int rows = (a.Hq / a.Hkv) * a.K;  // per (b, g)
   auto go = [&](auto sg_tag) {
     constexpr int SG = decltype(sg_tag)::value;
     constexpr int RPB = 256 / ((D / 4) * SG);
     const int chunks = (rows + RPB - 1) / RPB;
-    hipLaunchKernelGGL((attn_combine<T, D, SG>), dim3(chunks * a.B * a.Hkv), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((attn_combine<T, D, SG, NORM>), dim3(chunks * a.B * a.Hkv), dim3(256), 0, stream, a);
   };
   if (a.s_max >= 16) go(std::integral_constant<int, 256 / (D / 4)>());
   else if (a.s_max >= 3) go(std::integral_constant<int, 2>());
@@ -628,16 +638,20 @@ struct DmaPlan {
   }
 
   // the whole stage lies in the cached context (invalid page ids were
-  // replaced by page 0)
+  // replaced by page 0).  The stage is page aligned, so its four page ids are
+  // one 16-byte LDS read, done before the first DMA of the stage.
   __device__ static void issue_cached(char* st, const AttnArgs& a, const int* pages, int page_base, int g, int p0,
                                       int wave, int lane) {
+    const int4 pq = *reinterpret_cast<const int4*>(pages + ((p0 >> 4) - page_base));
+    const int pid0 = __builtin_amdgcn_readfirstlane(pq.x), pid1 = __builtin_amdgcn_readfirstlane(pq.y);
+    const int pid2 = __builtin_amdgcn_readfirstlane(pq.z), pid3 = __builtin_amdgcn_readfirstlane(pq.w);
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
       const int q = wave + NW * k;
       if (NI % NW != 0 && q >= NI) break;
       const int ten = q / Lay::IPT, ii = q % Lay::IPT;
-      const int tok0 = ten == 0 ? swap_bits23(ii * Lay::RPI) : ii * Lay::RPI;  // rows share one page
-      const int page = __builtin_amdgcn_readfirstlane(pages[((p0 + tok0) >> 4) - page_base]);
+      const int slot = (ii * Lay::RPI) >> 4;  // the instruction's rows share one page
+      const int page = slot == 0 ? pid0 : slot == 1 ? pid1 : slot == 2 ? pid2 : pid3;
       const char* base = (ten == 0 ? a.k_cache : a.v_cache) + (size_t)(page * a.Hkv + g) * (kPage * Lay::ROWB);
       char* dst = st + ten * Lay::TILEB + ii * 1024;
       dma16(base + voff(wave, lane, k), dst);
@@ -716,14 +730,14 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_stream(AttnArgs a) {
   constexpr int NT = kWave * NW;
   constexpr int KS = D / 16;
   constexpr int MB = D / 32;
-  static_assert(MB * 16 * kWave * 4 * 2 <= Lay::STAGE, "merge area: two heads per stage buffer");
-  static_assert(G <= 4, "merge area covers four heads");
+  static_assert(4 * (MB / 2) * 16 * kWave * 4 <= Lay::STAGE, "exchange area: four waves per stage buffer");
+  static_assert(G <= 4, "exchange areas cover eight waves");
 
   __shared__ __attribute__((aligned(1024))) char st0[Lay::STAGE];
   __shared__ __attribute__((aligned(1024))) char st1[Lay::STAGE];
   __shared__ __attribute__((aligned(1024))) char st2[Lay::STAGE];
   __shared__ __attribute__((aligned(1024))) char st3[Lay::STAGE];
-  __shared__ int pages[kMaxSplit / kPage];
+  __shared__ __attribute__((aligned(16))) int pages[kMaxSplit / kPage];
 
   const int BH = a.B * a.Hkv;
   const int bg = blockIdx.x % BH;
@@ -732,6 +746,16 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_stream(AttnArgs a) {
   const int tid = threadIdx.x;
   const int p_begin = s * a.split;
   const int page_base = p_begin >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int i = lane & 31, hi = lane >> 5;
+  const int hw = wave % G, sub = wave / G;
+  const int h = g * G + hw;
+
+  // Page ids, context length and this wave's query rows are loaded together
+  // and consumed (zeroing, LDS store) before the first K/V DMA is issued, so
+  // the prologue costs one global-memory latency and no compiler-placed wait
+  // on these loads can later stall behind the DMA (the compiler does not
+  // count the DMA loads).
   int pg[(kMaxSplit / kPage + NT - 1) / NT];
 #pragma unroll
   for (int k = 0; k < (kMaxSplit / kPage + NT - 1) / NT; ++k) {
@@ -739,16 +763,19 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_stream(AttnArgs a) {
     pg[k] = (x < a.split / kPage && lp < a.max_pages) ? a.page_table[(size_t)b * a.max_pages + lp] : -1;
   }
   int L = __builtin_amdgcn_readfirstlane(a.ctx_lens[b]);
+  typedef bf16x8 V8;
+  V8 qf[KS];
+  {
+    const char* qrow = a.q + ((size_t)(b * a.K + (i < a.K ? i : 0)) * a.Hq + h) * D * 2;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(V8, ld16(qrow + (16 * ks + 8 * hi) * 2));
+  }
   L = L < 0 ? 0 : (L > a.max_ctx ? a.max_ctx : L);
   const int N = L + a.K;
   const int S_b = L > 0 ? (L + a.split - 1) / a.split : 1;
   if (s >= S_b) return;
   const int p_end = s == S_b - 1 ? N : p_begin + a.split;
   const int ntiles = (p_end - p_begin + kTile - 1) / kTile;
-  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
-  const int i = lane & 31, hi = lane >> 5;
-  const int hw = wave % G, sub = wave / G;
-  const int h = g * G + hw;
 
   // ids outside [0, num_pages) read page 0 instead (results for such
   // positions are unspecified, but every access stays in bounds)
@@ -757,21 +784,16 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_stream(AttnArgs a) {
     const int x = tid + k * NT;
     if (x < kMaxSplit / kPage) pages[x] = (pg[k] >= 0 && pg[k] < a.num_pages) ? pg[k] : 0;
   }
-
-  typedef bf16x8 V8;
-  V8 qf[KS];
-  {
-    const char* qrow = a.q + ((size_t)(b * a.K + (i < a.K ? i : 0)) * a.Hq + h) * D * 2;
+  // all of the above loads complete here, before any DMA is in flight; the
+  // builtin (not inline assembly) so that the compiler's own wait tracking
+  // knows the query registers are ready (gfx9 encoding: vmcnt(0), expcnt and
+  // lgkmcnt at their maxima)
+  __builtin_amdgcn_s_waitcnt(0x0F70);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      qf[ks] = __builtin_bit_cast(V8, ld16(qrow + (16 * ks + 8 * hi) * 2));
-      if (i >= a.K) {
+  for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qf[ks][e] = (bf16)0.f;
-      }
-    }
-  }
-  __syncthreads();  // page ids visible (this also waits for the q loads)
+    for (int e = 0; e < 8; ++e) qf[ks][e] = i < a.K ? qf[ks][e] : (bf16)0.f;
+  __syncthreads();  // page ids visible
 
   f32x16 o[MB];
 #pragma unroll
@@ -797,9 +819,7 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_stream(AttnArgs a) {
 
   // One stage = QK (scores of this wave's 32 positions), softmax, PV.  The
   // scores of stage t+1 are computed during iteration t (software
-  // pipelining), and the two waves sharing a SIMD (the two halves of one
-  // head) run the phases in opposite orders, so one wave's MFMAs overlap the
-  // other's softmax VALU work.
+  // pipelining), so their MFMAs can overlap this stage's softmax VALU work.
   auto qk = [&](const char* stage, f32x16& sc) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc[r] = 0.f;
@@ -875,8 +895,13 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_stream(AttnArgs a) {
   if (ntiles > 2) wait_vmcnt<2 * Plan::NS>();
   else wait_vmcnt<0>();
   barrier_no_fence();
-  f32x16 s_cur;
-  qk(ring[0], s_cur);
+  // scores of stage t live in scores[t & 1] (kRing is even, so the parity is
+  // a compile-time constant in the unrolled body)
+  static_assert(kRing % 2 == 0, "score double buffer alternates with the ring");
+  f32x16 scores[2];
+  qk(ring[0], scores[0]);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) scores[1][r] = 0.f;
   const int my_lo = p_begin + 32 * sub;  // this wave's first position in a stage
   for (int t0 = 0; t0 < ntiles; t0 += kRing) {
 #pragma unroll
@@ -891,76 +916,99 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_stream(AttnArgs a) {
                   p_begin + (t + kRing - 1) * kTile, wave, lane);
       const char* cur = ring[u];
       const char* nxt = ring[(u + 1) % kRing];
-      const bool has_next = t + 1 < ntiles;
       const int pbase = my_lo + t * kTile;
       const bool mine = pbase < p_end;  // this wave's half of stage t holds positions
-      f32x16 s_next = s_cur;  // overwritten by qk when a next stage exists
       V8 p0, p1;
-      if (has_next) qk(nxt, s_next);
+      if (t + 1 < ntiles) qk(nxt, scores[(u + 1) & 1]);
       if (mine) {
-        softmax(s_cur, pbase, p0, p1);
+        softmax(scores[u & 1], pbase, p0, p1);
         pv(cur, p0, p1);
       }
-      s_cur = s_next;
     }
   }
 
-  // merge the two halves of each head through LDS (O of heads 0,1 in st0,
-  // heads 2,3 in st1; max and sum in st2)
+  // ---- epilogue.  The two 32-position halves of each head (sub 0, sub 1)
+  // are merged through LDS; afterwards sub 0 owns d blocks [0, MB/2) of the
+  // head and sub 1 owns [MB/2, MB).  Both evaluate the row statistics with
+  // the same expression (sub 0's values first), so they agree bit for bit.
   wait_vmcnt<0>();
-  __syncthreads();
-  float* mo = reinterpret_cast<float*>(hw < 2 ? st0 : st1) + (hw & 1) * (MB * 16) * kWave;
-  float* ml = reinterpret_cast<float*>(st2) + hw * 2 * kWave;
-  if (sub == 1) {
-#pragma unroll
-    for (int m = 0; m < MB; ++m)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mo[(m * 16 + r) * kWave + lane] = o[m][r];
-    ml[lane] = m_c;
-    ml[kWave + lane] = l;
-  }
-  __syncthreads();
-  if (sub == 1) return;
+  __syncthreads();  // the ring is free
+  constexpr int MH = MB / 2;
+  // exchange areas: wave slot k = 2 hw + sub; slots 0-3 in st0, 4-7 in st1
+  auto xslot = [&](int k) {
+    return reinterpret_cast<float*>(k < 4 ? st0 : st1) + (k & 3) * (MH * 16) * kWave;
+  };
   {
-    const float m1 = ml[lane], l1 = ml[kWave + lane];
-    const float mm = fmaxf(m_c, m1);
-    const float w0 = (m_c == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_c - mm);
-    const float w1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
+    float* xo = xslot(hw * 2 + sub);
+    float* xm = reinterpret_cast<float*>(st2) + (hw * 2 + sub) * 2 * kWave;
+    // the half the partner keeps (selects, not a runtime index, keep o in
+    // registers)
 #pragma unroll
-    for (int m = 0; m < MB; ++m)
+    for (int mm = 0; mm < MH; ++mm)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) o[m][r] = w0 * o[m][r] + w1 * mo[(m * 16 + r) * kWave + lane];
-    l = w0 * l + w1 * l1;
-    m_c = mm;
+      for (int r = 0; r < 16; ++r) xo[(mm * 16 + r) * kWave + lane] = sub == 0 ? o[MH + mm][r] : o[mm][r];
+    xm[lane] = m_c;
+    xm[kWave + lane] = l;
   }
-  const float l_row = l + __shfl_xor(l, 32, kWave);
-  if (i >= a.K) return;
+  __syncthreads();
+  f32x16 oh[MH];
+  float row_m, row_l;
+  {
+    const int other = 1 - sub;
+    const float* yo = xslot(hw * 2 + other);
+    const float* ym = reinterpret_cast<const float*>(st2) + (hw * 2 + other) * 2 * kWave;
+    const float m1 = ym[lane], l1 = ym[kWave + lane];
+    const float mA = sub == 0 ? m_c : m1, mB = sub == 0 ? m1 : m_c;
+    const float lA = sub == 0 ? l : l1, lB = sub == 0 ? l1 : l;
+    const float mm_ = fmaxf(mA, mB);
+    const float wA = (mA == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mA - mm_);
+    const float wB = (mB == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mB - mm_);
+#pragma unroll
+    for (int mm = 0; mm < MH; ++mm)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float own = sub == 0 ? o[mm][r] : o[MH + mm][r], oth = yo[(mm * 16 + r) * kWave + lane];
+        oh[mm][r] = sub == 0 ? wA * own + wB * oth : wA * oth + wB * own;
+      }
+    const float lh = wA * lA + wB * lB;  // this lane's half of the row sum
+    row_l = lh + __shfl_xor(lh, 32, kWave);
+    row_m = mm_;
+  }
+  const float inv = 1.f / row_l;
+  // lane (i, hi) holds, for d block m = sub * MH + mm, the elements
+  // d = 32 m + 8 rg + 4 hi + e at oh[mm][4 rg + e]
   if (S_b == 1) {
-    const float inv = 1.f / l_row;
+    if (i >= a.K) return;
     char* orow = a.out + ((size_t)(b * a.K + i) * a.Hq + h) * D * 2;
 #pragma unroll
-    for (int m = 0; m < MB; ++m)
+    for (int mm = 0; mm < MH; ++mm)
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
-        const int d0 = 32 * m + 8 * rg + 4 * hi;
+        const int d0 = 32 * (sub * MH + mm) + 8 * rg + 4 * hi;
         bf16x4 y;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = (bf16)(o[m][4 * rg + e] * inv);
+        for (int e = 0; e < 4; ++e) y[e] = (bf16)(oh[mm][4 * rg + e] * inv);
         *reinterpret_cast<bf16x4*>(orow + d0 * 2) = y;
       }
-  } else {
-    const size_t prow = ((size_t)(b * a.Hq + h) * a.s_max + s) * kRows + i;
-    float* po = a.ws_o + prow * D;
-#pragma unroll
-    for (int m = 0; m < MB; ++m)
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int d0 = 32 * m + 8 * rg + 4 * hi;
-        *reinterpret_cast<f32x4*>(po + d0) =
-            f32x4{o[m][4 * rg], o[m][4 * rg + 1], o[m][4 * rg + 2], o[m][4 * rg + 3]};
-      }
-    if (hi == 0) a.ws_ml[prow] = make_float2(m_c, l_row);
+    return;
   }
+
+  // ---- split context: the normalised partial (bf16, O / l) and the row
+  // statistics (max in log2 units, sum) go to slot s; attn_combine merges.
+  if (i >= a.K) return;
+  const size_t prow = ((size_t)(b * a.Hq + h) * a.s_max + s) * kRows + i;
+  char* pp = reinterpret_cast<char*>(a.ws_p) + prow * D * 2;
+#pragma unroll
+  for (int mm = 0; mm < MH; ++mm)
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      const int d0 = 32 * (sub * MH + mm) + 8 * rg + 4 * hi;
+      bf16x4 y;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) y[e] = (bf16)(oh[mm][4 * rg + e] * inv);
+      *reinterpret_cast<bf16x4*>(pp + d0 * 2) = y;
+    }
+  if (sub == 0 && hi == 0) a.ws_ml[prow] = make_float2(row_m, row_l);
 }
 
 // ---------------------------------------------------------------------------
@@ -990,13 +1038,32 @@ static int attn_s_max(const orthrus_attn_desc& d, int split) {
   return d.max_ctx_len > 0 ? ceil_div(d.max_ctx_len, split) : 1;
 }
 
-size_t attn_workspace_bytes(const orthrus_attn_desc& d) {
-  const int split = attn_split_tokens(d);
-  const int s_max = attn_s_max(d, split);
-  if (s_max <= 1) return 0;
-  const size_t rows = (size_t)d.batch * d.n_q_heads * s_max * kRows;
-  return rows * d.head_dim * sizeof(float) + rows * sizeof(float2);
+// bf16 with up to 4 query heads per KV head runs the LDS-DMA streaming
+// kernel (in-kernel split merge); everything else the register-staged kernel
+// plus attn_combine
+static bool attn_stream_path(const orthrus_attn_desc& d) {
+  return d.dtype == ORTHRUS_BF16 && d.n_q_heads / d.n_kv_heads <= 4;
 }
+
+struct WsLayout {
+  size_t bytes, off_ml;
+};
+
+static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// partial outputs (bf16 on the streaming path, fp32 otherwise), then the row
+// statistics
+static WsLayout attn_ws_layout(const orthrus_attn_desc& d) {
+  WsLayout w{0, 0};
+  const int s_max = attn_s_max(d, attn_split_tokens(d));
+  if (s_max <= 1) return w;
+  const size_t rows = (size_t)d.batch * d.n_q_heads * s_max * kRows;
+  w.off_ml = align256(rows * d.head_dim * (attn_stream_path(d) ? 2 : 4));
+  w.bytes = w.off_ml + rows * sizeof(float2);
+  return w;
+}
+
+size_t attn_workspace_bytes(const orthrus_attn_desc& d) { return attn_ws_layout(d).bytes; }
 
 template <typename T, int D, int G>
 static hipError_t launch_attn(const AttnArgs& a, int mode, hipStream_t stream) {
@@ -1017,7 +1084,7 @@ static hipError_t launch_attn(const AttnArgs& a, int mode, hipStream_t stream) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.s_max <= 1) return e;
-  return launch_combine<T, D>(a, stream);
+  return launch_combine<T, D, stream_path>(a, stream);
 }
 
 template <typename T, int D>
@@ -1077,9 +1144,15 @@ extern "C" orthrus_status orthrus_block_attn(const void* q, const void* k_cache,
   a.max_ctx = d.max_ctx_len;
   a.split = attn_split_tokens(d);
   a.s_max = attn_s_max(d, a.split);
-  const size_t rows = (size_t)d.batch * d.n_q_heads * a.s_max * kRows;
-  a.ws_o = need ? (float*)workspace : nullptr;
-  a.ws_ml = need ? (float2*)((char*)workspace + rows * d.head_dim * sizeof(float)) : nullptr;
+  a.ws_o = nullptr;
+  a.ws_p = nullptr;
+  a.ws_ml = nullptr;
+  if (need > 0) {
+    const WsLayout wl = attn_ws_layout(d);
+    if (attn_stream_path(d)) a.ws_p = (bf16*)workspace;
+    else a.ws_o = (float*)workspace;
+    a.ws_ml = (float2*)((char*)workspace + wl.off_ml);
+  }
   const float scale = d.softmax_scale > 0.f ? d.softmax_scale : 1.f / sqrtf((float)d.head_dim);
   a.c = scale * kLog2e;
   const int G = d.n_q_heads / d.n_kv_heads;

@@ -101,8 +101,9 @@ int32_t orthrus_abi_version(void);
 const char* orthrus_status_str(orthrus_status s);
 
 /* Bytes of caller-provided scratch orthrus_block_attn needs for `desc`
- * (split-context partial results).  0 for an invalid descriptor.  The
- * workspace needs no initialisation. */
+ * (split-context partial results: bf16 for bf16 storage with Hq/Hkv <= 4,
+ * fp32 otherwise, plus fp32 row statistics).  0 for an invalid descriptor or
+ * when no sequence can be split.  The workspace needs no initialisation. */
 size_t orthrus_block_attn_workspace_bytes(const orthrus_attn_desc* desc);
 
 /* Context positions per work-group that orthrus_block_attn will use for

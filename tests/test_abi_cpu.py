@@ -88,7 +88,15 @@ def test_split_and_workspace_arithmetic():
     assert split % 64 == 0 and 64 <= split <= 8192
     s_max = -(-8192 // split)           # splits partition the cached context
     rows = 1 * 32 * s_max * 32
-    assert lib.orthrus_block_attn_workspace_bytes(ctypes.byref(d)) == rows * 128 * 4 + rows * 8
+    up = lambda x: -(-x // 256) * 256
+    # bf16, 4 query heads per KV head: bf16 partials, then row stats
+    bf16_bytes = up(rows * 128 * 2) + rows * 8
+    assert lib.orthrus_block_attn_workspace_bytes(ctypes.byref(d)) == bf16_bytes
+    # fp32 storage: fp32 partials and row stats
+    d32 = good_desc(dtype=1)
+    split32 = lib.orthrus_block_attn_split_tokens(ctypes.byref(d32))
+    rows32 = 32 * -(-8192 // split32) * 32
+    assert lib.orthrus_block_attn_workspace_bytes(ctypes.byref(d32)) == rows32 * 128 * 4 + rows32 * 8
     d1 = good_desc(split_tokens=8192, max_ctx_len=100)      # one split: no workspace
     assert lib.orthrus_block_attn_workspace_bytes(ctypes.byref(d1)) == 0
 

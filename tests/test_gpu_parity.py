@@ -8,6 +8,7 @@ because that bound alone is loose at N(0,1) inputs, also <= 2e-2 * the largest
 block-dominant variants where a wrong key, page or mask gives an O(1) error.
 """
 
+import ctypes
 import math
 
 import numpy as np
@@ -196,6 +197,37 @@ def test_ragged_with_loose_max_ctx():
     say("loose max_ctx")
     inp = I.make_attn_inputs("qwen3_8b_8k", ctx_lens=[100], batch=1)
     check_attn(inp, AR, max_ctx=inp.page_table.shape[1] * 16 - 32)
+
+
+def test_attn_workspace_reused_across_shapes():
+    """One workspace serves calls with different batch sizes, context lengths
+    and split counts (no state survives a call); results meet the bar and the
+    first call repeated at the end gives identical bits."""
+    say("attention workspace reuse")
+    d = dev()
+    ob = K_()
+    cases = [(dict(ctx_lens=[8192]), 64), (dict(ctx_lens=[3001]), 256),
+             (dict(ctx_lens=[100, 5000, 64, 2000], batch=4), 128), (dict(ctx_lens=[700]), 0),
+             (dict(ctx_lens=[8192]), 64)]
+    inps = [I.make_attn_inputs("qwen3_8b_8k", **kw) for kw, _ in cases]
+    descs = [ob.make_desc(x.q, x.k_cache, x.page_table, x.max_ctx_len, None, sp) for x, (_, sp) in zip(inps, cases)]
+    need = [ob.block_attn_workspace_bytes(ds) for ds in descs]
+    ws = torch.full((max(need),), 0x7f, dtype=torch.uint8, device=d)   # any initial contents
+    first = None
+    for n, (x, (kw, sp)) in enumerate(zip(inps, cases)):
+        g = x.to(d)
+        out = ob.block_attn(g.q, g.k_cache, g.v_cache, g.k_blk, g.v_blk, g.page_table, g.ctx_lens, AR,
+                            max_ctx_len=x.max_ctx_len, split_tokens=sp, ws=ws)
+        torch.cuda.synchronize()
+        heads = [0, 13, 31]
+        ref = O.block_attn(x.q, x.k_cache, x.v_cache, x.k_blk, x.v_blk, x.page_table, x.ctx_lens, AR, heads=heads)
+        got = out.float().cpu().numpy().astype(np.float64)
+        err = np.abs(got - ref)[:, :, heads]
+        assert err.max() <= TOL * max_abs_v(x), (n, err.max())
+        if n == 0:
+            first = out.clone()
+        if n == len(cases) - 1:
+            assert torch.equal(out, first)
 
 
 # ---------------------------------------------------------------------------
