@@ -581,12 +581,12 @@ static hipError_t launch_combine(const AttnArgs& a, hipStream_t stream) {
 // attn_main, but the K/V stages go HBM -> LDS through the LDS-DMA path
 // (global_load_lds_dwordx4: no staging registers, no LDS store instructions)
 // and V stays token-major in LDS, read back transposed by ds_read_b64_tr_b16.
-// A ring of kRing 64-position stages (distinct LDS arrays, so the compiler's
-// wait tracking stays per buffer) keeps kRing - 1 stages of DMA in flight:
-// at stage t every wave waits for its own loads of stage t (vmcnt), one
-// barrier publishes the stage, then the DMA of stage t + kRing - 1 is issued
-// into the buffer stage t - 1 just released.  Work-group = 2G waves; wave w
-// serves query head g*G + w%G on the 32-position half w/G of each stage.
+// A ring of kRing 64-position stages (distinct LDS arrays) keeps kRing - 1
+// stages of DMA in flight: at stage t every wave waits for its own loads of
+// stage t + 1 (vmcnt), one barrier publishes it, then the DMA of stage
+// t + kRing - 1 is issued into the buffer stage t - 1 just released.
+// Work-group = 2G waves; wave w serves query head g*G + w%G on the
+// 32-position half w/G of each stage.
 constexpr int kRing = 4;
 
 template <int D>
@@ -599,7 +599,12 @@ struct StreamLayout {
   static constexpr int IPT = kTile / RPI;    // DMA instructions per tensor tile
   static constexpr int KSW = CPR - 1;        // K: chunk ^= row & KSW
   __device__ static int kswz(int row) { return row & KSW; }
-  __device__ static int vswz(int row) { return (row & 3) << 1; }  // V: chunk ^= 2 (row & 3)
+  // V: a 32-lane transposed read covers 4 consecutive rows x 64 bytes; the
+  // XOR puts those 4 x 4 chunks on 16 distinct chunk positions (all 64
+  // banks).  D = 128 rows are 256 B (every row starts at bank 0): chunk ^=
+  // 4 (row & 3).  D = 64 rows are 128 B (odd rows start at bank 32): chunk ^=
+  // 4 ((row >> 1) & 1).
+  __device__ static int vswz(int row) { return D == 128 ? (row & 3) << 2 : ((row >> 1) & 1) << 2; }
 };
 
 #define ORTHRUS_LDS __attribute__((address_space(3)))
@@ -829,8 +834,9 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_stream(AttnArgs a) {
       sc = mfma_step(av, qf[ks], sc);
     }
   };
-  // scores -> probabilities (as the two 16-position B operands of PV)
-  auto softmax = [&](f32x16& sc, int pbase, V8& p0, V8& p1) {
+  // softmax, first half: mask the tail, row max, lazy rescale of the
+  // running state; returns the reference max for the exponentials
+  auto sm_max = [&](f32x16& sc, int pbase) {
     // sc[r]: score of position pbase + 16(r/8) + 8hi + r%8 for row i
     if (pbase + 32 > L) {
 #pragma unroll
@@ -857,7 +863,11 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_stream(AttnArgs a) {
       l *= f;
       m_c = new_mc;
     }
-    const float mref = (m_c == -INFINITY) ? 0.f : m_c;
+    return (m_c == -INFINITY) ? 0.f : m_c;
+  };
+  // softmax, second half: probabilities (the two 16-position B operands of
+  // PV) and the row sum
+  auto sm_exp = [&](f32x16& sc, float mref, V8& p0, V8& p1) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       sc[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -mref));
@@ -888,7 +898,8 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_stream(AttnArgs a) {
   };
 
   char* const ring[kRing] = {st0, st1, st2, st3};
-  // prologue: stages 0 .. kRing-2 in flight; scores of stage 0
+  // prologue: stages 0 .. kRing-2 in flight; wait for stage 0, then the
+  // scores of stage 0
 #pragma unroll
   for (int u = 0; u < kRing - 1; ++u)
     Plan::issue(ring[u], a, pages, page_base, b, g, L, p_end, p_begin + u * kTile, wave, lane);
@@ -917,13 +928,16 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_stream(AttnArgs a) {
       const char* cur = ring[u];
       const char* nxt = ring[(u + 1) % kRing];
       const int pbase = my_lo + t * kTile;
-      const bool mine = pbase < p_end;  // this wave's half of stage t holds positions
+      // One basic block for the scheduler: the next stage's QK MFMAs are
+      // independent of this stage's exponentials and can issue beside them.
+      // Both run unconditionally: past the last stage the QK reads a stale
+      // buffer whose scores are never used, and a wave half wholly past the
+      // end of the last split has every position masked (zero weight).
       V8 p0, p1;
-      if (t + 1 < ntiles) qk(nxt, scores[(u + 1) & 1]);
-      if (mine) {
-        softmax(scores[u & 1], pbase, p0, p1);
-        pv(cur, p0, p1);
-      }
+      const float mref = sm_max(scores[u & 1], pbase);
+      qk(nxt, scores[(u + 1) & 1]);
+      sm_exp(scores[u & 1], mref, p0, p1);
+      pv(cur, p0, p1);
     }
   }
 

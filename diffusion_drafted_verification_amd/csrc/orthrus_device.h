@@ -42,8 +42,11 @@ __device__ __forceinline__ f32x16 mfma_step(f32x8 a, f32x8 b, f32x16 c) {
   return c;
 }
 
+// max of x over lanes l and l ^ 32: v_permlane32_swap exchanges the two
+// 32-lane halves between two registers (no LDS round trip)
 __device__ __forceinline__ float wave_max_xor32(float x) {
-  return fmaxf(x, __shfl_xor(x, 32, kWave));
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 }  // namespace orthrus
