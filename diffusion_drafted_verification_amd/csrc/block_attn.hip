@@ -621,6 +621,19 @@ __device__ __forceinline__ void dma16(const void* src, char* dst) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
 }
 
+// The same with 4 bytes per lane (lane l writes dst + 4 l).
+__device__ __forceinline__ void dma4(const void* src, char* dst) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)reinterpret_cast<uintptr_t>((ORTHRUS_LDS char*)dst));
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds) : "memory");
+}
+
+// a page id as used: ids outside [0, num_pages) read page 0 instead (results
+// for such positions are unspecified, but every access stays in bounds)
+__device__ __forceinline__ int valid_page(int p, int num_pages) {
+  return (unsigned)p < (unsigned)num_pages ? p : 0;
+}
+
 // DMA of one stage (positions p0 .. p0 + 63).  Lane l of a wave instruction
 // writes 16 bytes at the instruction's LDS base + 16 l, i.e. row (base row +
 // l / CPR), chunk slot l % CPR, and therefore loads the chunk the slot's
@@ -642,14 +655,9 @@ struct DmaPlan {
     return (tok & 15) * Lay::ROWB + chunk * 16;
   }
 
-  // the whole stage lies in the cached context (invalid page ids were
-  // replaced by page 0).  The stage is page aligned, so its four page ids are
-  // one 16-byte LDS read, done before the first DMA of the stage.
-  __device__ static void issue_cached(char* st, const AttnArgs& a, const int* pages, int page_base, int g, int p0,
-                                      int wave, int lane) {
-    const int4 pq = *reinterpret_cast<const int4*>(pages + ((p0 >> 4) - page_base));
-    const int pid0 = __builtin_amdgcn_readfirstlane(pq.x), pid1 = __builtin_amdgcn_readfirstlane(pq.y);
-    const int pid2 = __builtin_amdgcn_readfirstlane(pq.z), pid3 = __builtin_amdgcn_readfirstlane(pq.w);
+  // the whole stage lies in the cached context, in the (valid) pages pid0..3
+  __device__ static void issue_ids(char* st, const AttnArgs& a, int g, int pid0, int pid1, int pid2, int pid3,
+                                   int wave, int lane) {
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
       const int q = wave + NW * k;
@@ -661,6 +669,17 @@ struct DmaPlan {
       char* dst = st + ten * Lay::TILEB + ii * 1024;
       dma16(base + voff(wave, lane, k), dst);
     }
+  }
+
+  // the whole stage lies in the cached context; the stage is page aligned,
+  // so its four page ids are one 16-byte LDS read
+  __device__ static void issue_cached(char* st, const AttnArgs& a, const int* pages, int page_base, int g, int p0,
+                                      int wave, int lane) {
+    const int4 pq = *reinterpret_cast<const int4*>(pages + ((p0 >> 4) - page_base));
+    const int n = a.num_pages;
+    issue_ids(st, a, g, valid_page(__builtin_amdgcn_readfirstlane(pq.x), n),
+              valid_page(__builtin_amdgcn_readfirstlane(pq.y), n), valid_page(__builtin_amdgcn_readfirstlane(pq.z), n),
+              valid_page(__builtin_amdgcn_readfirstlane(pq.w), n), wave, lane);
   }
 
   // the stage reaches the context tail, the block rows or the split end:
@@ -682,8 +701,8 @@ struct DmaPlan {
       const int pos = p0 + tok;
       const char* src = blk + chunk * 16;
       if (pos < L && pos < p_end)
-        src = cache + ((size_t)(pages[(pos >> 4) - page_base] * a.Hkv + g) * kPage + (pos & 15)) * Lay::ROWB +
-              chunk * 16;
+        src = cache + ((size_t)(valid_page(pages[(pos >> 4) - page_base], a.num_pages) * a.Hkv + g) * kPage +
+                       (pos & 15)) * Lay::ROWB + chunk * 16;
       else if (pos >= L && pos < p_end)
         src = blk + ((size_t)(b * a.K + (pos - L)) * a.Hkv + g) * Lay::ROWB + chunk * 16;
       char* dst = st + ten * Lay::TILEB + ii * 1024;
@@ -756,24 +775,24 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_stream(AttnArgs a) {
   const int hw = wave % G, sub = wave / G;
   const int h = g * G + hw;
 
-  // Page ids, context length and this wave's query rows are loaded together
-  // and consumed (zeroing, LDS store) before the first K/V DMA is issued, so
-  // the prologue costs one global-memory latency and no compiler-placed wait
-  // on these loads can later stall behind the DMA (the compiler does not
-  // count the DMA loads).
-  int pg[(kMaxSplit / kPage + NT - 1) / NT];
+  // ---- prologue.  The context length and the page ids of the first three
+  // stages are scalar loads (constant address space: counted by lgkmcnt, not
+  // by vmcnt), so the K/V DMA of those stages starts after one load latency.
+  // The split's page table and the query rows reach LDS by DMA as well: no
+  // load the compiler tracks with vmcnt is in flight behind the K/V stream,
+  // so the hand-placed vmcnt waits below stay exact.
+  typedef const __attribute__((address_space(4))) int cint;
+  constexpr int NPRO = (kRing - 1) * kTile / kPage;  // page ids of the prologue stages
+  int L = ((cint*)a.ctx_lens)[b];
+  const bool ids_ok = page_base + NPRO <= a.max_pages;
+  int pid[NPRO];  // raw; checked where used
+  if (ids_ok) {
+    cint* row = (cint*)(a.page_table + (size_t)b * a.max_pages + page_base);
 #pragma unroll
-  for (int k = 0; k < (kMaxSplit / kPage + NT - 1) / NT; ++k) {
-    const int x = tid + k * NT, lp = page_base + x;
-    pg[k] = (x < a.split / kPage && lp < a.max_pages) ? a.page_table[(size_t)b * a.max_pages + lp] : -1;
-  }
-  int L = __builtin_amdgcn_readfirstlane(a.ctx_lens[b]);
-  typedef bf16x8 V8;
-  V8 qf[KS];
-  {
-    const char* qrow = a.q + ((size_t)(b * a.K + (i < a.K ? i : 0)) * a.Hq + h) * D * 2;
+    for (int j = 0; j < NPRO; ++j) pid[j] = row[j];
+  } else {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = __builtin_bit_cast(V8, ld16(qrow + (16 * ks + 8 * hi) * 2));
+    for (int j = 0; j < NPRO; ++j) pid[j] = 0;
   }
   L = L < 0 ? 0 : (L > a.max_ctx ? a.max_ctx : L);
   const int N = L + a.K;
@@ -782,23 +801,33 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_stream(AttnArgs a) {
   const int p_end = s == S_b - 1 ? N : p_begin + a.split;
   const int ntiles = (p_end - p_begin + kTile - 1) / kTile;
 
-  // ids outside [0, num_pages) read page 0 instead (results for such
-  // positions are unspecified, but every access stays in bounds)
-#pragma unroll
-  for (int k = 0; k < (kMaxSplit / kPage + NT - 1) / NT; ++k) {
-    const int x = tid + k * NT;
-    if (x < kMaxSplit / kPage) pages[x] = (pg[k] >= 0 && pg[k] < a.num_pages) ? pg[k] : 0;
+  // the split's page ids -> LDS (raw; checked where they are used); ids past
+  // the table row are never used
+  {
+    const int npt = min(a.split / kPage, a.max_pages - page_base);
+    const int* prow = a.page_table + (size_t)b * a.max_pages + page_base;
+    for (int k = wave; k * kWave < npt; k += NW) {
+      const int x = k * kWave + lane;
+      dma4(prow + (x < npt ? x : 0), reinterpret_cast<char*>(pages) + k * kWave * 4);
+    }
   }
-  // all of the above loads complete here, before any DMA is in flight; the
-  // builtin (not inline assembly) so that the compiler's own wait tracking
-  // knows the query registers are ready (gfx9 encoding: vmcnt(0), expcnt and
-  // lgkmcnt at their maxima)
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-#pragma unroll
-  for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qf[ks][e] = i < a.K ? qf[ks][e] : (bf16)0.f;
-  __syncthreads();  // page ids visible
+  // the G query heads of every block row -> st3 (free until stage 3 is
+  // issued): row i holds QR bytes, its 16-byte chunks XOR-swizzled by the row
+  // (i & QSW) so the per-lane reads below hit distinct banks; rows >= K read
+  // row 0 and are zeroed after the read
+  constexpr int QR = G * D * 2;
+  constexpr int QCH = QR / 16;
+  constexpr int QSW = (QCH < 16 ? QCH : 16) - 1;
+  constexpr int RQ = 1024 / QR;  // rows per DMA instruction
+  static_assert(kRows * QR <= Lay::STAGE, "query rows fit one stage buffer");
+  for (int k = wave; k < kRows / RQ; k += NW) {
+    const int row = k * RQ + lane / QCH, slot = lane % QCH;
+    const char* src = a.q + ((size_t)(b * a.K + (row < a.K ? row : 0)) * a.Hq + g * G) * D * 2 +
+                      ((slot ^ (row & QSW)) << 4);
+    dma16(src, st3 + k * 1024);
+  }
+  typedef bf16x8 V8;
+  V8 qf[KS];  // this wave's query rows (B operand of QK), read from st3 below
 
   f32x16 o[MB];
 #pragma unroll
@@ -898,14 +927,31 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_stream(AttnArgs a) {
   };
 
   char* const ring[kRing] = {st0, st1, st2, st3};
-  // prologue: stages 0 .. kRing-2 in flight; wait for stage 0, then the
-  // scores of stage 0
+  // stages 0 .. kRing-2 in flight: straight from the scalar page ids when all
+  // of them are whole cached stages, else through the LDS page table
+  if (ids_ok && p_begin + (kRing - 1) * kTile <= L && p_begin + (kRing - 1) * kTile <= p_end) {
 #pragma unroll
-  for (int u = 0; u < kRing - 1; ++u)
-    Plan::issue(ring[u], a, pages, page_base, b, g, L, p_end, p_begin + u * kTile, wave, lane);
+    for (int u = 0; u < kRing - 1; ++u)
+      Plan::issue_ids(ring[u], a, g, valid_page(pid[4 * u], a.num_pages), valid_page(pid[4 * u + 1], a.num_pages),
+                      valid_page(pid[4 * u + 2], a.num_pages), valid_page(pid[4 * u + 3], a.num_pages), wave, lane);
+  } else {
+    wait_vmcnt<0>();  // this wave's page-table (and query) DMA
+    __syncthreads();  // the split's page ids are in LDS
+#pragma unroll
+    for (int u = 0; u < kRing - 1; ++u)
+      Plan::issue(ring[u], a, pages, page_base, b, g, L, p_end, p_begin + u * kTile, wave, lane);
+  }
+  // stage 0 (and, issued before it, the page table and query rows) landed
   if (ntiles > 2) wait_vmcnt<2 * Plan::NS>();
   else wait_vmcnt<0>();
   barrier_no_fence();
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int chunk = (hw * (D * 2 / 16) + 2 * ks + hi) ^ (i & QSW);
+    qf[ks] = __builtin_bit_cast(V8, *reinterpret_cast<const u32x4*>(st3 + i * QR + chunk * 16));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) qf[ks][e] = i < a.K ? qf[ks][e] : (bf16)0.f;
+  }
   // scores of stage t live in scores[t & 1] (kRing is even, so the parity is
   // a compile-time constant in the unrolled body)
   static_assert(kRing % 2 == 0, "score double buffer alternates with the ring");
