@@ -3,20 +3,16 @@
 // AR head's greedy token (argmax over the vocabulary, lowest index on ties),
 // then the longest prefix of drafts that equals those tokens.
 //
-// One launch, three levels.  Each work-group scans one contiguous chunk of
-// one logits row with 16-byte loads (the scan is HBM-bound: 4 bytes per
-// logit) and reduces (value, index) pairs across the wave with xor shuffles
-// and across waves in LDS into one 64-bit key (order-preserving value bits
-// << 32 | ~index: the larger key is the larger value, then the lower index).
-// It stores the key and takes a ticket on its row; the last chunk of a row
-// reduces the row's keys to the greedy token and takes a ticket on its
-// sequence; the last row of a sequence compares the K tokens with the drafts
-// (wave ballot: first mismatch) and writes accept_len / next_token /
-// ar_tokens.  Every workspace word is cleared by the work-group that consumes
-// it (keys by the row's last chunk, tokens and tickets by their last reader),
-// so the whole workspace is zero again after every call, whatever shape the
-// next call has.  No address is hit by more than max(chunks, K)
-// atomics.
+// Two launches.  argmax_chunks: each work-group scans one contiguous chunk
+// of one logits row with 16-byte nontemporal loads (the scan is HBM-bound: 4
+// bytes per logit) and reduces (value, index) pairs across the wave with xor
+// shuffles and across waves in LDS into one 64-bit key (order-preserving
+// value bits << 32 | ~index: the larger key is the larger value, then the
+// lower index), stored to the workspace.  accept_rows: one work-group per
+// sequence reduces each row's chunk keys to the greedy token, then compares
+// the K tokens with the drafts (wave ballot: first mismatch) and writes
+// accept_len / next_token / ar_tokens.  The kernel boundary orders the two
+// passes: no atomics, no fences, and the workspace needs no initialisation.
 #include "orthrus_device.h"
 #include "orthrus_host.h"
 
@@ -31,9 +27,6 @@ struct AcceptArgs {
   int32_t* next_token;
   int32_t* ar_tokens;
   unsigned long long* part;   // [B*K, nchunks] chunk keys
-  int32_t* gtok;              // [B*K] greedy tokens
-  unsigned int* row_cnt;      // [B*K] tickets
-  unsigned int* seq_cnt;      // [B] tickets
   int B, K, V, chunk, nchunks;
 };
 
@@ -61,14 +54,12 @@ __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long k)
   return k;
 }
 
-__global__ void __launch_bounds__(kArgmaxThreads) argmax_accept(AcceptArgs a) {
+__global__ void __launch_bounds__(kArgmaxThreads) argmax_chunks(AcceptArgs a) {
   __shared__ float wv[kArgmaxThreads / kWave];
   __shared__ int wi[kArgmaxThreads / kWave];
-  __shared__ int row_last;
 
   const int row = blockIdx.x / a.nchunks;  // b * K + i
   const int ck = blockIdx.x % a.nchunks;
-  const int b = row / a.K;
   const int tid = threadIdx.x;
   const int begin = ck * a.chunk;
   const int end = min(begin + a.chunk, a.V);
@@ -109,43 +100,32 @@ __global__ void __launch_bounds__(kArgmaxThreads) argmax_accept(AcceptArgs a) {
   if (tid == 0) {
 #pragma unroll
     for (int w = 1; w < kArgmaxThreads / kWave; ++w) keep_better(bv, bi, wv[w], wi[w]);
-    const unsigned long long key =
+    a.part[(size_t)row * a.nchunks + ck] =
         ((unsigned long long)order_bits(bv) << 32) | (unsigned long long)(0xffffffffu - (uint32_t)bi);
-    __hip_atomic_store(&a.part[(size_t)row * a.nchunks + ck], key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __threadfence();
-    row_last = atomicAdd(&a.row_cnt[row], 1u) == (unsigned int)(a.nchunks - 1);
+  }
+}
+
+// One work-group per sequence: wave w reduces rows w, w + 4, ... (each row's
+// chunk keys, one per lane), then wave 0 scans the K greedy tokens.
+constexpr int kAcceptThreads = 256;
+
+__global__ void __launch_bounds__(kAcceptThreads) accept_rows(AcceptArgs a) {
+  __shared__ int32_t gtok[32];
+  const int b = blockIdx.x;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  for (int i = wave; i < a.K; i += kAcceptThreads / kWave) {
+    const unsigned long long* keys = a.part + (size_t)(b * a.K + i) * a.nchunks;
+    unsigned long long best = 0;
+    for (int q = lane; q < a.nchunks; q += kWave) best = keys[q] > best ? keys[q] : best;
+    best = wave_max_u64(best);
+    if (lane == 0) gtok[i] = (int32_t)(0xffffffffu - (uint32_t)(best & 0xffffffffu));
   }
   __syncthreads();
-  if (!row_last || wave != 0) return;
-
-  // last chunk of this row: the row's greedy token
-  __threadfence();
-  unsigned long long best = 0;
-  for (int q = lane; q < a.nchunks; q += kWave) {
-    unsigned long long* slot = &a.part[(size_t)row * a.nchunks + q];
-    const unsigned long long k = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(slot, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // leave the workspace zeroed
-    best = k > best ? k : best;
-  }
-  best = wave_max_u64(best);
-  int seq_last = 0;
-  if (lane == 0) {
-    const int32_t tok = (int32_t)(0xffffffffu - (uint32_t)(best & 0xffffffffu));
-    __hip_atomic_store(&a.gtok[row], tok, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&a.row_cnt[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __threadfence();
-    seq_last = atomicAdd(&a.seq_cnt[b], 1u) == (unsigned int)(a.K - 1);
-  }
-  seq_last = __shfl(seq_last, 0, kWave);
-  if (!seq_last) return;
-
-  // last row of sequence b: consensus over its K rows
-  __threadfence();
+  if (wave != 0) return;
   int32_t gt = 0;
   bool miss = false;
   if (lane < a.K) {
-    gt = __hip_atomic_load(&a.gtok[b * a.K + lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&a.gtok[b * a.K + lane], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    gt = gtok[lane];
     miss = a.drafts[b * a.K + lane] != gt;
     if (a.ar_tokens) a.ar_tokens[b * a.K + lane] = gt;
   }
@@ -156,7 +136,6 @@ __global__ void __launch_bounds__(kArgmaxThreads) argmax_accept(AcceptArgs a) {
   if (lane == 0) {
     a.accept_len[b] = acc;
     a.next_token[b] = nxt;
-    __hip_atomic_store(&a.seq_cnt[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -165,23 +144,10 @@ static int accept_chunk(int vocab) {
   return vocab < 8192 ? vocab : 8192;
 }
 
-struct AcceptLayout {
-  size_t part, gtok, row_cnt, seq_cnt, total;
-  int chunk, nchunks;
-};
-
-static AcceptLayout accept_layout(int batch, int block_k, int vocab) {
-  AcceptLayout L;
-  const size_t rows = (size_t)batch * block_k;
-  L.chunk = accept_chunk(vocab);
-  L.nchunks = (vocab + L.chunk - 1) / L.chunk;
-  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  L.part = 0;
-  L.gtok = up(rows * L.nchunks * 8);
-  L.row_cnt = L.gtok + up(rows * 4);
-  L.seq_cnt = L.row_cnt + up(rows * 4);
-  L.total = L.seq_cnt + up((size_t)batch * 4);
-  return L;
+static size_t accept_workspace(int batch, int block_k, int vocab, int* chunk, int* nchunks) {
+  *chunk = accept_chunk(vocab);
+  *nchunks = (vocab + *chunk - 1) / *chunk;
+  return (size_t)batch * block_k * *nchunks * sizeof(unsigned long long);
 }
 
 }  // namespace orthrus
@@ -190,7 +156,8 @@ using namespace orthrus;
 
 extern "C" size_t orthrus_greedy_accept_workspace_bytes(int32_t batch, int32_t block_k, int32_t vocab) {
   if (batch < 1 || block_k < 1 || block_k > 32 || vocab < 1) return 0;
-  return accept_layout(batch, block_k, vocab).total;
+  int chunk, nchunks;
+  return accept_workspace(batch, block_k, vocab, &chunk, &nchunks);
 }
 
 extern "C" orthrus_status orthrus_greedy_accept(const float* ar_logits, const int32_t* draft_tokens,
@@ -200,27 +167,27 @@ extern "C" orthrus_status orthrus_greedy_accept(const float* ar_logits, const in
   if (!ar_logits || !draft_tokens || !accept_len || !next_token) return ORTHRUS_ERR_NULL;
   if (batch < 1 || block_k < 1 || block_k > 32 || vocab < 1) return ORTHRUS_ERR_SHAPE;
   if (reinterpret_cast<uintptr_t>(ar_logits) & 3) return ORTHRUS_ERR_SHAPE;
-  const AcceptLayout lay = accept_layout(batch, block_k, vocab);
-  if (!workspace || workspace_bytes < lay.total || (reinterpret_cast<uintptr_t>(workspace) & 7))
+  int chunk, nchunks;
+  const size_t need = accept_workspace(batch, block_k, vocab, &chunk, &nchunks);
+  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 7))
     return ORTHRUS_ERR_WORKSPACE;
-  const long grid = (long)batch * block_k * lay.nchunks;
+  const long grid = (long)batch * block_k * nchunks;
   if (grid > 0x7fffffffL) return ORTHRUS_ERR_SHAPE;
-  char* ws = (char*)workspace;
   AcceptArgs a;
   a.logits = ar_logits;
   a.drafts = draft_tokens;
   a.accept_len = accept_len;
   a.next_token = next_token;
   a.ar_tokens = ar_tokens;
-  a.part = (unsigned long long*)(ws + lay.part);
-  a.gtok = (int32_t*)(ws + lay.gtok);
-  a.row_cnt = (unsigned int*)(ws + lay.row_cnt);
-  a.seq_cnt = (unsigned int*)(ws + lay.seq_cnt);
+  a.part = (unsigned long long*)workspace;
   a.B = batch;
   a.K = block_k;
   a.V = vocab;
-  a.chunk = lay.chunk;
-  a.nchunks = lay.nchunks;
-  hipLaunchKernelGGL(argmax_accept, dim3((unsigned)grid), dim3(kArgmaxThreads), 0, (hipStream_t)stream, a);
+  a.chunk = chunk;
+  a.nchunks = nchunks;
+  hipStream_t s = (hipStream_t)stream;
+  hipLaunchKernelGGL(argmax_chunks, dim3((unsigned)grid), dim3(kArgmaxThreads), 0, s, a);
+  if (hipGetLastError() != hipSuccess) return ORTHRUS_ERR_LAUNCH;
+  hipLaunchKernelGGL(accept_rows, dim3((unsigned)batch), dim3(kAcceptThreads), 0, s, a);
   return hipGetLastError() == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_LAUNCH;
 }

@@ -132,12 +132,12 @@ _workspaces = {}
 
 
 def workspace(device, nbytes, kind):
-    """A cached per-(device, kind) workspace of at least nbytes, zero-filled
-    when first allocated (the accept kernel leaves its workspace zeroed)."""
+    """A cached per-(device, kind) workspace of at least nbytes (the kernels
+    need no particular initial contents)."""
     key = (str(device), kind)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
 

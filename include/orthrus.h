@@ -127,8 +127,8 @@ orthrus_status orthrus_block_attn(const void* q, const void* k_cache, const void
                                   const orthrus_attn_desc* desc, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
-/* Bytes of the workspace orthrus_greedy_accept needs.  The workspace must be
- * zero-filled before its first use; every call leaves it zero-filled again. */
+/* Bytes of the workspace orthrus_greedy_accept needs (one 8-byte key per
+ * (row, 8192-logit chunk)).  The workspace needs no initialisation. */
 size_t orthrus_greedy_accept_workspace_bytes(int32_t batch, int32_t block_k, int32_t vocab);
 
 /* Greedy consensus of one step (explainer §2.3).

@@ -107,8 +107,8 @@ def test_accept_and_append_validation():
     assert lib.orthrus_greedy_accept(FAKE, FAKE, FAKE, FAKE, None, 1, 33, 100, FAKE, 1 << 20, None) == 2
     assert lib.orthrus_greedy_accept(FAKE, FAKE, FAKE, FAKE, None, 1, 32, 0, FAKE, 1 << 20, None) == 2
     need = lib.orthrus_greedy_accept_workspace_bytes(2, 32, 151936)
-    # chunk keys (64 rows x 19 chunks x 8 B), tokens, row and sequence tickets, 256-B aligned
-    assert need == 9728 + 256 + 256 + 256
+    # one 8-byte key per (row, 8192-logit chunk): 64 rows x 19 chunks
+    assert need == 64 * 19 * 8
     assert lib.orthrus_greedy_accept(FAKE, FAKE, FAKE, FAKE, None, 2, 32, 151936, FAKE, need - 1, None) == 4
     assert lib.orthrus_greedy_accept(FAKE, FAKE, FAKE, FAKE, None, 2, 32, 151936, None, need, None) == 4
     d = good_desc()

@@ -302,12 +302,13 @@ def test_accept_unaligned_vocab(V):
 
 
 def test_accept_workspace_reused_across_shapes():
-    """A workspace used by a large call serves a smaller call of another
-    shape (the kernel leaves every workspace word zero)."""
+    """A workspace used by a large call serves calls of other shapes, with
+    any initial contents (no state survives a call)."""
     say("accept shapes")
     from diffusion_drafted_verification_amd import orthrus as ob
     d = dev()
-    ws = torch.zeros(ob.lib().orthrus_greedy_accept_workspace_bytes(16, 32, 151936), dtype=torch.uint8, device=d)
+    ws = torch.full((ob.lib().orthrus_greedy_accept_workspace_bytes(16, 32, 151936),), 0xA5, dtype=torch.uint8,
+                    device=d)
     for (B, K, V) in [(16, 32, 151936), (4, 32, 151936), (1, 1, 64), (3, 7, 20000), (16, 32, 151936)]:
         x = torch.randn(B, K, V, generator=torch.Generator().manual_seed(B * K))
         g = torch.from_numpy(O.greedy_argmax(x.numpy())).int()
@@ -317,8 +318,6 @@ def test_accept_workspace_reused_across_shapes():
         ra, rn, rg = O.greedy_accept(x.numpy(), dr.numpy())
         assert np.array_equal(tok.cpu().numpy(), rg) and np.array_equal(acc.cpu().numpy(), ra)
         assert np.array_equal(nxt.cpu().numpy(), rn)
-        torch.cuda.synchronize()
-        assert int(ws.count_nonzero().item()) == 0
 
 
 def test_accept_workspace_is_reset_between_calls():
