@@ -253,7 +253,7 @@ def main():
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(ROOT, args.batch, args.ctx),
-            "kernel": "block_attn call (attn_main + attn_combine)", "us_per_call": round(ms_call * 1e3, 3),
+            "kernel": "block_attn call (attn_stream + attn_combine)", "us_per_call": round(ms_call * 1e3, 3),
             "us_diff": round(ms_diff * 1e3, 3), "us_ar": round(ms_ar * 1e3, 3),
             "bytes_per_call": step.kv_bytes_call, "split_tokens": split,
             "mfma_tflops": round(flops / (ms_call * 1e-3) / 1e12, 1)}
