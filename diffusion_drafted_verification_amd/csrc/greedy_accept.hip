@@ -106,19 +106,30 @@ __global__ void __launch_bounds__(kArgmaxThreads) argmax_chunks(AcceptArgs a) {
 }
 
 // One work-group per sequence: wave w reduces rows w, w + 4, ... (each row's
-// chunk keys, one per lane), then wave 0 scans the K greedy tokens.
+// chunk keys, one per lane; the first 64 keys of all its rows are loaded
+// before any is reduced), then wave 0 scans the K greedy tokens.
 constexpr int kAcceptThreads = 256;
+constexpr int kAcceptWaves = kAcceptThreads / kWave;
+constexpr int kRowsPerWave = (32 + kAcceptWaves - 1) / kAcceptWaves;
 
 __global__ void __launch_bounds__(kAcceptThreads) accept_rows(AcceptArgs a) {
   __shared__ int32_t gtok[32];
   const int b = blockIdx.x;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  for (int i = wave; i < a.K; i += kAcceptThreads / kWave) {
+  unsigned long long best[kRowsPerWave];
+#pragma unroll
+  for (int j = 0; j < kRowsPerWave; ++j) {
+    const int i = wave + kAcceptWaves * j;
+    best[j] = (i < a.K && lane < a.nchunks) ? a.part[(size_t)(b * a.K + i) * a.nchunks + lane] : 0ull;
+  }
+#pragma unroll
+  for (int j = 0; j < kRowsPerWave; ++j) {
+    const int i = wave + kAcceptWaves * j;
+    if (i >= a.K) break;
     const unsigned long long* keys = a.part + (size_t)(b * a.K + i) * a.nchunks;
-    unsigned long long best = 0;
-    for (int q = lane; q < a.nchunks; q += kWave) best = keys[q] > best ? keys[q] : best;
-    best = wave_max_u64(best);
-    if (lane == 0) gtok[i] = (int32_t)(0xffffffffu - (uint32_t)(best & 0xffffffffu));
+    for (int q = lane + kWave; q < a.nchunks; q += kWave) best[j] = keys[q] > best[j] ? keys[q] : best[j];
+    const unsigned long long m = wave_max_u64(best[j]);
+    if (lane == 0) gtok[i] = (int32_t)(0xffffffffu - (uint32_t)(m & 0xffffffffu));
   }
   __syncthreads();
   if (wave != 0) return;
