@@ -561,9 +561,111 @@ __global__ void __launch_bounds__(256) attn_combine(AttnArgs a) {
   }
 }
 
+// Merge of bf16 normalised partials (streaming path).  A row (b, i, h) is
+// served by SG lane groups of D/8 lanes; a lane owns 8 consecutive outputs
+// and the splits sg, sg + SG, ... (at most SPL of them: every load is issued
+// before any is used), and the SG groups of a row (adjacent within one wave)
+// merge with xor shuffles: no LDS, no barrier.  A work-group covers 4 waves x
+// 64 / (SG D/8) consecutive rows of one (b, g); block id = chunk * (B Hkv) +
+// b Hkv + g as for attn_combine.
+template <int D, int SG, int SPL>
+__global__ void __launch_bounds__(256) attn_combine_bf16(AttnArgs a) {
+  constexpr int C = D / 8;               // lanes per row and split group
+  constexpr int RPW = kWave / (C * SG);  // rows per wave
+  constexpr int RPB = 4 * RPW;           // rows per work-group
+  static_assert(RPW >= 1, "a row fits one wave");
+  const int BH = a.B * a.Hkv, G = a.Hq / a.Hkv;
+  const int bg = blockIdx.x % BH, chunk = blockIdx.x / BH;
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int rl = chunk * RPB + wave * RPW + lane / (C * SG);  // row within (b, g): w * K + i
+  const int sg = (lane / C) % SG, c = lane % C;
+  const bool live = rl < G * a.K;
+  const int w = live ? rl / a.K : 0, i = live ? rl % a.K : 0;
+  const int h = g * G + w;
+  int L = a.ctx_lens[b];
+  L = L < 0 ? 0 : (L > a.max_ctx ? a.max_ctx : L);
+  const int S_b = L > 0 ? (L + a.split - 1) / a.split : 1;
+  if (S_b <= 1) return;  // uniform over the work-group
+  const size_t base = (size_t)(b * a.Hq + h) * a.s_max * kRows + i;
+
+  float M = -INFINITY, den = 0.f;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int s0 = sg; s0 < S_b; s0 += SG * SPL) {
+    float2 ml[SPL];
+    u32x4 x[SPL];
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) {
+      const int sp = s0 + SG * j;
+      const size_t r = base + (size_t)(sp < S_b ? sp : 0) * kRows;
+      ml[j] = a.ws_ml[r];
+      x[j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(a.ws_p) + r * D * 2 + c * 16);
+      if (sp >= S_b) ml[j].x = -INFINITY;
+    }
+    float mnew = M;
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) mnew = fmaxf(mnew, ml[j].x);
+    if (mnew != -INFINITY) {
+      const float sc = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - mnew);
+      den *= sc;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] *= sc;
+#pragma unroll
+      for (int j = 0; j < SPL; ++j) {
+        const float wj = (ml[j].x == -INFINITY) ? 0.f : ml[j].y * __builtin_amdgcn_exp2f(ml[j].x - mnew);
+        den += wj;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          acc[2 * k] += wj * __uint_as_float(x[j][k] << 16);
+          acc[2 * k + 1] += wj * __uint_as_float(x[j][k] & 0xffff0000u);
+        }
+      }
+      M = mnew;
+    }
+  }
+  // merge the SG split groups of the row (lanes c + C q, q < SG)
+#pragma unroll
+  for (int off = C; off < C * SG; off <<= 1) {
+    const float Mo = __shfl_xor(M, off, kWave);
+    const float Mall = fmaxf(M, Mo);
+    const float sc = (M == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(M - Mall);
+    den *= sc;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= sc;
+    den += __shfl_xor(den, off, kWave);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], off, kWave);
+    M = Mall;
+  }
+  if (!live || sg != 0) return;
+  const float inv = 1.f / den;
+  u32x4 y;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const bf16 lo = (bf16)(acc[2 * k] * inv), hi2 = (bf16)(acc[2 * k + 1] * inv);
+    y[k] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi2) << 16);
+  }
+  *reinterpret_cast<u32x4*>(a.out + ((size_t)(b * a.K + i) * a.Hq + h) * D * 2 + c * 16) = y;
+}
+
 template <typename T, int D, bool NORM>
 static hipError_t launch_combine(const AttnArgs& a, hipStream_t stream) {
   const int rows = (a.Hq / a.Hkv) * a.K;  // per (b, g)
+  if constexpr (NORM) {
+    // split groups per row so that a lane holds at most 8 splits in flight
+    auto go2 = [&](auto sg_tag) {
+      constexpr int SG = decltype(sg_tag)::value;
+      constexpr int RPB = 4 * (kWave / ((D / 8) * SG));
+      const int chunks = (rows + RPB - 1) / RPB;
+      hipLaunchKernelGGL((attn_combine_bf16<D, SG, 8>), dim3(chunks * a.B * a.Hkv), dim3(256), 0, stream, a);
+    };
+    if (a.s_max > 16) go2(std::integral_constant<int, 4>());
+    else if (a.s_max > 8) go2(std::integral_constant<int, 2>());
+    else go2(std::integral_constant<int, 1>());
+    return hipGetLastError();
+  }
   auto go = [&](auto sg_tag) {
     constexpr int SG = decltype(sg_tag)::value;
     constexpr int RPB = 256 / ((D / 4) * SG);
