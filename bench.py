@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a graph")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--no-long-context", action="store_true",
+                   help="skip the 36-layer step at batch 4, 32768 cached tokens")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="run one plain device copy of this size first (calibrates HBM byte counters)")
     return p.parse_args()
@@ -59,10 +61,10 @@ def log(*a):
 class Step:
     """Buffers and calls of one decode step (all layers)."""
 
-    def __init__(self, ob, I, torch, batch, ctx, layers, split_tokens, seed=0):
+    def __init__(self, ob, I, torch, batch, ctx, layers, split_tokens, seed=0, workload="qwen3_8b_8k"):
         self.ob, self.torch = ob, torch
         d = torch.device("cuda:0")
-        w = I.WORKLOADS["qwen3_8b_8k"]
+        w = I.WORKLOADS[workload]
         self.B, self.K, self.Hq, self.Hkv, self.D = batch, w["block_k"], w["n_q_heads"], w["n_kv_heads"], w["head_dim"]
         self.layers, self.split = layers, split_tokens
         lens = [ctx] * batch
@@ -72,16 +74,16 @@ class Step:
         self.max_ctx = ctx
         self.L = []
         for l in range(layers):
-            a = I.make_attn_inputs("qwen3_8b_8k", seed=seed, layer=l, device=d, ctx_lens=lens, batch=batch)
-            q_ar = I._randn(a.q.shape, torch.bfloat16, d, I._seed(seed + 1, "qwen3_8b_8k", l, "q"))
-            kb_ar = I._randn(a.k_blk.shape, torch.bfloat16, d, I._seed(seed + 1, "qwen3_8b_8k", l, "k_blk"))
-            vb_ar = I._randn(a.v_blk.shape, torch.bfloat16, d, I._seed(seed + 1, "qwen3_8b_8k", l, "v_blk"))
+            a = I.make_attn_inputs(workload, seed=seed, layer=l, device=d, ctx_lens=lens, batch=batch)
+            q_ar = I._randn(a.q.shape, torch.bfloat16, d, I._seed(seed + 1, workload, l, "q"))
+            kb_ar = I._randn(a.k_blk.shape, torch.bfloat16, d, I._seed(seed + 1, workload, l, "k_blk"))
+            vb_ar = I._randn(a.v_blk.shape, torch.bfloat16, d, I._seed(seed + 1, workload, l, "v_blk"))
             self.L.append(dict(k_cache=a.k_cache, v_cache=a.v_cache, q_diff=a.q, kb_diff=a.k_blk, vb_diff=a.v_blk,
                                q_ar=q_ar, kb_ar=kb_ar, vb_ar=vb_ar, out_diff=torch.empty_like(a.q),
                                out_ar=torch.empty_like(a.q)))
-        self.logits, t = I.make_logits(batch, self.K, I.QWEN3_VOCAB, seed=seed, workload="qwen3_8b_8k", plant=True,
+        self.logits, t = I.make_logits(batch, self.K, I.QWEN3_VOCAB, seed=seed, workload=workload, plant=True,
                                        device=d)
-        self.prefix = I.geometric_prefix(batch, self.K, seed=seed, workload="qwen3_8b_8k")
+        self.prefix = I.geometric_prefix(batch, self.K, seed=seed, workload=workload)
         self.drafts = I.make_drafts(t.cpu(), self.prefix, I.QWEN3_VOCAB, seed=seed).to(d)
         self.new_ctx = torch.empty(batch, dtype=torch.int32, device=d)
         self.append_ptrs = ob.LayerPointers([x["k_cache"] for x in self.L], [x["v_cache"] for x in self.L],
@@ -275,6 +277,28 @@ def main():
             torch.cuda.empty_cache()
         step = None
 
+    longctx = None
+    if not args.no_long_context:
+        log("long-context step")
+        step = None
+        torch.cuda.empty_cache()
+        s5 = Step(ob, I, torch, 4, 32768, 36, 0, seed=0, workload="qwen3_8b_32k_b4")
+        s5.run()
+        torch.cuda.synchronize()
+        committed = int(torch.clamp(s5.acc + 1, max=s5.K).sum().item())
+        rep5 = capture(torch, s5.run) if use_graph else s5.run
+        ms5 = time_region(torch, rep5, 5, 2)
+        kv5 = 2 * 36 * s5.kv_bytes_call
+        longctx = {"workload": "qwen3_8b_32k_b4 step: B4 Hq32/Hkv8 D128 ctx32768 K32, 36 layers x (DIFF_BIDIR + "
+                               "AR_CAUSAL) + accept(V=151936) + kv_append into 36 layers",
+                   "us_per_step": round(ms5 * 1e3, 1), "kv_bytes_per_step": kv5,
+                   "kv_gbs": round(kv5 / (ms5 * 1e-3) / 1e9, 1),
+                   "frac_hbm": round(kv5 / (ms5 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                   "committed_tokens_per_step": committed,
+                   "committed_tokens_per_s": round(committed / (ms5 * 1e-3), 1)}
+        del s5, rep5
+        torch.cuda.empty_cache()
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline")
@@ -290,7 +314,7 @@ def main():
                        "batch": args.batch, "ctx": args.ctx, "block_k": 32, "layers": args.layers,
                        "graph": use_graph, "parallelism": "none (1 GPU)"},
             "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-            "roofline": roof, "cpu_baseline": cpu, "sweep": sweep or None}
+            "roofline": roof, "cpu_baseline": cpu, "sweep": sweep or None, "long_context_step": longctx}
     print(json.dumps(line), flush=True)
 
 
