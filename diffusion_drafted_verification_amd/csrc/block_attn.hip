@@ -1096,19 +1096,26 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_stream(AttnArgs a) {
   wait_vmcnt<0>();
   __syncthreads();  // the ring is free
   constexpr int MH = MB / 2;
-  // exchange areas: wave slot k = 2 hw + sub; slots 0-3 in st0, 4-7 in st1
-  auto xslot = [&](int k) {
-    return reinterpret_cast<float*>(k < 4 ? st0 : st1) + (k & 3) * (MH * 16) * kWave;
-  };
+  constexpr int NC = MH * 4;                 // 16-byte chunks a lane hands over
+  constexpr int XSH = NC == 8 ? 1 : 2;       // chunk swizzle: 16 lanes of a
+  // 16-byte access cover all 64 banks (lane stride 16 NC bytes)
+  // exchange areas: wave slot k = 2 hw + sub; slots 0-3 in st0, 4-7 in st1;
+  // lane l's chunk c at (c ^ ((l >> XSH) & (NC - 1)))
+  auto xslot = [&](int k) { return (k < 4 ? st0 : st1) + (k & 3) * (NC * 16) * kWave + lane * (NC * 16); };
+  const int xsw = (lane >> XSH) & (NC - 1);
   {
-    float* xo = xslot(hw * 2 + sub);
+    char* xo = xslot(hw * 2 + sub);
     float* xm = reinterpret_cast<float*>(st2) + (hw * 2 + sub) * 2 * kWave;
     // the half the partner keeps (selects, not a runtime index, keep o in
     // registers)
 #pragma unroll
-    for (int mm = 0; mm < MH; ++mm)
+    for (int c = 0; c < NC; ++c) {
+      const int mm = c / 4, r0 = 4 * (c % 4);
+      f32x4 v;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) xo[(mm * 16 + r) * kWave + lane] = sub == 0 ? o[MH + mm][r] : o[mm][r];
+      for (int e = 0; e < 4; ++e) v[e] = sub == 0 ? o[MH + mm][r0 + e] : o[mm][r0 + e];
+      *reinterpret_cast<f32x4*>(xo + ((c ^ xsw) << 4)) = v;
+    }
     xm[lane] = m_c;
     xm[kWave + lane] = l;
   }
@@ -1117,7 +1124,7 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_stream(AttnArgs a) {
   float row_m, row_l;
   {
     const int other = 1 - sub;
-    const float* yo = xslot(hw * 2 + other);
+    const char* yo = xslot(hw * 2 + other);
     const float* ym = reinterpret_cast<const float*>(st2) + (hw * 2 + other) * 2 * kWave;
     const float m1 = ym[lane], l1 = ym[kWave + lane];
     const float mA = sub == 0 ? m_c : m1, mB = sub == 0 ? m1 : m_c;
@@ -1126,51 +1133,53 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_stream(AttnArgs a) {
     const float wA = (mA == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mA - mm_);
     const float wB = (mB == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mB - mm_);
 #pragma unroll
-    for (int mm = 0; mm < MH; ++mm)
+    for (int c = 0; c < NC; ++c) {
+      const int mm = c / 4, r0 = 4 * (c % 4);
+      const f32x4 oth = *reinterpret_cast<const f32x4*>(yo + ((c ^ xsw) << 4));
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float own = sub == 0 ? o[mm][r] : o[MH + mm][r], oth = yo[(mm * 16 + r) * kWave + lane];
-        oh[mm][r] = sub == 0 ? wA * own + wB * oth : wA * oth + wB * own;
+      for (int e = 0; e < 4; ++e) {
+        const float own = sub == 0 ? o[mm][r0 + e] : o[MH + mm][r0 + e];
+        oh[mm][r0 + e] = sub == 0 ? wA * own + wB * oth[e] : wA * oth[e] + wB * own;
       }
+    }
     const float lh = wA * lA + wB * lB;  // this lane's half of the row sum
     row_l = lh + __shfl_xor(lh, 32, kWave);
     row_m = mm_;
   }
+  if (i >= a.K) return;  // both lanes of a swap pair share i
   const float inv = 1.f / row_l;
-  // lane (i, hi) holds, for d block m = sub * MH + mm, the elements
-  // d = 32 m + 8 rg + 4 hi + e at oh[mm][4 rg + e]
-  if (S_b == 1) {
-    if (i >= a.K) return;
-    char* orow = a.out + ((size_t)(b * a.K + i) * a.Hq + h) * D * 2;
+  // Lane (i, hi) holds, for d block m = sub MH + mm, the elements
+  // d = 32 m + 8 rg + 4 hi + e at oh[mm][4 rg + e].  One permlane32 swap per
+  // packed register pair hands rg = 2, 3 of lane (i, 0) to lane (i, 1) and
+  // rg = 0, 1 of lane (i, 1) to lane (i, 0): each lane then owns the 8
+  // consecutive elements d = 32 m + 16 hi + 8 j + (0..7), j = 0, 1, and
+  // writes them as one 16-byte store.
+  auto pack2 = [](float x, float y) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (bf16)x) | ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)y) << 16);
+  };
+  char* const row_out = S_b == 1 ? a.out + ((size_t)(b * a.K + i) * a.Hq + h) * D * 2
+                                 : reinterpret_cast<char*>(a.ws_p) +
+                                       (((size_t)(b * a.Hq + h) * a.s_max + s) * kRows + i) * D * 2;
 #pragma unroll
-    for (int mm = 0; mm < MH; ++mm)
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int d0 = 32 * (sub * MH + mm) + 8 * rg + 4 * hi;
-        bf16x4 y;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) y[e] = (bf16)(oh[mm][4 * rg + e] * inv);
-        *reinterpret_cast<bf16x4*>(orow + d0 * 2) = y;
-      }
-    return;
-  }
-
-  // ---- split context: the normalised partial (bf16, O / l) and the row
-  // statistics (max in log2 units, sum) go to slot s; attn_combine merges.
-  if (i >= a.K) return;
-  const size_t prow = ((size_t)(b * a.Hq + h) * a.s_max + s) * kRows + i;
-  char* pp = reinterpret_cast<char*>(a.ws_p) + prow * D * 2;
-#pragma unroll
-  for (int mm = 0; mm < MH; ++mm)
+  for (int mm = 0; mm < MH; ++mm) {
+    uint32_t pk[4][2];
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
-      const int d0 = 32 * (sub * MH + mm) + 8 * rg + 4 * hi;
-      bf16x4 y;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) y[e] = (bf16)(oh[mm][4 * rg + e] * inv);
-      *reinterpret_cast<bf16x4*>(pp + d0 * 2) = y;
+      pk[rg][0] = pack2(oh[mm][4 * rg] * inv, oh[mm][4 * rg + 1] * inv);
+      pk[rg][1] = pack2(oh[mm][4 * rg + 2] * inv, oh[mm][4 * rg + 3] * inv);
     }
-  if (sub == 0 && hi == 0) a.ws_ml[prow] = make_float2(row_m, row_l);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const auto s0 = __builtin_amdgcn_permlane32_swap(pk[j][0], pk[j + 2][0], false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(pk[j][1], pk[j + 2][1], false, false);
+      const int d0 = 32 * (sub * MH + mm) + 16 * hi + 8 * j;
+      *reinterpret_cast<u32x4*>(row_out + d0 * 2) = u32x4{s0[0], s1[0], s0[1], s1[1]};
+    }
+  }
+  // ---- split context: the row statistics (max in log2 units, sum) go with
+  // the normalised partial (bf16, O / l) to slot s; attn_combine merges.
+  if (S_b > 1 && sub == 0 && hi == 0)
+    a.ws_ml[((size_t)(b * a.Hq + h) * a.s_max + s) * kRows + i] = make_float2(row_m, row_l);
 }
 
 // ---------------------------------------------------------------------------
