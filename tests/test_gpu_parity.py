@@ -162,6 +162,43 @@ def test_group_sizes_and_head_dims(G, D, dtype):
         check_attn(inp, mode, scale=1.0)
 
 
+def random_attn_case(n):
+    """Seeded random shape n: group size, KV heads, head dim, dtype, batch,
+    ragged context lengths (with empties and page-boundary lengths), block
+    size, split length, page-table slack and a loose max_ctx bound."""
+    rng = np.random.default_rng([2024, n])
+    G = int(rng.choice([1, 2, 4, 8]))
+    Hkv = int(rng.choice([h for h in (1, 2, 4, 8) if G * h <= 32]))
+    D = int(rng.choice([64, 128]))
+    dtype = torch.float32 if rng.random() < 0.2 else torch.bfloat16
+    B = int(rng.integers(1, 5))
+    K = int(rng.choice([1, 2, 5, 16, 31, 32]))
+    L = [int(rng.choice([0, 1, 15, 16, 17, 63, 64, 65, rng.integers(0, 2600)])) for _ in range(B)]
+    split = int(rng.choice([0, 0, 64, 128, 192, 256, 512, 4096]))
+    extra = int(rng.integers(0, 40))
+    table, n_pages = I.make_page_table(L, K, 16, shuffle=True, seed=n, extra_pages=extra)
+    slack = int(rng.integers(0, 3))  # spare table columns: a looser max_ctx bound
+    if slack:
+        table = np.concatenate([table, np.full((B, slack), -1, dtype=np.int32)], axis=1)
+    max_ctx = table.shape[1] * 16 - K if slack else max(L)
+    g = torch.Generator().manual_seed(7000 + n)
+    r = lambda *shape: torch.randn(*shape, generator=g).to(dtype)
+    inp = I.AttnInputs(r(B, K, G * Hkv, D), r(n_pages, Hkv, 16, D), r(n_pages, Hkv, 16, D), r(B, K, Hkv, D),
+                       r(B, K, Hkv, D), torch.from_numpy(table), torch.tensor(L, dtype=torch.int32), max_ctx)
+    mode = DIFF if rng.random() < 0.5 else AR
+    return inp, mode, split, dict(G=G, Hkv=Hkv, D=D, dtype=str(dtype), B=B, K=K, L=L, split=split, mode=mode,
+                                  max_ctx=max_ctx)
+
+
+@pytest.mark.parametrize("n", range(24))
+def test_randomized_shapes(n):
+    """Seeded random shapes across every supported group size, head dim,
+    dtype, block size, split length and ragged batch (see random_attn_case)."""
+    inp, mode, split, desc = random_attn_case(n)
+    say("random", n, desc)
+    check_attn(inp, mode, split=split, max_ctx=inp.max_ctx_len)
+
+
 def test_gpu_invariants():
     """K = 1: both modes give identical bits; page relabelling gives identical
     bits; the last row agrees between modes; two runs give identical bits."""
