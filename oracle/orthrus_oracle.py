@@ -40,7 +40,12 @@ Readings of points the pages leave open (each one is listed in the design doc):
   accepted drafts), written at cache positions L .. L+n-1;
 * grouped-query attention maps query head h to KV head h * Hkv // Hq; the
   softmax scale defaults to 1/sqrt(D); no soft-cap, window or bias;
-* argmax ties go to the lowest index; -0.0 equals +0.0 (IEEE compare).
+* argmax ties go to the lowest index; -0.0 equals +0.0 (IEEE compare);
+* at temperature T > 0 a draft is accepted when u * q[x] < p[x] (p, q the
+  AR and diffusion softmaxes at T; u a given uniform), and the correction at
+  the first rejection is drawn from max(p - q, 0) by inverse CDF with a
+  second given uniform (the standard lossless rejection rule; the pages name
+  temperature settings without the rule).
 
 Pins: every function here is pinned in tests/test_oracle_pins.py against
 closed forms, invariants and brute force (see each docstring).
@@ -203,6 +208,55 @@ def greedy_accept(ar_logits, draft_tokens):
     acc = np.array([accept_prefix(drafts[b], g[b]) for b in range(B)], dtype=np.int64)
     nxt = np.array([g[b, min(acc[b], K - 1)] for b in range(B)], dtype=np.int64)
     return acc, nxt, g
+
+
+def softmax_t(logits, temperature):
+    """Row-wise softmax of logits / T in fp64 (the sampling distribution of
+    a head at temperature T > 0)."""
+    x = _f64(logits) / float(temperature)
+    m = np.max(x, axis=-1, keepdims=True)
+    e = np.exp(x - m)
+    return e / np.sum(e, axis=-1, keepdims=True)
+
+
+def sample_accept(ar_logits, draft_logits, draft_tokens, u_accept, u_resample, temperature):
+    """Lossless acceptance of sampled drafts at temperature T > 0 (the
+    stochastic form of the consensus step: the pages name temperature
+    settings; this is the standard rejection rule that keeps the AR head's
+    distribution exact).
+
+    For each sequence b, rows i = 0 .. K-1 in order, with p = softmax(ar/T),
+    q = softmax(draft/T) of row i and x = draft_tokens[b, i]:
+      accept x when u_accept[b, i] * q[x] < p[x] (probability min(1, p/q));
+      at the first rejection i: accept_len = i and next_token is drawn from
+      the residual r = max(p - q, 0) / sum(r) by inverse CDF,
+      next = min{v : cumsum(r)[v] > u_resample[b] * sum(r)}.
+    With no rejection: accept_len = K, next_token = x of row K - 1.
+    The step commits min(accept_len + 1, K) tokens, as in the greedy case.
+    Returns (accept_len [B], next_token [B]).
+    """
+    drafts = _i64(draft_tokens)
+    ua = _f64(u_accept)
+    ur = _f64(u_resample)
+    p_all = softmax_t(ar_logits, temperature)
+    q_all = softmax_t(draft_logits, temperature)
+    B, K = drafts.shape
+    acc = np.full(B, K, dtype=np.int64)
+    nxt = drafts[:, K - 1].copy()
+    for b in range(B):
+        for i in range(K):
+            p, q, x = p_all[b, i], q_all[b, i], drafts[b, i]
+            if ua[b, i] * q[x] < p[x]:
+                continue
+            r = np.maximum(p - q, 0.0)
+            total = r.sum()
+            if total <= 0.0:  # p == q: cannot reject; kept for completeness
+                r, total = p, 1.0
+            c = np.cumsum(r)
+            acc[b] = i
+            nxt[b] = int(np.flatnonzero(c > ur[b] * total)[0])
+            break
+    return acc, nxt
 
 
 def commit_count(accept_len, K):

@@ -512,3 +512,88 @@ def test_step_accounting_geometric_prefix():
     expect = 1 + 11.7 * (1 - (11.7 / 12.7) ** 31)
     assert abs(expect - 11.78) < 0.01
     assert abs(n.mean() - expect) < 4 * n.std() / math.sqrt(len(n))
+
+
+# ---------------------------------------------------------------------------
+# sampling accept (temperature > 0)
+# ---------------------------------------------------------------------------
+
+def test_sample_accept_is_lossless_by_quadrature():
+    """The first committed token of a step is distributed exactly as the AR
+    head's softmax p, whatever the draft distribution q (the lossless
+    property).  Drafts x ~ q; the acceptance probability of x and the
+    correction distribution are measured by midpoint quadrature over the two
+    uniforms, then combined: P(v) = q[v] P(acc | v) + sum_x q[x] (1 - P(acc | x)) P(corr = v)."""
+    rng = np.random.default_rng(11)
+    V, T, N = 6, 0.7, 2000
+    ar = rng.normal(0, 1.5, size=(1, 1, V))
+    dr = rng.normal(0, 1.5, size=(1, 1, V))
+    p = O.softmax_t(ar, T)[0, 0]
+    q = O.softmax_t(dr, T)[0, 0]
+    grid = (np.arange(N) + 0.5) / N
+    ar_b = np.repeat(ar, N, axis=0)
+    dr_b = np.repeat(dr, N, axis=0)
+    p_acc = np.zeros(V)
+    for x in range(V):
+        acc, _ = O.sample_accept(ar_b, dr_b, np.full((N, 1), x), grid[:, None], np.zeros(N), T)
+        p_acc[x] = np.mean(acc == 1)
+    # correction distribution: a draft that is rejected for u close to 1
+    xr = int(np.argmin(p / q))
+    assert p[xr] < q[xr]
+    acc, nxt = O.sample_accept(ar_b, dr_b, np.full((N, 1), xr), np.full((N, 1), 1 - 1e-12), grid, T)
+    assert (acc == 0).all()
+    p_corr = np.bincount(nxt, minlength=V) / N
+    P = q * p_acc + np.sum(q * (1 - p_acc)) * p_corr
+    assert np.abs(P - p).max() < 3.0 / N
+    # and the measured pieces are the closed forms
+    assert np.abs(p_acc - np.minimum(1, p / q)).max() <= 1.0 / N
+    r = np.maximum(p - q, 0)
+    assert np.abs(p_corr - r / r.sum()).max() <= 1.0 / N
+
+
+def test_sample_accept_equal_heads_accept_everything():
+    rng = np.random.default_rng(12)
+    lg = rng.normal(size=(3, 8, 50))
+    drafts = rng.integers(0, 50, size=(3, 8))
+    acc, nxt = O.sample_accept(lg, lg, drafts, rng.random((3, 8)) * 0.999, rng.random(3), 1.3)
+    assert (acc == 8).all() and np.array_equal(nxt, drafts[:, -1])
+
+
+def test_sample_accept_low_temperature_is_greedy():
+    """T -> 0 with drafts at the diffusion head's argmax reduces to the greedy
+    consensus (accepted prefix and AR correction token)."""
+    rng = np.random.default_rng(13)
+    B, K, V = 4, 10, 300
+    ar = rng.normal(size=(B, K, V))
+    dr = rng.normal(size=(B, K, V))
+    g = O.greedy_argmax(ar)
+    for b in range(B):  # a clear AR winner: p is one-hot at T -> 0
+        for i in range(K):
+            ar[b, i, g[b, i]] += 1.0
+    pre = [3, 0, 10, 7]
+    for b in range(B):
+        for i in range(K):
+            if i < pre[b]:  # the diffusion head agrees with the AR head here
+                dr[b, i, g[b, i]] = dr[b, i].max() + 1.0
+            else:           # and picks another token from here on
+                alt = (g[b, i] + 1 + i) % V
+                dr[b, i, alt] = dr[b, i].max() + 1.0
+    drafts = O.greedy_argmax(dr)
+    acc, nxt = O.sample_accept(ar, dr, drafts, rng.random((B, K)) * 0.98, rng.random(B), 1e-3)
+    ga, gn, _ = O.greedy_accept(ar, drafts)
+    assert np.array_equal(acc, ga) and np.array_equal(nxt, gn)
+    assert list(acc) == pre
+
+
+def test_sample_accept_impossible_draft_is_rejected():
+    """A draft the AR head gives zero probability is always rejected, at any
+    uniform, and the correction is never that token."""
+    rng = np.random.default_rng(14)
+    V = 40
+    ar = rng.normal(size=(1, 2, V))
+    dr = rng.normal(size=(1, 2, V))
+    ar[0, 1, 7] = -np.inf
+    drafts = np.array([[int(np.argmax(ar[0, 0])), 7]])
+    for u in (0.0, 0.3, 0.999):
+        acc, nxt = O.sample_accept(ar, dr, drafts, np.array([[0.0, u]]), np.array([u]), 0.9)
+        assert acc[0] == 1 and nxt[0] != 7
