@@ -231,7 +231,8 @@ def sample_accept(ar_logits, draft_logits, draft_tokens, u_accept, u_resample, t
       at the first rejection i: accept_len = i and next_token is drawn from
       the residual r = max(p - q, 0) / sum(r) by inverse CDF,
       next = min{v : cumsum(r)[v] > u_resample[b] * sum(r)}.
-    With no rejection: accept_len = K, next_token = x of row K - 1.
+    With no rejection: accept_len = K, next_token = x of row K - 1.  A draft
+    outside [0, V) has probability zero under both heads and is rejected.
     The step commits min(accept_len + 1, K) tokens, as in the greedy case.
     Returns (accept_len [B], next_token [B]).
     """
@@ -243,10 +244,12 @@ def sample_accept(ar_logits, draft_logits, draft_tokens, u_accept, u_resample, t
     B, K = drafts.shape
     acc = np.full(B, K, dtype=np.int64)
     nxt = drafts[:, K - 1].copy()
+    V = p_all.shape[-1]
     for b in range(B):
         for i in range(K):
             p, q, x = p_all[b, i], q_all[b, i], drafts[b, i]
-            if ua[b, i] * q[x] < p[x]:
+            # a token outside the vocabulary has p = q = 0: never accepted
+            if 0 <= x < V and ua[b, i] * q[x] < p[x]:
                 continue
             r = np.maximum(p - q, 0.0)
             total = r.sum()

@@ -597,3 +597,21 @@ def test_sample_accept_impossible_draft_is_rejected():
     for u in (0.0, 0.3, 0.999):
         acc, nxt = O.sample_accept(ar, dr, drafts, np.array([[0.0, u]]), np.array([u]), 0.9)
         assert acc[0] == 1 and nxt[0] != 7
+
+
+def test_sample_accept_out_of_vocabulary_draft_falls_back_to_p():
+    """A draft outside [0, V) has zero probability under both heads, so it is
+    rejected; with equal heads the residual max(p - q, 0) is zero everywhere
+    and the correction is then a draw from p itself: over a midpoint grid of
+    u_resample the corrections' frequencies are p to quadrature accuracy."""
+    rng = np.random.default_rng(15)
+    V, T, N = 7, 0.8, 3000
+    lg = rng.normal(0, 1.2, size=(1, 3, V))
+    p = O.softmax_t(lg, T)[0, 2]
+    grid = (np.arange(N) + 0.5) / N
+    lg_b = np.repeat(lg, N, axis=0)
+    for bad in (-1, V, 2**31 - 1):
+        drafts = np.tile(np.array([[1, 4, bad]]), (N, 1))
+        acc, nxt = O.sample_accept(lg_b, lg_b, drafts, np.full((N, 3), 0.5), grid, T)
+        assert (acc == 2).all()
+        assert np.abs(np.bincount(nxt, minlength=V) / N - p).max() <= 1.0 / N
