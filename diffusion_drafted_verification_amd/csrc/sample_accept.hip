@@ -1,0 +1,423 @@
+// Lossless acceptance of sampled drafts at temperature T > 0 on gfx950: the
+// stochastic form of the consensus step of one Orthrus decode step (Orthrus
+// explainer, gist.science arXiv 2605.12825, technical summary §2.3; §4 names
+// the temperature settings).  For each sequence, rows in order, with
+// p = softmax(ar_logits / T) and q = softmax(draft_logits / T) of the row and
+// x the draft token: x is accepted when u_accept * q[x] < p[x]; at the first
+// rejection the correction token is drawn from max(p - q, 0) by inverse CDF
+// with u_resample (from p itself when that residual is zero everywhere).
+// The uniforms are inputs.
+//
+// Three launches, no atomics, every reduction in a fixed order (run-to-run
+// bit-identical):
+//   sample_stats  one work-group per (row, 8192-logit chunk): the chunk's max
+//                 and sum of 2^((x - max) log2e / T) for both heads, 16-byte
+//                 nontemporal loads (HBM-bound: 8 bytes per logit pair);
+//   sample_resid  one work-group per (sequence, chunk): all 256 threads first
+//                 decide the sequence's rows (8 threads per row merge the
+//                 chunk pairs into the row normalisers; a wave ballot finds
+//                 the first rejection), then sum max(p - q, 0) over the
+//                 chunk of the rejected row; chunk 0 stores the decision;
+//   sample_pick   one work-group per sequence: wave scan of the chunk sums
+//                 finds the chunk where the running sum passes
+//                 u_resample * total, a work-group scan of 32-logit runs
+//                 finds the run, one thread walks the run in index order.
+// The kernel boundaries order the passes; the workspace needs no
+// initialisation.
+#include "orthrus_device.h"
+#include "orthrus_host.h"
+
+namespace orthrus {
+
+constexpr int kSampleThreads = 256;
+constexpr int kSampleWaves = kSampleThreads / kWave;
+constexpr int kSampleChunk = 8192;
+constexpr int kRowThreads = kSampleThreads / 32;  // threads per block row in the decision
+constexpr int kRun = kSampleChunk / kSampleThreads;
+
+struct SampleArgs {
+  const float* ar;      // [B, K, V]
+  const float* dr;      // [B, K, V]
+  const int32_t* drafts;
+  const float* u_acc;   // [B, K]
+  const float* u_res;   // [B]
+  int32_t* accept_len;
+  int32_t* next_token;
+  f32x4* stats;         // [B*K, nchunks] (max_p, sum_p, max_q, sum_q)
+  f32x4* rowstat;       // [B] normalisers (M_p, Z_p, M_q, Z_q) of the rejected row
+  int32_t* rej;         // [B] rejected row, K when every draft was accepted
+  float* rsum;          // [B, nchunks] residual sums of the rejected row
+  float c;              // log2(e) / T
+  int B, K, V, chunk, nchunks;
+};
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// (max m, sum s of 2^((x - m) c)) pairs; -inf logits carry no mass
+__device__ __forceinline__ void ms_merge(float& m, float& s, float m2, float s2, float c) {
+  const float mm = fmaxf(m, m2);
+  if (mm == -INFINITY) return;
+  s = s * ex2((m - mm) * c) + s2 * ex2((m2 - mm) * c);
+  m = mm;
+}
+
+__device__ __forceinline__ void ms_add1(float& m, float& s, float x, float c) { ms_merge(m, s, x, 1.f, c); }
+
+__device__ __forceinline__ void ms_add4(float& m, float& s, f32x4 v, float c) {
+  const float mm = fmaxf(m, fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
+  if (mm == -INFINITY) return;
+  s = s * ex2((m - mm) * c) + ((ex2((v[0] - mm) * c) + ex2((v[1] - mm) * c)) +
+                               (ex2((v[2] - mm) * c) + ex2((v[3] - mm) * c)));
+  m = mm;
+}
+
+// one head's chunk pair: scalar head to 16-byte alignment, vector body, tail
+__device__ __forceinline__ void chunk_pair(const float* x, int begin, int end, int tid, float c, float& m,
+                                           float& s) {
+  const int mis = (int)((reinterpret_cast<uintptr_t>(x + begin) >> 2) & 3);
+  const int head_end = min(end, begin + ((4 - mis) & 3));
+  for (int idx = begin + tid; idx < head_end; idx += kSampleThreads) ms_add1(m, s, x[idx], c);
+  const int nvec = (end - head_end) >> 2;
+  const f32x4* xv = reinterpret_cast<const f32x4*>(x + head_end);
+#pragma unroll 4
+  for (int k = tid; k < nvec; k += kSampleThreads) ms_add4(m, s, __builtin_nontemporal_load(xv + k), c);
+  for (int idx = head_end + 4 * nvec + tid; idx < end; idx += kSampleThreads) ms_add1(m, s, x[idx], c);
+}
+
+__global__ void __launch_bounds__(kSampleThreads) sample_stats(SampleArgs a) {
+  __shared__ f32x4 red[kSampleWaves];
+  const int row = blockIdx.x / a.nchunks, ck = blockIdx.x % a.nchunks;
+  const int tid = threadIdx.x;
+  const int begin = ck * a.chunk, end = min(begin + a.chunk, a.V);
+  float mp = -INFINITY, sp = 0.f, mq = -INFINITY, sq = 0.f;
+  chunk_pair(a.ar + (size_t)row * a.V, begin, end, tid, a.c, mp, sp);
+  chunk_pair(a.dr + (size_t)row * a.V, begin, end, tid, a.c, mq, sq);
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    ms_merge(mp, sp, __shfl_xor(mp, off, kWave), __shfl_xor(sp, off, kWave), a.c);
+    ms_merge(mq, sq, __shfl_xor(mq, off, kWave), __shfl_xor(sq, off, kWave), a.c);
+  }
+  if (tid % kWave == 0) red[tid / kWave] = f32x4{mp, sp, mq, sq};
+  __syncthreads();
+  if (tid == 0) {
+    mp = red[0][0], sp = red[0][1], mq = red[0][2], sq = red[0][3];
+#pragma unroll
+    for (int w = 1; w < kSampleWaves; ++w) {
+      ms_merge(mp, sp, red[w][0], red[w][1], a.c);
+      ms_merge(mq, sq, red[w][2], red[w][3], a.c);
+    }
+    a.stats[(size_t)row * a.nchunks + ck] = f32x4{mp, sp, mq, sq};
+  }
+}
+
+__device__ __forceinline__ float prob(float x, float m, float z, float c) { return ex2((x - m) * c) / z; }
+
+__device__ __forceinline__ float resid(const float* xp, const float* xq, const f32x4& n, float c, bool use_p,
+                                       int v) {
+  const float p = prob(xp[v], n[0], n[1], c);
+  return use_p ? p : fmaxf(p - prob(xq[v], n[2], n[3], c), 0.f);
+}
+
+__device__ __forceinline__ float resid4(f32x4 xp, f32x4 xq, const f32x4& n, float c) {
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) s += fmaxf(prob(xp[j], n[0], n[1], c) - prob(xq[j], n[2], n[3], c), 0.f);
+  return s;
+}
+
+__global__ void __launch_bounds__(kSampleThreads) sample_resid(SampleArgs a) {
+  __shared__ f32x4 nrm[32];
+  __shared__ int ok[32];
+  __shared__ int rej_s;
+  __shared__ float red[kSampleWaves];
+  const int b = blockIdx.x / a.nchunks, ck = blockIdx.x % a.nchunks;
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+
+  // decision: kRowThreads threads per row merge its chunk pairs (chunks
+  // sub, sub + 8, ...), a butterfly over the 8 gives the normalisers
+  {
+    const int i = tid / kRowThreads, sub = tid % kRowThreads;
+    const bool live = i < a.K;
+    const int row = b * a.K + i;
+    int x = 0;
+    float xa = 0.f, xd = 0.f;
+    bool in = false;
+    if (live && sub == 0) {
+      x = a.drafts[row];
+      in = x >= 0 && x < a.V;  // a draft outside the vocabulary is rejected
+      if (in) {
+        xa = a.ar[(size_t)row * a.V + x];
+        xd = a.dr[(size_t)row * a.V + x];
+      }
+    }
+    float mp = -INFINITY, sp = 0.f, mq = -INFINITY, sq = 0.f;
+    if (live)
+      for (int q = sub; q < a.nchunks; q += kRowThreads) {
+        const f32x4 t = a.stats[(size_t)row * a.nchunks + q];
+        ms_merge(mp, sp, t[0], t[1], a.c);
+        ms_merge(mq, sq, t[2], t[3], a.c);
+      }
+#pragma unroll
+    for (int off = 1; off < kRowThreads; off <<= 1) {
+      ms_merge(mp, sp, __shfl_xor(mp, off, kWave), __shfl_xor(sp, off, kWave), a.c);
+      ms_merge(mq, sq, __shfl_xor(mq, off, kWave), __shfl_xor(sq, off, kWave), a.c);
+    }
+    if (live && sub == 0) {
+      const float px = in ? prob(xa, mp, sp, a.c) : 0.f;
+      const float qx = in ? prob(xd, mq, sq, a.c) : 0.f;
+      ok[i] = a.u_acc[row] * qx < px;
+      nrm[i] = f32x4{mp, sp, mq, sq};
+    }
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const unsigned long long mask = __ballot(lane < a.K && !ok[lane]);
+    if (lane == 0) rej_s = mask ? (__ffsll((long long)mask) - 1) : a.K;
+  }
+  __syncthreads();
+  const int r = rej_s;
+  if (ck == 0 && tid == 0) {
+    a.accept_len[b] = r;
+    a.rej[b] = r;
+    if (r == a.K) a.next_token[b] = a.drafts[b * a.K + a.K - 1];
+    else a.rowstat[b] = nrm[r];
+  }
+  if (r == a.K) return;  // uniform: every draft accepted
+
+  const f32x4 n = nrm[r];
+  const size_t off = (size_t)(b * a.K + r) * a.V;
+  const float* xp = a.ar + off;
+  const float* xq = a.dr + off;
+  const int begin = ck * a.chunk, end = min(begin + a.chunk, a.V);
+  float s = 0.f;
+  if (((reinterpret_cast<uintptr_t>(xp) ^ reinterpret_cast<uintptr_t>(xq)) & 15) == 0) {
+    const int mis = (int)((reinterpret_cast<uintptr_t>(xp + begin) >> 2) & 3);
+    const int head_end = min(end, begin + ((4 - mis) & 3));
+    for (int v = begin + tid; v < head_end; v += kSampleThreads) s += resid(xp, xq, n, a.c, false, v);
+    const int nvec = (end - head_end) >> 2;
+    const f32x4* pv = reinterpret_cast<const f32x4*>(xp + head_end);
+    const f32x4* qv = reinterpret_cast<const f32x4*>(xq + head_end);
+#pragma unroll 4
+    for (int k = tid; k < nvec; k += kSampleThreads) s += resid4(pv[k], qv[k], n, a.c);
+    for (int v = head_end + 4 * nvec + tid; v < end; v += kSampleThreads) s += resid(xp, xq, n, a.c, false, v);
+  } else {
+    for (int v = begin + tid; v < end; v += kSampleThreads) s += resid(xp, xq, n, a.c, false, v);
+  }
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) s += __shfl_xor(s, o, kWave);
+  if (lane == 0) red[wave] = s;
+  __syncthreads();
+  if (tid == 0) {
+    float t = red[0];
+#pragma unroll
+    for (int w = 1; w < kSampleWaves; ++w) t += red[w];
+    a.rsum[(size_t)b * a.nchunks + ck] = t;
+  }
+}
+
+// inclusive prefix sum over the wave (fixed order)
+__device__ __forceinline__ float wave_scan(float x, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const float y = __shfl_up(x, o, kWave);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) x += __shfl_xor(x, o, kWave);
+  return x;
+}
+
+// mass of chunk k of the rejected row: the residual sum, or (when the
+// residual is zero everywhere) p's mass from the chunk pair
+__device__ __forceinline__ float chunk_mass(const SampleArgs& a, int b, int r, const f32x4& n, bool use_p, int k) {
+  if (!use_p) return a.rsum[(size_t)b * a.nchunks + k];
+  const f32x4 t = a.stats[(size_t)(b * a.K + r) * a.nchunks + k];
+  return t[0] == -INFINITY ? 0.f : t[1] * ex2((t[0] - n[0]) * a.c) / n[1];
+}
+
+__global__ void __launch_bounds__(kSampleThreads) sample_pick(SampleArgs a) {
+  __shared__ float wtot[kSampleWaves];
+  __shared__ int wpick[kSampleWaves];
+  __shared__ int chosen_s;
+  __shared__ float target_s;
+  const int b = blockIdx.x;
+  const int r = a.rej[b];
+  if (r >= a.K) return;  // every draft accepted: next_token is already written
+  const f32x4 n = a.rowstat[b];
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+
+  if (wave == 0) {
+    // total residual mass (lane-strided, then butterfly)
+    float t = 0.f;
+    for (int k = lane; k < a.nchunks; k += kWave) t += a.rsum[(size_t)b * a.nchunks + k];
+    t = wave_sum(t);
+    const bool use_p = !(t > 0.f);
+    if (use_p) {
+      t = 0.f;
+      for (int k = lane; k < a.nchunks; k += kWave) t += chunk_mass(a, b, r, n, true, k);
+      t = wave_sum(t);
+    }
+    const float target = a.u_res[b] * t;
+    // first chunk whose running sum passes the target; the last chunk with
+    // mass if rounding leaves the target at or past the end
+    float carry = 0.f;
+    int ck = -1, last = -1;
+    float run_ck = 0.f, run_last = 0.f;
+    for (int k0 = 0; k0 < a.nchunks && ck < 0; k0 += kWave) {
+      const int k = k0 + lane;
+      const float cs = k < a.nchunks ? chunk_mass(a, b, r, n, use_p, k) : 0.f;
+      const float incl = carry + wave_scan(cs, lane);
+      const unsigned long long hit = __ballot(cs > 0.f && incl > target);
+      const unsigned long long mass = __ballot(cs > 0.f);
+      if (hit) {
+        const int l = __ffsll((long long)hit) - 1;
+        ck = k0 + l;
+        run_ck = __shfl(incl - cs, l, kWave);
+      } else if (mass) {
+        const int l = 63 - __clzll((long long)mass);
+        last = k0 + l;
+        run_last = __shfl(incl - cs, l, kWave);
+      }
+      carry = __shfl(incl, kWave - 1, kWave);
+    }
+    if (ck < 0) {
+      ck = last < 0 ? 0 : last;
+      run_ck = run_last;
+    }
+    if (lane == 0) {
+      chosen_s = use_p ? -1 - ck : ck;  // sign carries the mode
+      target_s = target - run_ck;       // mass still to pass inside the chunk
+    }
+  }
+  __syncthreads();
+  const bool use_p = chosen_s < 0;
+  const int ck = use_p ? -1 - chosen_s : chosen_s;
+  const float base = target_s;
+  const size_t off = (size_t)(b * a.K + r) * a.V;
+  const float* xp = a.ar + off;
+  const float* xq = a.dr + off;
+  const int begin = ck * a.chunk, end = min(begin + a.chunk, a.V);
+  const int lo = min(begin + tid * kRun, end), hi = min(lo + kRun, end);
+  float s = 0.f;
+  for (int v = lo; v < hi; ++v) s += resid(xp, xq, n, a.c, use_p, v);
+  // exclusive start of each thread's run: wave scan plus the earlier waves
+  const float incl_w = wave_scan(s, lane);
+  if (lane == kWave - 1) wtot[wave] = incl_w;
+  __syncthreads();
+  float before = 0.f;
+  for (int w = 0; w < wave; ++w) before += wtot[w];
+  const float start = before + (incl_w - s);
+  const unsigned long long hit = __ballot(s > 0.f && start + s > base);
+  const unsigned long long mass = __ballot(s > 0.f);
+  if (lane == 0)
+    wpick[wave] = hit ? wave * kWave + (__ffsll((long long)hit) - 1)
+                      : (mass ? -2 - (wave * kWave + 63 - __clzll((long long)mass)) : -1);
+  __syncthreads();
+  int pick = -1, last = -1;
+  for (int w = 0; w < kSampleWaves; ++w) {
+    const int p = wpick[w];
+    if (p >= 0) {
+      pick = p;
+      break;
+    }
+    if (p <= -2) last = -2 - p;
+  }
+  const bool past_end = pick < 0;
+  if (past_end) pick = last;
+  if (pick < 0) {  // no mass in the chunk (cannot happen for a chosen chunk)
+    if (tid == 0) a.next_token[b] = begin;
+    return;
+  }
+  if (tid != pick) return;
+  float run = start;
+  int v_last = lo;
+  for (int v = lo; v < hi; ++v) {
+    const float rv = resid(xp, xq, n, a.c, use_p, v);
+    if (rv > 0.f) {
+      v_last = v;
+      if (!past_end && run + rv > base) {
+        a.next_token[b] = v;
+        return;
+      }
+    }
+    run += rv;
+  }
+  a.next_token[b] = v_last;  // rounding left the target at or past the last mass
+}
+
+static size_t sample_workspace(int batch, int block_k, int vocab, int* nchunks, size_t* off) {
+  *nchunks = (vocab + kSampleChunk - 1) / kSampleChunk;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t rows = (size_t)batch * block_k;
+  off[0] = 0;                                             // stats
+  off[1] = up(rows * *nchunks * sizeof(f32x4));           // rowstat
+  off[2] = off[1] + up((size_t)batch * sizeof(f32x4));    // rej
+  off[3] = off[2] + up((size_t)batch * sizeof(int32_t));  // rsum
+  return off[3] + up((size_t)batch * *nchunks * sizeof(float));
+}
+
+static bool sample_shape_ok(int batch, int block_k, int vocab) {
+  if (batch < 1 || block_k < 1 || block_k > 32 || vocab < 1) return false;
+  const long nchunks = (vocab + (long)kSampleChunk - 1) / kSampleChunk;
+  return (long)batch * block_k * nchunks <= 0x7fffffffL;
+}
+
+}  // namespace orthrus
+
+using namespace orthrus;
+
+extern "C" size_t orthrus_sample_accept_workspace_bytes(int32_t batch, int32_t block_k, int32_t vocab) {
+  if (!sample_shape_ok(batch, block_k, vocab)) return 0;
+  int nchunks;
+  size_t off[4];
+  return sample_workspace(batch, block_k, vocab, &nchunks, off);
+}
+
+extern "C" orthrus_status orthrus_sample_accept(const float* ar_logits, const float* draft_logits,
+                                                const int32_t* draft_tokens, const float* u_accept,
+                                                const float* u_resample, float temperature, int32_t* accept_len,
+                                                int32_t* next_token, int32_t batch, int32_t block_k, int32_t vocab,
+                                                void* workspace, size_t workspace_bytes, void* stream) {
+  if (!ar_logits || !draft_logits || !draft_tokens || !u_accept || !u_resample || !accept_len || !next_token)
+    return ORTHRUS_ERR_NULL;
+  if (!sample_shape_ok(batch, block_k, vocab)) return ORTHRUS_ERR_SHAPE;
+  if (!(temperature > 0.f) || !(temperature < INFINITY)) return ORTHRUS_ERR_SHAPE;
+  const float c = 1.4426950408889634f / temperature;
+  if (!(c < INFINITY)) return ORTHRUS_ERR_SHAPE;  // T so small that log2(e) / T overflows
+  int nchunks;
+  size_t off[4];
+  const size_t need = sample_workspace(batch, block_k, vocab, &nchunks, off);
+  if (!workspace || workspace_bytes < need || (reinterpret_cast<uintptr_t>(workspace) & 15))
+    return ORTHRUS_ERR_WORKSPACE;
+  char* ws = (char*)workspace;
+  SampleArgs a;
+  a.ar = ar_logits;
+  a.dr = draft_logits;
+  a.drafts = draft_tokens;
+  a.u_acc = u_accept;
+  a.u_res = u_resample;
+  a.accept_len = accept_len;
+  a.next_token = next_token;
+  a.stats = (f32x4*)(ws + off[0]);
+  a.rowstat = (f32x4*)(ws + off[1]);
+  a.rej = (int32_t*)(ws + off[2]);
+  a.rsum = (float*)(ws + off[3]);
+  a.c = c;
+  a.B = batch;
+  a.K = block_k;
+  a.V = vocab;
+  a.chunk = kSampleChunk;
+  a.nchunks = nchunks;
+  hipStream_t s = (hipStream_t)stream;
+  hipLaunchKernelGGL(sample_stats, dim3((unsigned)((long)batch * block_k * nchunks)), dim3(kSampleThreads), 0, s,
+                     a);
+  if (hipGetLastError() != hipSuccess) return ORTHRUS_ERR_LAUNCH;
+  hipLaunchKernelGGL(sample_resid, dim3((unsigned)((long)batch * nchunks)), dim3(kSampleThreads), 0, s, a);
+  if (hipGetLastError() != hipSuccess) return ORTHRUS_ERR_LAUNCH;
+  hipLaunchKernelGGL(sample_pick, dim3((unsigned)batch), dim3(kSampleThreads), 0, s, a);
+  return hipGetLastError() == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_LAUNCH;
+}

@@ -1,8 +1,10 @@
 """Seeded synthetic inputs for one dual-view decode step.
 
 This module only draws random numbers and lays them out; it contains none of
-the step's arithmetic (no attention, no argmax, no acceptance), so the HIP
-path and the CPU oracle can both be fed from it.
+the step's arithmetic (no attention, no greedy argmax, no acceptance), so the
+HIP path and the CPU oracle can both be fed from it.  (Sampled drafts are
+drawn from the draft head's own distribution with the Gumbel-max trick: the
+drafting that precedes the step, not part of it.)
 
 Workloads (Qwen3-shaped layers; the pages publish no kernel-level workload,
 so the shapes are the Qwen3 family the method is evaluated on):
@@ -51,7 +53,8 @@ WORKLOADS = {
 }
 
 _TENSOR_IDS = {"ctx": 1, "pages": 2, "q": 3, "k_cache": 4, "v_cache": 5, "k_blk": 6, "v_blk": 7,
-               "logits": 8, "targets": 9, "prefix": 10, "drafts": 11}
+               "logits": 8, "targets": 9, "prefix": 10, "drafts": 11, "draft_logits": 12, "gumbel": 13,
+               "u_accept": 14, "u_resample": 15}
 
 
 def _seed(seed, workload, layer, tensor):
@@ -206,3 +209,29 @@ def block_kv_bytes_per_step(block_k, layers, n_kv_heads, head_dim, elem_bytes=2)
     """Size of one block's transient K/V over all layers (the method's O(1)
     memory overhead: the block rows are a K-row buffer, not a second cache)."""
     return block_k * layers * n_kv_heads * head_dim * 2 * elem_bytes
+
+
+def make_sample_inputs(batch, block_k, vocab, temperature, seed=0, workload="", std=4.0, draft_noise=0.2,
+                       device="cpu"):
+    """Inputs of the sampled consensus at temperature T.
+
+    AR logits ~ N(0, std^2); the draft head approximates them:
+    draft_logits = ar_logits + N(0, draft_noise^2) (draft_noise = 0 gives
+    equal heads).  Draft tokens are samples of softmax(draft_logits / T),
+    drawn as argmax(draft_logits / T + Gumbel noise); u_accept [B, K] and
+    u_resample [B] are U[0, 1) fp32.  Returns
+    (ar_logits, draft_logits, draft_tokens int32, u_accept, u_resample).
+    """
+    ar, _ = make_logits(batch, block_k, vocab, seed=seed, workload=workload, std=std, device=device)
+    noise = torch.randn((batch, block_k, vocab), generator=_gen(device, _seed(seed, workload, 0, "draft_logits")),
+                        device=device, dtype=torch.float32)
+    dr = ar + noise.mul_(draft_noise)
+    u = torch.rand((batch, block_k, vocab), generator=_gen(device, _seed(seed, workload, 0, "gumbel")),
+                   device=device, dtype=torch.float64).clamp_(min=1e-300)
+    gumbel = -torch.log(-torch.log(u))
+    drafts = torch.argmax(dr.double() / temperature + gumbel, dim=-1).to(torch.int32)
+    ua = torch.rand((batch, block_k), generator=_gen(device, _seed(seed, workload, 0, "u_accept")),
+                    device=device, dtype=torch.float32)
+    ur = torch.rand((batch,), generator=_gen(device, _seed(seed, workload, 0, "u_resample")),
+                    device=device, dtype=torch.float32)
+    return ar, dr, drafts, ua, ur

@@ -45,6 +45,8 @@ SIGNATURES = {
     "orthrus_block_attn": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _DESC_P, _vp, _sz, _vp]),
     "orthrus_greedy_accept_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "orthrus_greedy_accept": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
+    "orthrus_sample_accept_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "orthrus_sample_accept": (_i32, [_vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
     "orthrus_kv_append": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _DESC_P, _vp]),
     "orthrus_kv_append_layers": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _DESC_P, _vp]),
     "orthrus_copy_probe": (_i32, [_vp, _vp, _sz, _vp]),
@@ -192,6 +194,31 @@ def greedy_accept(ar_logits, draft_tokens, *, want_ar_tokens=True, ws=None, stre
                                      B, K, V, _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "orthrus_greedy_accept")
     return acc, nxt, g
+
+
+def sample_accept(ar_logits, draft_logits, draft_tokens, u_accept, u_resample, temperature, *, ws=None,
+                  stream=None):
+    """orthrus_sample_accept: returns (accept_len [B], next_token [B]), int32
+    on the logits' device."""
+    dev = _gpu(ar_logits, draft_logits, draft_tokens, u_accept, u_resample)
+    if (ar_logits.dtype != torch.float32 or draft_logits.dtype != torch.float32
+            or u_accept.dtype != torch.float32 or u_resample.dtype != torch.float32
+            or draft_tokens.dtype != torch.int32):
+        raise OrthrusError("logits and uniforms must be fp32, draft_tokens int32")
+    B, K, V = ar_logits.shape
+    if tuple(draft_logits.shape) != (B, K, V) or tuple(draft_tokens.shape) != (B, K) \
+            or tuple(u_accept.shape) != (B, K) or tuple(u_resample.shape) != (B,):
+        raise OrthrusError("draft_logits [B, K, V], draft_tokens and u_accept [B, K], u_resample [B]")
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    nxt = torch.empty(B, dtype=torch.int32, device=dev)
+    need = lib().orthrus_sample_accept_workspace_bytes(B, K, V)
+    if ws is None:
+        ws = workspace(dev, need, "sample")
+    st = lib().orthrus_sample_accept(_ptr(ar_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(u_accept),
+                                     _ptr(u_resample), float(temperature), _ptr(acc), _ptr(nxt), B, K, V,
+                                     _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "orthrus_sample_accept")
+    return acc, nxt
 
 
 def kv_append(k_cache, v_cache, k_blk, v_blk, page_table, ctx_lens, accept_len, *, new_ctx_lens=None,

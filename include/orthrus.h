@@ -1,7 +1,8 @@
 /*
  * orthrus.h -- C ABI of the MI355X (gfx950) hot path of one Orthrus
  * dual-view decode step: block attention over a shared paged KV cache,
- * greedy consensus (argmax + longest-prefix accept) and KV append.
+ * greedy consensus (argmax + longest-prefix accept), its sampling form at
+ * temperature T > 0, and KV append.
  *
  * Semantics follow the Orthrus explainer page for "Orthrus: Memory-Efficient
  * Parallel Token Generation via Dual-View Diffusion" (gist.science, arXiv
@@ -31,8 +32,9 @@
  *                                            is P*D contiguous elements)
  *   page_table      [B, max_pages_per_seq]   int32 physical page ids
  *   ctx_lens        [B]                      int32 cached tokens per sequence
- *   ar_logits       [B, K, V]                fp32
+ *   ar_logits, draft_logits [B, K, V]        fp32
  *   draft_tokens    [B, K]                   int32
+ *   u_accept [B, K], u_resample [B]          fp32
  *   accept_len, next_token, new_ctx_lens [B] int32
  *   ar_tokens, slots[B, K]                   int32
  * Logical position p of sequence b lives in page page_table[b][p / P], slot
@@ -144,6 +146,36 @@ orthrus_status orthrus_greedy_accept(const float* ar_logits, const int32_t* draf
                                      int32_t* accept_len, int32_t* next_token, int32_t* ar_tokens,
                                      int32_t batch, int32_t block_k, int32_t vocab, void* workspace,
                                      size_t workspace_bytes, void* stream);
+
+/* Bytes of the workspace orthrus_sample_accept needs (per row and
+ * 8192-logit chunk one 16-byte pair of (max, sum) for each head, plus per
+ * sequence the decision and one residual sum per chunk).  0 for an invalid
+ * shape.  The workspace needs no initialisation. */
+size_t orthrus_sample_accept_workspace_bytes(int32_t batch, int32_t block_k, int32_t vocab);
+
+/* Lossless consensus at temperature T > 0: the stochastic form of the
+ * accept step (explainer §2.3; §4 names the sampling temperatures), the
+ * standard rejection rule under which the committed tokens follow the AR
+ * head's distribution.  For row i of sequence b, p = softmax(ar_logits/T),
+ * q = softmax(draft_logits/T) (fp32, each row's max subtracted) and
+ * x = draft_tokens[b, i]:
+ *   x is accepted when u_accept[b, i] * q[x] < p[x];
+ *   accept_len[b] = the first rejected i, or K when none is rejected;
+ *   next_token[b] = at a rejection, the smallest v whose running sum of
+ *                   r = max(p - q, 0) exceeds u_resample[b] * sum(r) (from p
+ *                   itself when r is zero everywhere); with no rejection,
+ *                   draft_tokens[b, K-1].
+ * The step commits min(accept_len + 1, K) tokens: the accepted drafts, then
+ * next_token.  The caller draws the uniforms (u_accept [B, K] and
+ * u_resample [B], fp32 in [0, 1)); draft_logits has ar_logits' layout
+ * [B, K, V] fp32.  A draft outside [0, V) is rejected.  Every row needs a
+ * finite logit; logits must not be NaN or +inf.  T must be finite with
+ * log2(e) / T finite.  1 <= K <= 32, 1 <= V < 2^31. */
+orthrus_status orthrus_sample_accept(const float* ar_logits, const float* draft_logits,
+                                     const int32_t* draft_tokens, const float* u_accept,
+                                     const float* u_resample, float temperature, int32_t* accept_len,
+                                     int32_t* next_token, int32_t batch, int32_t block_k, int32_t vocab,
+                                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Commit the accepted block rows to the shared cache (explainer §2.3: the
  * cache keeps only the committed positions).

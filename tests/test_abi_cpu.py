@@ -24,7 +24,7 @@ def declared_entry_points():
 
 def test_exports_every_declared_symbol():
     names = declared_entry_points()
-    assert len(names) == 10
+    assert len(names) == 12
     assert set(names) == set(B.SIGNATURES)
     lib = B.lib()
     for n in names:
@@ -121,6 +121,33 @@ def test_accept_and_append_validation():
                                         ctypes.byref(d), None) == 2
     assert lib.orthrus_copy_probe(FAKE, FAKE, 17, None) == 2
     assert lib.orthrus_copy_probe(None, FAKE, 16, None) == 1
+
+
+def test_sample_accept_validation():
+    lib = B.lib()
+    args = lambda **kw: dict(dict(ar=FAKE, dr=FAKE, d=FAKE, ua=FAKE, ur=FAKE, t=0.7, acc=FAKE, nxt=FAKE, b=2,
+                                   k=32, v=151936, ws=FAKE, wsb=1 << 20), **kw)
+
+    def call(**kw):
+        a = args(**kw)
+        return lib.orthrus_sample_accept(a["ar"], a["dr"], a["d"], a["ua"], a["ur"], a["t"], a["acc"], a["nxt"],
+                                         a["b"], a["k"], a["v"], a["ws"], a["wsb"], None)
+
+    for ptr in ("ar", "dr", "d", "ua", "ur", "acc", "nxt"):
+        assert call(**{ptr: None}) == 1, ptr
+    assert call(k=33) == 2 and call(k=0) == 2 and call(v=0) == 2 and call(b=0) == 2
+    for t in (0.0, -1.0, float("inf"), float("nan"), 1e-45):   # 1e-45: log2(e) / T overflows
+        assert call(t=t) == 2, t
+    # per (row, chunk) one 16-byte pair for each head pair; per sequence the
+    # row normalisers, the decision and one residual sum per chunk (each
+    # region rounded up to 256 bytes)
+    up = lambda x: -(-x // 256) * 256
+    need = lib.orthrus_sample_accept_workspace_bytes(2, 32, 151936)
+    assert need == up(64 * 19 * 16) + up(2 * 16) + up(2 * 4) + up(2 * 19 * 4)
+    assert lib.orthrus_sample_accept_workspace_bytes(1, 33, 100) == 0
+    assert call(wsb=need - 1) == 4
+    assert call(ws=None, wsb=need) == 4
+    assert call(ws=ctypes.c_void_p(4096 + 8), wsb=need) == 4   # 16-byte alignment
 
 
 def test_binding_refuses_cpu_tensors():

@@ -1,0 +1,230 @@
+"""Parity of the sampled consensus (temperature T > 0) through the C ABI with
+the fp64 CPU oracle.
+
+accept_len and next_token are integers, so the bar is equality.  The kernel
+takes the two decisions in fp32 (p[x] against u * q[x], and the inverse-CDF
+crossing of u * sum(r)), the oracle in fp64; a sequence whose fp64 margin at
+either decision is within the fp32 rounding of the inputs (relative 1e-4 of
+the compared quantities) may go either way.  Such sequences are counted and
+checked for validity instead: every accepted row satisfies the rule within
+the margin, the rejected row fails it within the margin, and the correction
+token carries residual mass with its cumulative interval within the margin
+of the target.  Each test also bounds how many sequences were excused.
+"""
+
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+from diffusion_drafted_verification_amd import inputs as I
+from oracle import orthrus_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+MARGIN = 1e-4
+
+
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def ob():
+    from diffusion_drafted_verification_amd import orthrus
+    return orthrus
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def run_gpu(ar, dr, drafts, ua, ur, T, ws=None):
+    d = dev()
+    acc, nxt = ob().sample_accept(ar.to(d), dr.to(d), drafts.to(d), ua.to(d), ur.to(d), T, ws=ws)
+    torch.cuda.synchronize()
+    return acc.cpu().numpy().astype(np.int64), nxt.cpu().numpy().astype(np.int64)
+
+
+def residual(p, q):
+    r = np.maximum(p - q, 0.0)
+    if r.sum() <= 0.0:
+        return p
+    return r
+
+
+def check_sample(ar, dr, drafts, ua, ur, T, *, max_excused=0.1, ws=None):
+    """GPU vs oracle; returns (accept_len, next_token, n_excused)."""
+    ga, gn = run_gpu(ar, dr, drafts, ua, ur, T, ws=ws)
+    ra, rn = O.sample_accept(ar.numpy(), dr.numpy(), drafts.numpy(), ua.numpy(), ur.numpy(), T)
+    p_all = O.softmax_t(ar.numpy(), T)
+    q_all = O.softmax_t(dr.numpy(), T)
+    x_all = drafts.numpy().astype(np.int64)
+    u = ua.numpy().astype(np.float64)
+    uR = ur.numpy().astype(np.float64)
+    B, K, V = p_all.shape
+    excused = 0
+    for b in range(B):
+        if ga[b] == ra[b] and gn[b] == rn[b]:
+            continue
+        # either decision may be within rounding: check the GPU's result is
+        # valid to the margin
+        excused += 1
+        a = int(ga[b])
+        assert 0 <= a <= K, (b, a)
+        for i in range(min(a + 1, K)):
+            x = x_all[b, i]
+            inv = 0 <= x < V
+            lhs = u[b, i] * q_all[b, i, x] if inv else 0.0
+            rhs = p_all[b, i, x] if inv else 0.0
+            scale = max(lhs, rhs, 1e-30)
+            if i < a:
+                assert inv and lhs < rhs + MARGIN * scale, (b, i, lhs, rhs)
+            else:
+                assert not inv or lhs >= rhs - MARGIN * scale, (b, i, lhs, rhs)
+        if a == K:
+            assert gn[b] == x_all[b, K - 1]
+            continue
+        r = residual(p_all[b, a], q_all[b, a])
+        g = int(gn[b])
+        assert 0 <= g < V, (b, g)
+        c = np.cumsum(r)
+        tot = r.sum()
+        target = uR[b] * tot
+        lo = c[g - 1] if g > 0 else 0.0
+        assert r[g] > -MARGIN * tot and (r[g] > 0 or abs(c[g] - target) <= MARGIN * tot), (b, g, r[g])
+        assert lo - MARGIN * tot <= target <= c[g] + MARGIN * tot, (b, g, lo, target, c[g])
+    assert excused <= max(1, max_excused * B), (excused, B)
+    return ga, gn, excused
+
+
+@pytest.mark.parametrize("T", [0.6, 1.0])
+def test_sample_tiny(T):
+    say("sample tiny", T)
+    args = I.make_sample_inputs(8, 32, 1024, T, seed=3, workload="tiny_fp32")
+    ga, _, _ = check_sample(*args, T)
+    assert len(set(ga.tolist())) > 2   # a spread of accept lengths
+
+
+@pytest.mark.parametrize("B,T", [(1, 1.0), (4, 0.6), (16, 1.0), (16, 0.6)])
+def test_sample_qwen_vocab(B, T):
+    say("sample qwen vocab", B, T)
+    args = I.make_sample_inputs(B, 32, I.QWEN3_VOCAB, T, seed=B, workload="qwen3_8b_8k")
+    check_sample(*args, T)
+
+
+@pytest.mark.parametrize("K", [1, 7, 32])
+@pytest.mark.parametrize("V", [1, 3, 8191, 8193, 20011])
+def test_sample_ragged_shapes(K, V):
+    """Block sizes 1..32 and vocabularies from one token to a ragged tail over
+    several 8192-logit chunks (rows start unaligned when V % 4 != 0)."""
+    say("sample ragged", K, V)
+    args = I.make_sample_inputs(5, K, V, 0.8, seed=K * 7 + V, workload="")
+    ga, gn, _ = check_sample(*args, 0.8)
+    if V == 1:
+        assert (ga == K).all() and (gn == 0).all()
+
+
+def test_sample_heads_with_different_alignment():
+    """draft_logits starting 4 bytes off ar_logits' 16-byte alignment takes
+    the residual pass's scalar path; the results are the same."""
+    say("sample misaligned heads")
+    ar, dr, drafts, ua, ur = I.make_sample_inputs(4, 32, 20000, 0.9, seed=21, workload="")
+    d = dev()
+    buf = torch.empty(dr.numel() + 1, dtype=torch.float32, device=d)
+    dr_off = buf[1:].view(dr.shape)
+    dr_off.copy_(dr.to(d))
+    acc, nxt = ob().sample_accept(ar.to(d), dr_off, drafts.to(d), ua.to(d), ur.to(d), 0.9)
+    a2, n2 = ob().sample_accept(ar.to(d), dr.to(d), drafts.to(d), ua.to(d), ur.to(d), 0.9)
+    torch.cuda.synchronize()
+    assert torch.equal(acc, a2) and torch.equal(nxt, n2)
+    check_sample(ar, dr, drafts, ua, ur, 0.9)
+
+
+def test_sample_equal_heads_accept_everything():
+    say("sample equal heads")
+    ar, _, drafts, ua, ur = I.make_sample_inputs(6, 32, 5000, 1.0, seed=5, workload="", draft_noise=0.0)
+    ga, gn = run_gpu(ar, ar.clone(), drafts, ua, ur, 1.0)
+    assert (ga == 32).all() and np.array_equal(gn, drafts[:, -1].numpy())
+
+
+def test_sample_zero_probability_and_out_of_vocabulary_drafts():
+    """A draft with -inf AR logit (p[x] = 0) or outside [0, V) is rejected at
+    any uniform; with equal heads the correction comes from p (the residual
+    is zero everywhere)."""
+    say("sample impossible drafts")
+    B, K, V, T = 6, 8, 3000, 0.7
+    ar, dr, drafts, ua, ur = I.make_sample_inputs(B, K, V, T, seed=6, workload="")
+    drafts = drafts.clone()
+    ar = ar.clone()
+    # b0: -inf at the draft of row 3; b1: draft -1 at row 0; b2: draft V at row 5
+    ar[0, 3, drafts[0, 3]] = -float("inf")
+    drafts[1, 0] = -1
+    drafts[2, 5] = V
+    # b3..b5: equal heads with a draft outside the vocabulary at row 2
+    dr = dr.clone()
+    dr[3:] = ar[3:]
+    drafts[3:, 2] = torch.tensor([-5, V, 2**31 - 1], dtype=torch.int32)
+    ga, gn, _ = check_sample(ar, dr, drafts, ua, ur, T, max_excused=0)
+    assert ga[0] <= 3 and ga[1] == 0 and ga[2] <= 5
+    assert (ga[3:] == 2).all()
+    assert gn[0] != drafts[0, 3] or ga[0] < 3
+
+
+def test_sample_low_temperature():
+    """T = 0.02: p and q are close to one-hot; the rule then behaves like the
+    greedy consensus and the decisions are far from their boundaries."""
+    say("sample low T")
+    args = I.make_sample_inputs(8, 32, I.QWEN3_VOCAB, 0.02, seed=8, workload="qwen3_8b_8k")
+    check_sample(*args, 0.02)
+
+
+def test_sample_high_temperature():
+    say("sample high T")
+    args = I.make_sample_inputs(4, 32, 50000, 8.0, seed=9, workload="", draft_noise=1.0)
+    check_sample(*args, 8.0)
+
+
+def test_sample_deterministic_and_workspace_reuse():
+    """A workspace full of stale bytes, reused across shapes, gives the same
+    results as a fresh one, and repeated calls are bit-identical."""
+    say("sample workspace reuse")
+    d = dev()
+    need = ob().lib().orthrus_sample_accept_workspace_bytes(16, 32, I.QWEN3_VOCAB)
+    ws = torch.full((need,), 0xA5, dtype=torch.uint8, device=d)
+    for (B, K, V, T, s) in [(16, 32, I.QWEN3_VOCAB, 1.0, 1), (3, 5, 9000, 0.7, 2), (16, 32, I.QWEN3_VOCAB, 0.6, 3)]:
+        args = I.make_sample_inputs(B, K, V, T, seed=s, workload="qwen3_8b_8k")
+        ga, gn, _ = check_sample(*args, T, ws=ws)
+        ga2, gn2 = run_gpu(*args, T, ws=ws)
+        ga3, gn3 = run_gpu(*args, T)
+        assert np.array_equal(ga, ga2) and np.array_equal(gn, gn2)
+        assert np.array_equal(ga, ga3) and np.array_equal(gn, gn3)
+
+
+def test_sample_lossless_monte_carlo():
+    """The lossless property on the GPU: every sequence shares one AR row p
+    and one draft row q; drafts are independent samples of q and the
+    uniforms are independent.  The first committed token (the draft when
+    row 0 is accepted, else the correction) must follow p: each token's
+    frequency is within 5 binomial standard deviations of p."""
+    say("sample lossless monte carlo")
+    rng = np.random.default_rng(77)
+    N, V, T = 60000, 6, 0.7
+    ar1 = rng.normal(0, 1.5, size=V)
+    dr1 = rng.normal(0, 1.5, size=V)
+    p = O.softmax_t(ar1[None], T)[0]
+    q = O.softmax_t(dr1[None], T)[0]
+    ar = torch.from_numpy(np.tile(ar1, (N, 2, 1))).float()
+    dr = torch.from_numpy(np.tile(dr1, (N, 2, 1))).float()
+    x = rng.choice(V, size=(N, 2), p=q / q.sum()).astype(np.int32)
+    ua = torch.from_numpy(rng.random((N, 2)).astype(np.float32))
+    ur = torch.from_numpy(rng.random(N).astype(np.float32))
+    ga, gn = run_gpu(ar, dr, torch.from_numpy(x), ua, ur, T)
+    first = np.where(ga >= 1, x[:, 0], gn)
+    freq = np.bincount(first, minlength=V) / N
+    sd = np.sqrt(p * (1 - p) / N)
+    assert (np.abs(freq - p) <= 5 * sd + 1e-12).all(), (freq, p)
+    # and the draft distribution alone would fail the same check
+    assert (np.abs(q - p) > 5 * sd).any()

@@ -50,3 +50,27 @@ def test_drafts_agree_on_exactly_the_prefix():
     d = I.make_drafts(t, pre, 1000, seed=1).numpy()
     for b, a in enumerate(pre):
         assert np.array_equal(d[b, :a], t[b, :a]) and d[b, a] != t[b, a]
+
+
+def test_sample_inputs_shapes_seeds_and_draft_distribution():
+    """Seeded and reproducible; drafts follow softmax(draft_logits / T): at a
+    tiny vocabulary the empirical draft frequencies of many rows sharing one
+    draft row match that softmax."""
+    a = I.make_sample_inputs(3, 5, 100, 0.7, seed=4, workload="qwen3_8b_8k")
+    b = I.make_sample_inputs(3, 5, 100, 0.7, seed=4, workload="qwen3_8b_8k")
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    ar, dr, d, ua, ur = a
+    assert ar.shape == dr.shape == (3, 5, 100) and d.shape == ua.shape == (3, 5) and ur.shape == (3,)
+    assert d.dtype == torch.int32 and ua.dtype == ur.dtype == torch.float32
+    assert float(ua.min()) >= 0 and float(ua.max()) < 1
+    assert 0.1 < float((dr - ar).std()) < 0.3            # draft head near the AR head
+    # each draft is a sample of its own row's softmax(draft_logits / T): over
+    # many rows the indicator minus the row's probability averages to zero
+    n, V, T = 20000, 4, 0.9
+    _, dr, d, _, _ = I.make_sample_inputs(1, n, V, T, seed=1, workload="", std=1.0)
+    q = torch.softmax(dr[0].double() / T, dim=-1)
+    ind = torch.nn.functional.one_hot(d[0].long(), V).double()
+    dev_ = (ind - q).mean(0)
+    sd = torch.sqrt((q * (1 - q)).mean(0) / n)
+    assert (dev_.abs() < 5 * sd).all(), (dev_, sd)
