@@ -47,6 +47,7 @@ def parse():
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a graph")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--no-sample", action="store_true", help="skip the sampled-consensus timing")
     p.add_argument("--no-long-context", action="store_true",
                    help="skip the 36-layer step at batch 4, 32768 cached tokens")
     p.add_argument("--copy-probe-mib", type=int, default=0,
@@ -177,6 +178,36 @@ def measured_traffic(root, batch, ctx):
     return None if w is None else int(w["hbm_bytes_per_call"])
 
 
+def sample_accept_timing(torch, ob, I, use_graph, temperature=1.0):
+    """Sampled consensus (orthrus_sample_accept) over both heads' fp32 logits
+    [B, 32, 151936] at B = 1 and 16.  Each graph replay cycles through enough
+    input copies (>= 600 MB) that every call reads its logits from HBM, not
+    from the 256 MB Infinity Cache.  Algorithmic bytes per call: both heads'
+    logits once, 2 * B * K * V * 4."""
+    d = torch.device("cuda:0")
+    V, K = I.QWEN3_VOCAB, 32
+    out = {}
+    for bs in (1, 16):
+        args = I.make_sample_inputs(bs, K, V, temperature, seed=bs, workload="qwen3_8b_8k", device=d)
+        nbytes = 2 * bs * K * V * 4
+        n = max(2, math.ceil(600e6 / nbytes))
+        sets = [args] + [tuple(t.clone() for t in args) for _ in range(n - 1)]
+        ws = torch.empty(ob.lib().orthrus_sample_accept_workspace_bytes(bs, K, V), dtype=torch.uint8, device=d)
+        acc, _ = ob.sample_accept(*args, temperature, ws=ws)
+        mean_acc = float(acc.float().mean().item())
+        fn = lambda: [ob.sample_accept(*c, temperature, ws=ws) for c in sets]
+        rep = capture(torch, fn) if use_graph else fn
+        ms = time_region(torch, rep, 10, 2) / n
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[f"bs{bs}"] = {"us_per_call": round(ms * 1e3, 2), "bytes_per_call": nbytes, "gbs": round(gbs, 1),
+                          "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "mean_accept_len": round(mean_acc, 2),
+                          "input_copies": n}
+        del sets, args, rep, ws
+        torch.cuda.empty_cache()
+    return {"kernel": "orthrus_sample_accept (sample_stats + sample_resid + sample_pick)",
+            "temperature": temperature, "vocab": V, "block_k": K, **out}
+
+
 def cpu_baseline(step, I, seconds):
     """The fp64 oracle, as is, on one layer of the step (both views, accept,
     append) at the same shapes; repeated for about `seconds`."""
@@ -299,6 +330,13 @@ def main():
         del s5, rep5
         torch.cuda.empty_cache()
 
+    sample = None
+    if not args.no_sample:
+        log("sampled consensus")
+        step = None
+        torch.cuda.empty_cache()
+        sample = sample_accept_timing(torch, ob, I, use_graph)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline")
@@ -314,7 +352,8 @@ def main():
                        "batch": args.batch, "ctx": args.ctx, "block_k": 32, "layers": args.layers,
                        "graph": use_graph, "parallelism": "none (1 GPU)"},
             "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-            "roofline": roof, "cpu_baseline": cpu, "sweep": sweep or None, "long_context_step": longctx}
+            "roofline": roof, "cpu_baseline": cpu, "sweep": sweep or None, "long_context_step": longctx,
+            "sample_accept": sample}
     print(json.dumps(line), flush=True)
 
 

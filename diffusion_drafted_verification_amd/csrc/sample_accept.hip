@@ -44,7 +44,7 @@ struct SampleArgs {
   int32_t* accept_len;
   int32_t* next_token;
   f32x4* stats;         // [B*K, nchunks] (max_p, sum_p, max_q, sum_q)
-  f32x4* rowstat;       // [B] normalisers (M_p, Z_p, M_q, Z_q) of the rejected row
+  f32x4* rowstat;       // [B] (M_p, 1 / Z_p, M_q, 1 / Z_q) of the rejected row
   int32_t* rej;         // [B] rejected row, K when every draft was accepted
   float* rsum;          // [B, nchunks] residual sums of the rejected row
   float c;              // log2(e) / T
@@ -61,8 +61,6 @@ __device__ __forceinline__ void ms_merge(float& m, float& s, float m2, float s2,
   m = mm;
 }
 
-__device__ __forceinline__ void ms_add1(float& m, float& s, float x, float c) { ms_merge(m, s, x, 1.f, c); }
-
 __device__ __forceinline__ void ms_add4(float& m, float& s, f32x4 v, float c) {
   const float mm = fmaxf(m, fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3])));
   if (mm == -INFINITY) return;
@@ -71,17 +69,22 @@ __device__ __forceinline__ void ms_add4(float& m, float& s, f32x4 v, float c) {
   m = mm;
 }
 
-// one head's chunk pair: scalar head to 16-byte alignment, vector body, tail
-__device__ __forceinline__ void chunk_pair(const float* x, int begin, int end, int tid, float c, float& m,
-                                           float& s) {
+constexpr int kVecPerThread = kSampleChunk / 4 / kSampleThreads;
+
+// [begin, end) of one row as a scalar head up to 16-byte alignment (< 4
+// logits), whole 16-byte vectors (at most kVecPerThread per thread) and a
+// scalar tail (< 4 logits)
+struct Split16 {
+  int head_end, nvec, tail;
+};
+
+__device__ __forceinline__ Split16 split16(const float* x, int begin, int end) {
   const int mis = (int)((reinterpret_cast<uintptr_t>(x + begin) >> 2) & 3);
-  const int head_end = min(end, begin + ((4 - mis) & 3));
-  for (int idx = begin + tid; idx < head_end; idx += kSampleThreads) ms_add1(m, s, x[idx], c);
-  const int nvec = (end - head_end) >> 2;
-  const f32x4* xv = reinterpret_cast<const f32x4*>(x + head_end);
-#pragma unroll 4
-  for (int k = tid; k < nvec; k += kSampleThreads) ms_add4(m, s, __builtin_nontemporal_load(xv + k), c);
-  for (int idx = head_end + 4 * nvec + tid; idx < end; idx += kSampleThreads) ms_add1(m, s, x[idx], c);
+  Split16 sp;
+  sp.head_end = min(end, begin + ((4 - mis) & 3));
+  sp.nvec = (end - sp.head_end) >> 2;
+  sp.tail = sp.head_end + 4 * sp.nvec;
+  return sp;
 }
 
 __global__ void __launch_bounds__(kSampleThreads) sample_stats(SampleArgs a) {
@@ -89,28 +92,59 @@ __global__ void __launch_bounds__(kSampleThreads) sample_stats(SampleArgs a) {
   const int row = blockIdx.x / a.nchunks, ck = blockIdx.x % a.nchunks;
   const int tid = threadIdx.x;
   const int begin = ck * a.chunk, end = min(begin + a.chunk, a.V);
-  float mp = -INFINITY, sp = 0.f, mq = -INFINITY, sq = 0.f;
-  chunk_pair(a.ar + (size_t)row * a.V, begin, end, tid, a.c, mp, sp);
-  chunk_pair(a.dr + (size_t)row * a.V, begin, end, tid, a.c, mq, sq);
+  const float* xp = a.ar + (size_t)row * a.V;
+  const float* xq = a.dr + (size_t)row * a.V;
+  const Split16 sp = split16(xp, begin, end), sq_ = split16(xq, begin, end);
+  const f32x4* pv = reinterpret_cast<const f32x4*>(xp + sp.head_end);
+  const f32x4* qv = reinterpret_cast<const f32x4*>(xq + sq_.head_end);
+  const f32x4 none = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  // every load of both heads is issued before any is consumed
+  f32x4 vp[kVecPerThread], vq[kVecPerThread];
+#pragma unroll
+  for (int j = 0; j < kVecPerThread; ++j) {
+    const int k = tid + kSampleThreads * j;
+    vp[j] = k < sp.nvec ? __builtin_nontemporal_load(pv + k) : none;
+    vq[j] = k < sq_.nvec ? __builtin_nontemporal_load(qv + k) : none;
+  }
+  const int hi_ = begin + tid, ti = sp.tail + tid, tq = sq_.tail + tid, hq = begin + tid;
+  const float ph = hi_ < sp.head_end ? xp[hi_] : -INFINITY, pt = ti < end ? xp[ti] : -INFINITY;
+  const float qh = hq < sq_.head_end ? xq[hq] : -INFINITY, qt = tq < end ? xq[tq] : -INFINITY;
+  float mp = -INFINITY, sp_ = 0.f, mq = -INFINITY, sq = 0.f;
+  ms_add4(mp, sp_, f32x4{ph, pt, -INFINITY, -INFINITY}, a.c);
+  ms_add4(mq, sq, f32x4{qh, qt, -INFINITY, -INFINITY}, a.c);
+#pragma unroll
+  for (int j = 0; j < kVecPerThread; ++j) {
+    ms_add4(mp, sp_, vp[j], a.c);
+    ms_add4(mq, sq, vq[j], a.c);
+  }
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
-    ms_merge(mp, sp, __shfl_xor(mp, off, kWave), __shfl_xor(sp, off, kWave), a.c);
+    ms_merge(mp, sp_, __shfl_xor(mp, off, kWave), __shfl_xor(sp_, off, kWave), a.c);
     ms_merge(mq, sq, __shfl_xor(mq, off, kWave), __shfl_xor(sq, off, kWave), a.c);
   }
-  if (tid % kWave == 0) red[tid / kWave] = f32x4{mp, sp, mq, sq};
+  if (tid % kWave == 0) red[tid / kWave] = f32x4{mp, sp_, mq, sq};
   __syncthreads();
   if (tid == 0) {
-    mp = red[0][0], sp = red[0][1], mq = red[0][2], sq = red[0][3];
+    mp = red[0][0], sp_ = red[0][1], mq = red[0][2], sq = red[0][3];
 #pragma unroll
     for (int w = 1; w < kSampleWaves; ++w) {
-      ms_merge(mp, sp, red[w][0], red[w][1], a.c);
+      ms_merge(mp, sp_, red[w][0], red[w][1], a.c);
       ms_merge(mq, sq, red[w][2], red[w][3], a.c);
     }
-    a.stats[(size_t)row * a.nchunks + ck] = f32x4{mp, sp, mq, sq};
+    a.stats[(size_t)row * a.nchunks + ck] = f32x4{mp, sp_, mq, sq};
   }
 }
 
-__device__ __forceinline__ float prob(float x, float m, float z, float c) { return ex2((x - m) * c) / z; }
+// probability of logit x from the row's (max m, reciprocal of the sum rz).
+// The product is rounded on its own (never contracted into a later p - q),
+// so equal heads give p - q == 0 exactly and a zero residual.
+__device__ __forceinline__ float prob(float x, float m, float rz, float c) {
+#pragma clang fp contract(off)
+  return ex2((x - m) * c) * rz;
+}
+
+// row normalisers (M_p, Z_p, M_q, Z_q) -> (M_p, 1 / Z_p, M_q, 1 / Z_q)
+__device__ __forceinline__ f32x4 recip_sums(f32x4 n) { return f32x4{n[0], 1.f / n[1], n[2], 1.f / n[3]}; }
 
 __device__ __forceinline__ float resid(const float* xp, const float* xq, const f32x4& n, float c, bool use_p,
                                        int v) {
@@ -163,10 +197,11 @@ __global__ void __launch_bounds__(kSampleThreads) sample_resid(SampleArgs a) {
       ms_merge(mq, sq, __shfl_xor(mq, off, kWave), __shfl_xor(sq, off, kWave), a.c);
     }
     if (live && sub == 0) {
-      const float px = in ? prob(xa, mp, sp, a.c) : 0.f;
-      const float qx = in ? prob(xd, mq, sq, a.c) : 0.f;
+      const f32x4 nr = recip_sums(f32x4{mp, sp, mq, sq});
+      const float px = in ? prob(xa, nr[0], nr[1], a.c) : 0.f;
+      const float qx = in ? prob(xd, nr[2], nr[3], a.c) : 0.f;
       ok[i] = a.u_acc[row] * qx < px;
-      nrm[i] = f32x4{mp, sp, mq, sq};
+      nrm[i] = nr;
     }
   }
   __syncthreads();
@@ -236,7 +271,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 __device__ __forceinline__ float chunk_mass(const SampleArgs& a, int b, int r, const f32x4& n, bool use_p, int k) {
   if (!use_p) return a.rsum[(size_t)b * a.nchunks + k];
   const f32x4 t = a.stats[(size_t)(b * a.K + r) * a.nchunks + k];
-  return t[0] == -INFINITY ? 0.f : t[1] * ex2((t[0] - n[0]) * a.c) / n[1];
+  return t[0] == -INFINITY ? 0.f : t[1] * ex2((t[0] - n[0]) * a.c) * n[1];
 }
 
 __global__ void __launch_bounds__(kSampleThreads) sample_pick(SampleArgs a) {
@@ -245,23 +280,28 @@ __global__ void __launch_bounds__(kSampleThreads) sample_pick(SampleArgs a) {
   __shared__ int chosen_s;
   __shared__ float target_s;
   const int b = blockIdx.x;
-  const int r = a.rej[b];
-  if (r >= a.K) return;  // every draft accepted: next_token is already written
-  const f32x4 n = a.rowstat[b];
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  // the decision, the normalisers and the first 64 chunk sums are loaded
+  // together (rowstat is only used when a row was rejected)
+  const int r = a.rej[b];
+  const f32x4 n = a.rowstat[b];
+  float cs0 = (wave == 0 && lane < a.nchunks) ? a.rsum[(size_t)b * a.nchunks + lane] : 0.f;
+  const float u = a.u_res[b];
+  if (r >= a.K) return;  // every draft accepted: next_token is already written
 
   if (wave == 0) {
     // total residual mass (lane-strided, then butterfly)
-    float t = 0.f;
-    for (int k = lane; k < a.nchunks; k += kWave) t += a.rsum[(size_t)b * a.nchunks + k];
+    float t = cs0;
+    for (int k = lane + kWave; k < a.nchunks; k += kWave) t += a.rsum[(size_t)b * a.nchunks + k];
     t = wave_sum(t);
     const bool use_p = !(t > 0.f);
     if (use_p) {
-      t = 0.f;
-      for (int k = lane; k < a.nchunks; k += kWave) t += chunk_mass(a, b, r, n, true, k);
+      cs0 = lane < a.nchunks ? chunk_mass(a, b, r, n, true, lane) : 0.f;
+      t = cs0;
+      for (int k = lane + kWave; k < a.nchunks; k += kWave) t += chunk_mass(a, b, r, n, true, k);
       t = wave_sum(t);
     }
-    const float target = a.u_res[b] * t;
+    const float target = u * t;
     // first chunk whose running sum passes the target; the last chunk with
     // mass if rounding leaves the target at or past the end
     float carry = 0.f;
@@ -269,7 +309,7 @@ __global__ void __launch_bounds__(kSampleThreads) sample_pick(SampleArgs a) {
     float run_ck = 0.f, run_last = 0.f;
     for (int k0 = 0; k0 < a.nchunks && ck < 0; k0 += kWave) {
       const int k = k0 + lane;
-      const float cs = k < a.nchunks ? chunk_mass(a, b, r, n, use_p, k) : 0.f;
+      const float cs = k0 == 0 ? cs0 : (k < a.nchunks ? chunk_mass(a, b, r, n, use_p, k) : 0.f);
       const float incl = carry + wave_scan(cs, lane);
       const unsigned long long hit = __ballot(cs > 0.f && incl > target);
       const unsigned long long mass = __ballot(cs > 0.f);
@@ -302,8 +342,21 @@ __global__ void __launch_bounds__(kSampleThreads) sample_pick(SampleArgs a) {
   const float* xq = a.dr + off;
   const int begin = ck * a.chunk, end = min(begin + a.chunk, a.V);
   const int lo = min(begin + tid * kRun, end), hi = min(lo + kRun, end);
+  // the thread's run of logits, all loads in flight, then its masses kept
+  // in registers for the walk
+  float xa[kRun], xd[kRun], rv[kRun];
+#pragma unroll
+  for (int j = 0; j < kRun; ++j) {
+    xa[j] = lo + j < hi ? xp[lo + j] : -INFINITY;
+    xd[j] = lo + j < hi ? xq[lo + j] : -INFINITY;
+  }
   float s = 0.f;
-  for (int v = lo; v < hi; ++v) s += resid(xp, xq, n, a.c, use_p, v);
+#pragma unroll
+  for (int j = 0; j < kRun; ++j) {
+    const float p = prob(xa[j], n[0], n[1], a.c);
+    rv[j] = lo + j >= hi ? 0.f : (use_p ? p : fmaxf(p - prob(xd[j], n[2], n[3], a.c), 0.f));
+    s += rv[j];
+  }
   // exclusive start of each thread's run: wave scan plus the earlier waves
   const float incl_w = wave_scan(s, lane);
   if (lane == kWave - 1) wtot[wave] = incl_w;
@@ -333,20 +386,20 @@ __global__ void __launch_bounds__(kSampleThreads) sample_pick(SampleArgs a) {
     return;
   }
   if (tid != pick) return;
+  // walk the run in index order: the first logit whose running sum passes
+  // the target, else (rounding left the target at or past the run's mass)
+  // the last logit with mass
   float run = start;
-  int v_last = lo;
-  for (int v = lo; v < hi; ++v) {
-    const float rv = resid(xp, xq, n, a.c, use_p, v);
-    if (rv > 0.f) {
-      v_last = v;
-      if (!past_end && run + rv > base) {
-        a.next_token[b] = v;
-        return;
-      }
+  int found = -1, v_last = lo;
+#pragma unroll
+  for (int j = 0; j < kRun; ++j) {
+    if (found < 0 && rv[j] > 0.f) {
+      v_last = lo + j;
+      if (!past_end && run + rv[j] > base) found = lo + j;
     }
-    run += rv;
+    run += rv[j];
   }
-  a.next_token[b] = v_last;  // rounding left the target at or past the last mass
+  a.next_token[b] = found >= 0 ? found : v_last;
 }
 
 static size_t sample_workspace(int batch, int block_k, int vocab, int* nchunks, size_t* off) {
