@@ -16,7 +16,9 @@ Output: one JSON line.  `value` = block-attention KV bytes read per step /
 step time (GB/s).  `roofline` = the block-attention call (main + combine
 kernels) timed alone with HIP events on its stream, against the 8 TB/s HBM
 peak.  `cpu_baseline` = the fp64 oracle on a bounded sample of the same step
-on the host cores.
+on the host cores.  `sample_accept` = the sampled consensus at temperature 1
+(orthrus_sample_accept over both heads' [B, 32, 151936] fp32 logits) timed
+on its own at B = 1 and 16; it is not part of the greedy step above.
 """
 
 from __future__ import annotations
