@@ -41,6 +41,8 @@ Readings of points the pages leave open (each one is listed in the design doc):
 * grouped-query attention maps query head h to KV head h * Hkv // Hq; the
   softmax scale defaults to 1/sqrt(D); no soft-cap, window or bias;
 * argmax ties go to the lowest index; -0.0 equals +0.0 (IEEE compare);
+* the LM head is a plain linear map hidden @ weight^T with weight stored as
+  [V, H] (no bias, no logit scaling or soft-cap);
 * at temperature T > 0 a draft is accepted when u * q[x] < p[x] (p, q the
   AR and diffusion softmaxes at T; u a given uniform), and the correction at
   the first rejection is drawn from max(p - q, 0) by inverse CDF with a
@@ -208,6 +210,33 @@ def greedy_accept(ar_logits, draft_tokens):
     acc = np.array([accept_prefix(drafts[b], g[b]) for b in range(B)], dtype=np.int64)
     nxt = np.array([g[b, min(acc[b], K - 1)] for b in range(B)], dtype=np.int64)
     return acc, nxt, g
+
+
+def lm_head_logits(hidden, weight):
+    """Logits of the language-model head: logits[m, v] = sum_k hidden[m, k] *
+    weight[v, k], in fp64 (products of bf16 values are exact in fp64).
+
+    hidden [..., H] (the final hidden states of the block rows), weight
+    [V, H] (one row per vocabulary entry, the usual linear-layer layout).
+    The LM head turns each view's block rows into the token distributions
+    that §2.3 compares (diffusion drafts, AR targets).
+    """
+    h = _f64(hidden)
+    w = _f64(weight)
+    return h @ w.T
+
+
+def lm_head_argmax(hidden, weight):
+    """Greedy token of each row: greedy_argmax of lm_head_logits (lowest
+    index on ties)."""
+    return greedy_argmax(lm_head_logits(hidden, weight))
+
+
+def lm_head_greedy_accept(hidden, weight, draft_tokens):
+    """Greedy consensus straight from the AR view's final hidden states
+    [B, K, H]: greedy_accept of lm_head_logits.  Returns (accept_len [B],
+    next_token [B], g [B, K])."""
+    return greedy_accept(lm_head_logits(hidden, weight), draft_tokens)
 
 
 def softmax_t(logits, temperature):

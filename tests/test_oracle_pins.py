@@ -615,3 +615,70 @@ def test_sample_accept_out_of_vocabulary_draft_falls_back_to_p():
         acc, nxt = O.sample_accept(lg_b, lg_b, drafts, np.full((N, 3), 0.5), grid, T)
         assert (acc == 2).all()
         assert np.abs(np.bincount(nxt, minlength=V) / N - p).max() <= 1.0 / N
+
+
+# ---------------------------------------------------------------------------
+# LM head with argmax
+# ---------------------------------------------------------------------------
+
+def _pm1_rows(rng, V, H):
+    """V distinct rows of +-1 (distinct with overwhelming probability; checked)."""
+    w = rng.choice([-1.0, 1.0], size=(V, H))
+    assert len({r.tobytes() for r in w}) == V
+    return w
+
+
+def test_lm_head_logits_brute_force():
+    """Tiny integer inputs: every logit equals the dot product summed term by
+    term in Python integers."""
+    rng = np.random.default_rng(21)
+    M, H, V = 3, 5, 7
+    h = rng.integers(-4, 5, size=(M, H))
+    w = rng.integers(-4, 5, size=(V, H))
+    got = O.lm_head_logits(h.astype(float), w.astype(float))
+    for m in range(M):
+        for v in range(V):
+            assert got[m, v] == sum(int(h[m, k]) * int(w[v, k]) for k in range(H))
+
+
+def test_lm_head_argmax_planted_by_cauchy_schwarz():
+    """hidden row m = weight row t_m with +-1 rows of equal norm: by
+    Cauchy-Schwarz the logit H at t_m is the unique maximum, so the argmax is
+    t_m.  Non-square shapes catch a transposed operand."""
+    rng = np.random.default_rng(22)
+    M, H, V = 6, 64, 300
+    w = _pm1_rows(rng, V, H)
+    t = rng.integers(0, V, size=M)
+    h = w[t] * 0.5                      # positive scaling keeps the argmax
+    assert np.array_equal(O.lm_head_argmax(h, w), t)
+    assert np.array_equal(O.lm_head_argmax(-h, -w), t)   # (-h)(-w) = hw
+
+
+def test_lm_head_argmax_duplicate_rows_tie_to_lowest_index():
+    rng = np.random.default_rng(23)
+    M, H, V = 4, 32, 50
+    w = _pm1_rows(rng, V, H)
+    t = np.array([10, 20, 30, 40])
+    h = w[t].copy()
+    w2 = w.copy()
+    w2[[3, 25, 31, 49]] = w[t]          # a copy of each winner: below, above, above, above
+    assert list(O.lm_head_argmax(h, w2)) == [3, 20, 30, 40]
+
+
+def test_lm_head_greedy_accept_from_planted_hidden_states():
+    """The AR view's hidden states planted so that the greedy tokens are known:
+    drafts that agree on exactly the first a positions give accept_len a and
+    the planted correction token."""
+    rng = np.random.default_rng(24)
+    B, K, H, V = 3, 8, 48, 120
+    w = _pm1_rows(rng, V, H)
+    t = rng.integers(0, V, size=(B, K))
+    h = w[t]
+    pre = [0, 5, 8]
+    drafts = t.copy()
+    for b in range(B):
+        if pre[b] < K:
+            drafts[b, pre[b]] = (t[b, pre[b]] + 1) % V
+    acc, nxt, g = O.lm_head_greedy_accept(h, w, drafts)
+    assert list(acc) == pre and np.array_equal(g, t)
+    assert list(nxt) == [t[0, 0], t[1, 5], t[2, 7]]
