@@ -50,6 +50,7 @@ def parse():
     p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a graph")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-sample", action="store_true", help="skip the sampled-consensus timing")
+    p.add_argument("--no-lm-head", action="store_true", help="skip the LM-head timing")
     p.add_argument("--no-long-context", action="store_true",
                    help="skip the 36-layer step at batch 4, 32768 cached tokens")
     p.add_argument("--copy-probe-mib", type=int, default=0,
@@ -210,6 +211,41 @@ def sample_accept_timing(torch, ob, I, use_graph, temperature=1.0):
             "temperature": temperature, "vocab": V, "block_k": K, **out}
 
 
+def lm_head_timing(torch, ob, I, use_graph):
+    """LM head with fused argmax (orthrus_lm_head_greedy_accept) over the
+    Qwen3-8B head: bf16 weight [151936, 4096] (1.24 GB, larger than the
+    256 MB Infinity Cache, so every call streams it from HBM) and the AR
+    view's hidden states [B, 32, 4096], at B = 1, 4 and 16.  Algorithmic
+    bytes per call: the weight once plus the hidden states; flops:
+    2 * B * 32 * 4096 * 151936."""
+    d = torch.device("cuda:0")
+    H, V, K = I.QWEN3_8B_HIDDEN, I.QWEN3_VOCAB, 32
+    _, w, _ = I.make_lm_head_inputs(1, H, V, seed=0, workload="qwen3_8b_8k", device=d)
+    out = {}
+    for bs in (1, 4, 16):
+        h, _, _ = I.make_lm_head_inputs(bs * K, H, 1, seed=bs, workload="qwen3_8b_8k", device=d)
+        h = h.view(bs, K, H)
+        drafts = torch.zeros((bs, K), dtype=torch.int32, device=d)
+        ws = torch.empty(ob.lib().orthrus_lm_head_workspace_bytes(bs * K, H, V), dtype=torch.uint8, device=d)
+        n = 4
+        fn = lambda: [ob.lm_head_greedy_accept(h, w, drafts, ws=ws) for _ in range(n)]
+        fn()
+        rep = capture(torch, fn) if use_graph else fn
+        ms = time_region(torch, rep, 5, 2) / n
+        nbytes = V * H * 2 + bs * K * H * 2
+        flops = 2.0 * bs * K * H * V
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[f"bs{bs}"] = {"us_per_call": round(ms * 1e3, 2), "bytes_per_call": nbytes, "gbs": round(gbs, 1),
+                          "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                          "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                          "frac_mfma_bf16": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+        del h, ws, rep
+    del w
+    torch.cuda.empty_cache()
+    return {"kernel": "orthrus_lm_head_greedy_accept (lm_head_tiles + lm_head_finish)", "hidden": H,
+            "vocab": V, "block_k": K, **out}
+
+
 def cpu_baseline(step, I, seconds):
     """The fp64 oracle, as is, on one layer of the step (both views, accept,
     append) at the same shapes; repeated for about `seconds`."""
@@ -339,6 +375,13 @@ def main():
         torch.cuda.empty_cache()
         sample = sample_accept_timing(torch, ob, I, use_graph)
 
+    lmhead = None
+    if not args.no_lm_head:
+        log("lm head")
+        step = None
+        torch.cuda.empty_cache()
+        lmhead = lm_head_timing(torch, ob, I, use_graph)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline")
@@ -355,7 +398,7 @@ def main():
                        "graph": use_graph, "parallelism": "none (1 GPU)"},
             "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
             "roofline": roof, "cpu_baseline": cpu, "sweep": sweep or None, "long_context_step": longctx,
-            "sample_accept": sample}
+            "sample_accept": sample, "lm_head": lmhead}
     print(json.dumps(line), flush=True)
 
 

@@ -1,0 +1,358 @@
+// Language-model head with a fused greedy argmax on gfx950: the projection
+// that turns each view's final hidden states into the tokens the consensus
+// step compares (Orthrus explainer, gist.science arXiv 2605.12825, technical
+// summary §2.3: the diffusion head's drafts and the frozen AR head's exact
+// targets both come out of the model's vocabulary projection).
+//
+//   logits[m, v] = sum_k hidden[m, k] * weight[v, k]   (bf16 in, fp32 accumulate)
+//   token[m]     = lowest v attaining max_v logits[m, v]
+//
+// The logits never reach memory.  At decode sizes (rows = B * K = 32 .. 128)
+// the weight [V, H] is read once per call and every byte of it feeds `rows`
+// multiply-adds, so the kernel is bound by the weight stream from HBM.
+//
+// lm_head_tiles: one work-group of 4 waves per (128-row vocabulary tile,
+// group of up to MT x 32 hidden rows).  Each wave streams its 32 weight rows
+// straight from HBM into MFMA A-operand registers (no reuse, so no LDS),
+// double-buffered by phase of KP hidden elements; lane (r, half) loads KP
+// contiguous bytes of row r, so a wave reads whole 2 * KP-byte row segments.
+// The hidden rows of the phase are staged once per work-group in LDS (XOR
+// chunk swizzle, conflict-free 16-byte reads) as the B operand.  Products run
+// on v_mfma_f32_32x32x16_bf16 with D[n][m] in the accumulators, so each lane
+// owns one hidden row m and 16 vocabulary rows: the tile's argmax is a
+// per-lane max, one exchange between the lane halves and one merge of the
+// four waves in LDS, stored as a 64-bit key (order-preserving value bits << 32
+// | ~index: a larger key is a larger value, then a lower index).  Blocks of
+// one tile (its row groups) are placed on one XCD so that, when the rows need
+// several groups, the later groups find the weight tile in that XCD's L2.
+//
+// lm_head_finish: one work-group per group of rows reduces each row's tile
+// keys (all loads of a lane issued before the reduction), writes the tokens
+// and, for the accept entry point, compares them with the drafts (wave
+// ballot: first mismatch) exactly as the greedy consensus does.
+#include "orthrus_device.h"
+#include "orthrus_host.h"
+
+namespace orthrus {
+
+constexpr int kLmWaves = 4;
+constexpr int kLmThreads = kLmWaves * kWave;
+constexpr int kLmTileN = kLmWaves * 32;  // vocabulary rows per tile
+constexpr int kLmFinWaves = 16;
+constexpr int kLmFinThreads = kLmFinWaves * kWave;
+
+struct LmArgs {
+  const bf16* h;               // [M, H]
+  const bf16* w;               // [V, H]
+  unsigned long long* part;    // [M, ntiles] tile keys
+  const int32_t* drafts;       // [M] (accept) or nullptr
+  int32_t* tokens;             // [M] or nullptr
+  float* maxv;                 // [M] or nullptr
+  int32_t* accept_len;         // [M / R]
+  int32_t* next_token;         // [M / R]
+  int M, H, V, ntiles, mgroups, R;
+};
+
+__device__ __forceinline__ uint32_t lm_order_bits(float v) {
+  if (v == 0.f) v = 0.f;  // -0.0 and +0.0 are equal: one encoding
+  const uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float lm_from_order_bits(uint32_t b) {
+  return __uint_as_float((b & 0x80000000u) ? (b & 0x7fffffffu) : ~b);
+}
+
+__device__ __forceinline__ void lm_keep(float& bv, int& bi, float v, int i) {
+  if (v > bv || (v == bv && i < bi)) {
+    bv = v;
+    bi = i;
+  }
+}
+
+template <int MT, int KP>
+__global__ void __launch_bounds__(kLmThreads) lm_head_tiles(LmArgs a) {
+  constexpr int CH = KP / 8;     // 16-byte chunks of one hidden row per phase
+  constexpr int NW = KP / 16;    // weight chunks per lane per phase = MFMA steps
+  constexpr int ROWS = MT * 32;  // hidden rows per work-group
+  constexpr int NA = ROWS * CH / kLmThreads;
+  static_assert(CH >= 16 && (ROWS * CH) % kLmThreads == 0, "phase shape");
+  __shared__ u32x4 hs[2][ROWS * CH];
+  __shared__ float rv[kLmWaves][32];
+  __shared__ int ri[kLmWaves][32];
+
+  // block -> (tile, row group): the row groups of one tile share an XCD
+  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+  const int tile = (local / a.mgroups) * 8 + xcd, mg = local % a.mgroups;
+  if (tile >= a.ntiles) return;  // uniform: padding of the tile count to 8
+
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int g = lane >> 5, c32 = lane & 31;
+  const int m0 = mg * ROWS;
+  const int nbase = tile * kLmTileN + wave * 32;
+  const int n = nbase + c32;
+  // rows past the vocabulary read row 0 (in bounds) and are dropped below
+  const bf16* wrow = a.w + (size_t)(n < a.V ? n : 0) * a.H + g * (KP / 2);
+  const int P = a.H / KP;
+
+  auto load_w = [&](int p, u32x4(&wv)[NW]) {
+    const bf16* src = wrow + (size_t)p * KP;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) wv[i] = ld16(src + 8 * i);
+  };
+  auto load_h = [&](int p, u32x4(&hv)[NA]) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int q = tid + kLmThreads * i, r = q / CH, c = q % CH;
+      const int m = min(m0 + r, a.M - 1);  // rows past M repeat the last row and are dropped
+      hv[i] = ld16(a.h + (size_t)m * a.H + (size_t)p * KP + 8 * c);
+    }
+  };
+  auto store_h = [&](int buf, const u32x4(&hv)[NA]) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int q = tid + kLmThreads * i, r = q / CH, c = q % CH;
+      hs[buf][r * CH + (c ^ (r & 15))] = hv[i];
+    }
+  };
+  // lane (c32, g) holds weight elements k0 + g KP/2 + 8 s + e of step s; the
+  // B operand of the same step is hidden row c32 at the same k: chunk g NW + s
+  auto compute = [&](int buf, const u32x4(&wv)[NW], f32x16(&acc)[MT]) {
+#pragma unroll
+    for (int s = 0; s < NW; ++s) {
+      const bf16x8 av = __builtin_bit_cast(bf16x8, wv[s]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int r = mt * 32 + c32, c = g * NW + s;
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, hs[buf][r * CH + (c ^ (r & 15))]);
+        acc[mt] = mfma_step(av, bv, acc[mt]);
+      }
+    }
+  };
+
+  f32x16 acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[mt][e] = 0.f;
+
+  u32x4 hv[NA], w0[NW], w1[NW];
+  load_h(0, hv);
+  load_w(0, w0);
+  store_h(0, hv);
+  __syncthreads();
+  for (int p = 0; p < P; p += 2) {
+    // phase p: weights w0, hidden buffer 0; the hidden rows of phase p + 1
+    // are loaded first so that their wait does not cover the weight loads
+    if (p + 1 < P) {
+      load_h(p + 1, hv);
+      load_w(p + 1, w1);
+    }
+    compute(0, w0, acc);
+    if (p + 1 < P) store_h(1, hv);
+    __syncthreads();
+    if (p + 1 >= P) break;
+    // phase p + 1: weights w1, hidden buffer 1
+    if (p + 2 < P) {
+      load_h(p + 2, hv);
+      load_w(p + 2, w0);
+    }
+    compute(1, w1, acc);
+    if (p + 2 < P) store_h(0, hv);
+    __syncthreads();
+  }
+
+  // argmax of the tile per hidden row.  Accumulator register e of lane
+  // (c32, g) holds vocabulary row nbase + 8 (e / 4) + 4 g + e % 4 and hidden
+  // row m0 + 32 mt + c32; the rows grow with e, so a strict compare keeps
+  // the lowest index.
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int nn = nbase + 8 * (e >> 2) + 4 * g + (e & 3);
+      if (nn < a.V && acc[mt][e] > bv) {
+        bv = acc[mt][e];
+        bi = nn;
+      }
+    }
+    lm_keep(bv, bi, __shfl_xor(bv, 32, kWave), __shfl_xor(bi, 32, kWave));
+    if (g == 0) {
+      rv[wave][c32] = bv;
+      ri[wave][c32] = bi;
+    }
+    __syncthreads();
+    if (wave == 0 && g == 0) {
+#pragma unroll
+      for (int w = 1; w < kLmWaves; ++w) lm_keep(bv, bi, rv[w][c32], ri[w][c32]);
+      const int m = m0 + mt * 32 + c32;
+      if (m < a.M)
+        a.part[(size_t)m * a.ntiles + tile] =
+            ((unsigned long long)lm_order_bits(bv) << 32) | (unsigned long long)(0xffffffffu - (uint32_t)bi);
+    }
+    __syncthreads();
+  }
+}
+
+__device__ __forceinline__ unsigned long long lm_max_u64(unsigned long long x, unsigned long long y) {
+  return x > y ? x : y;
+}
+
+__device__ __forceinline__ unsigned long long lm_wave_max_u64(unsigned long long k) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)k, off, kWave);
+    const uint32_t hi = __shfl_xor((uint32_t)(k >> 32), off, kWave);
+    k = lm_max_u64(k, ((unsigned long long)hi << 32) | lo);
+  }
+  return k;
+}
+
+// one work-group per group of R rows (one sequence's K rows for the accept
+// entry point); wave w reduces rows w and w + 16
+__global__ void __launch_bounds__(kLmFinThreads) lm_head_finish(LmArgs a) {
+  __shared__ int32_t gtok[32];
+  const int grp = blockIdx.x;
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  for (int i = wave; i < a.R; i += kLmFinWaves) {
+    const int m = grp * a.R + i;
+    if (m >= a.M) break;
+    const unsigned long long* keys = a.part + (size_t)m * a.ntiles;
+    unsigned long long k0 = 0, k1 = 0, k2 = 0, k3 = 0;
+    int q = lane;
+    for (; q + 3 * kWave < a.ntiles; q += 4 * kWave) {
+      const unsigned long long x0 = keys[q], x1 = keys[q + kWave], x2 = keys[q + 2 * kWave],
+                               x3 = keys[q + 3 * kWave];
+      k0 = lm_max_u64(k0, x0);
+      k1 = lm_max_u64(k1, x1);
+      k2 = lm_max_u64(k2, x2);
+      k3 = lm_max_u64(k3, x3);
+    }
+    for (; q < a.ntiles; q += kWave) k0 = lm_max_u64(k0, keys[q]);
+    const unsigned long long best = lm_wave_max_u64(lm_max_u64(lm_max_u64(k0, k1), lm_max_u64(k2, k3)));
+    const int32_t tok = (int32_t)(0xffffffffu - (uint32_t)(best & 0xffffffffu));
+    if (lane == 0) {
+      gtok[i] = tok;
+      if (a.tokens) a.tokens[m] = tok;
+      if (a.maxv) a.maxv[m] = lm_from_order_bits((uint32_t)(best >> 32));
+    }
+  }
+  if (!a.drafts) return;
+  __syncthreads();
+  if (wave != 0) return;
+  const int K = a.R, b = grp;
+  bool miss = false;
+  int32_t gt = 0;
+  if (lane < K) {
+    gt = gtok[lane];
+    miss = a.drafts[b * K + lane] != gt;
+  }
+  const unsigned long long mask = __ballot(miss);
+  const int acc = mask ? (__ffsll((long long)mask) - 1) : K;
+  const int last = acc < K ? acc : K - 1;
+  const int nxt = __shfl(gt, last, kWave);
+  if (lane == 0) {
+    a.accept_len[b] = acc;
+    a.next_token[b] = nxt;
+  }
+}
+
+static bool lm_shape_ok(long rows, int hidden, int vocab) {
+  if (rows < 1 || vocab < 1 || hidden < 256 || hidden > 65536 || hidden % 256 != 0) return false;
+  const long ntiles = (vocab + (long)kLmTileN - 1) / kLmTileN;
+  const long tiles8 = (ntiles + 7) / 8 * 8;
+  const long mgroups = (rows + 127) / 128;  // the smallest row-group size used is 32 (MT = 1) for rows <= 32
+  return tiles8 * mgroups * 4 <= 0x7fffffffL && rows <= (1L << 24);
+}
+
+static size_t lm_workspace(long rows, int vocab) {
+  const long ntiles = (vocab + (long)kLmTileN - 1) / kLmTileN;
+  return (size_t)rows * ntiles * sizeof(unsigned long long);
+}
+
+template <int MT, int KP>
+static orthrus_status lm_launch_tiles(const LmArgs& a, hipStream_t s) {
+  const long tiles8 = ((long)a.ntiles + 7) / 8 * 8;
+  hipLaunchKernelGGL((lm_head_tiles<MT, KP>), dim3((unsigned)(tiles8 * a.mgroups)), dim3(kLmThreads), 0, s, a);
+  return hipGetLastError() == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_LAUNCH;
+}
+
+static orthrus_status lm_run(LmArgs a, hipStream_t s, int finish_groups) {
+  a.ntiles = (a.V + kLmTileN - 1) / kLmTileN;
+  orthrus_status st;
+  if (a.M <= 32) {
+    a.mgroups = 1;
+    st = lm_launch_tiles<1, 256>(a, s);
+  } else if (a.M <= 64) {
+    a.mgroups = 1;
+    st = lm_launch_tiles<2, 256>(a, s);
+  } else {
+    a.mgroups = (a.M + 127) / 128;
+    st = lm_launch_tiles<4, 128>(a, s);
+  }
+  if (st != ORTHRUS_OK) return st;
+  hipLaunchKernelGGL(lm_head_finish, dim3((unsigned)finish_groups), dim3(kLmFinThreads), 0, s, a);
+  return hipGetLastError() == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_LAUNCH;
+}
+
+static bool lm_aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+}  // namespace orthrus
+
+using namespace orthrus;
+
+extern "C" size_t orthrus_lm_head_workspace_bytes(int32_t rows, int32_t hidden_size, int32_t vocab) {
+  if (!lm_shape_ok(rows, hidden_size, vocab)) return 0;
+  return lm_workspace(rows, vocab);
+}
+
+extern "C" orthrus_status orthrus_lm_head_argmax(const void* hidden, const void* weight, int32_t* tokens,
+                                                 float* max_logits, int32_t rows, int32_t hidden_size,
+                                                 int32_t vocab, void* workspace, size_t workspace_bytes,
+                                                 void* stream) {
+  if (!hidden || !weight || !tokens) return ORTHRUS_ERR_NULL;
+  if (!lm_shape_ok(rows, hidden_size, vocab)) return ORTHRUS_ERR_SHAPE;
+  if (!lm_aligned(hidden) || !lm_aligned(weight)) return ORTHRUS_ERR_SHAPE;
+  if (!workspace || workspace_bytes < lm_workspace(rows, vocab) || (reinterpret_cast<uintptr_t>(workspace) & 7))
+    return ORTHRUS_ERR_WORKSPACE;
+  LmArgs a = {};
+  a.h = (const bf16*)hidden;
+  a.w = (const bf16*)weight;
+  a.part = (unsigned long long*)workspace;
+  a.tokens = tokens;
+  a.maxv = max_logits;
+  a.M = rows;
+  a.H = hidden_size;
+  a.V = vocab;
+  a.R = 32;
+  return lm_run(a, (hipStream_t)stream, (rows + 31) / 32);
+}
+
+extern "C" orthrus_status orthrus_lm_head_greedy_accept(const void* hidden, const void* weight,
+                                                        const int32_t* draft_tokens, int32_t* accept_len,
+                                                        int32_t* next_token, int32_t* ar_tokens, int32_t batch,
+                                                        int32_t block_k, int32_t hidden_size, int32_t vocab,
+                                                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (!hidden || !weight || !draft_tokens || !accept_len || !next_token) return ORTHRUS_ERR_NULL;
+  if (batch < 1 || block_k < 1 || block_k > 32) return ORTHRUS_ERR_SHAPE;
+  const long rows = (long)batch * block_k;
+  if (!lm_shape_ok(rows, hidden_size, vocab)) return ORTHRUS_ERR_SHAPE;
+  if (!lm_aligned(hidden) || !lm_aligned(weight)) return ORTHRUS_ERR_SHAPE;
+  if (!workspace || workspace_bytes < lm_workspace(rows, vocab) || (reinterpret_cast<uintptr_t>(workspace) & 7))
+    return ORTHRUS_ERR_WORKSPACE;
+  LmArgs a = {};
+  a.h = (const bf16*)hidden;
+  a.w = (const bf16*)weight;
+  a.part = (unsigned long long*)workspace;
+  a.drafts = draft_tokens;
+  a.tokens = ar_tokens;
+  a.accept_len = accept_len;
+  a.next_token = next_token;
+  a.M = (int)rows;
+  a.H = hidden_size;
+  a.V = vocab;
+  a.R = block_k;
+  return lm_run(a, (hipStream_t)stream, batch);
+}

@@ -54,7 +54,7 @@ WORKLOADS = {
 
 _TENSOR_IDS = {"ctx": 1, "pages": 2, "q": 3, "k_cache": 4, "v_cache": 5, "k_blk": 6, "v_blk": 7,
                "logits": 8, "targets": 9, "prefix": 10, "drafts": 11, "draft_logits": 12, "gumbel": 13,
-               "u_accept": 14, "u_resample": 15}
+               "u_accept": 14, "u_resample": 15, "lm_hidden": 16, "lm_weight": 17, "lm_targets": 18}
 
 
 def _seed(seed, workload, layer, tensor):
@@ -235,3 +235,33 @@ def make_sample_inputs(batch, block_k, vocab, temperature, seed=0, workload="", 
     ur = torch.rand((batch,), generator=_gen(device, _seed(seed, workload, 0, "u_resample")),
                     device=device, dtype=torch.float32)
     return ar, dr, drafts, ua, ur
+
+
+QWEN3_8B_HIDDEN = 4096
+
+
+def make_lm_head_inputs(rows, hidden, vocab, seed=0, workload="", planted=False, device="cpu"):
+    """Final hidden states [rows, hidden] and an LM-head weight [vocab, hidden],
+    both bf16.
+
+    Default: hidden ~ N(0, 1), weight ~ N(0, (3 / sqrt(hidden))^2), so logits
+    have a standard deviation of about 3.  With `planted`, weight rows are
+    random +-1 and hidden row m is a copy of weight row targets[m] (drawn
+    uniformly): every logit is an integer of magnitude <= hidden (exact in
+    fp32 and bf16 products) and, the rows being distinct, targets[m] is the
+    unique maximum by Cauchy-Schwarz.  Returns (hidden, weight, targets or
+    None); targets is int32 [rows].
+    """
+    gen = _gen(device, _seed(seed, workload, 0, "lm_weight"))
+    if not planted:
+        w = torch.randn((vocab, hidden), generator=gen, device=device, dtype=torch.float32)
+        w = w.mul_(3.0 / math.sqrt(hidden)).to(torch.bfloat16)
+        h = torch.randn((rows, hidden), generator=_gen(device, _seed(seed, workload, 0, "lm_hidden")),
+                        device=device, dtype=torch.float32).to(torch.bfloat16)
+        return h, w, None
+    bits = torch.randint(0, 2, (vocab, hidden), generator=gen, device=device, dtype=torch.int8)
+    w = (bits.to(torch.bfloat16) * 2 - 1).to(torch.bfloat16)
+    t = torch.randint(0, vocab, (rows,), generator=_gen(device, _seed(seed, workload, 0, "lm_targets")),
+                      device=device, dtype=torch.int64)
+    h = w[t].clone()
+    return h, w, t.to(torch.int32)

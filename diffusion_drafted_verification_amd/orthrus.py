@@ -47,6 +47,9 @@ SIGNATURES = {
     "orthrus_greedy_accept": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
     "orthrus_sample_accept_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "orthrus_sample_accept": (_i32, [_vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
+    "orthrus_lm_head_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "orthrus_lm_head_argmax": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
+    "orthrus_lm_head_greedy_accept": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp]),
     "orthrus_kv_append": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _DESC_P, _vp]),
     "orthrus_kv_append_layers": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _DESC_P, _vp]),
     "orthrus_copy_probe": (_i32, [_vp, _vp, _sz, _vp]),
@@ -219,6 +222,53 @@ def sample_accept(ar_logits, draft_logits, draft_tokens, u_accept, u_resample, t
                                      _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "orthrus_sample_accept")
     return acc, nxt
+
+
+def _lm_check(hidden, weight):
+    if hidden.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
+        raise OrthrusError("hidden and weight must be bf16")
+    if weight.dim() != 2 or hidden.shape[-1] != weight.shape[1]:
+        raise OrthrusError("weight must be [V, H] with H = hidden.shape[-1]")
+
+
+def lm_head_argmax(hidden, weight, *, want_max=False, ws=None, stream=None):
+    """orthrus_lm_head_argmax over hidden [..., H]: returns (tokens [...]
+    int32, max_logits [...] fp32 or None)."""
+    dev = _gpu(hidden, weight)
+    _lm_check(hidden, weight)
+    H, V = weight.shape[1], weight.shape[0]
+    rows = hidden.numel() // H
+    tok = torch.empty(hidden.shape[:-1], dtype=torch.int32, device=dev)
+    mx = torch.empty(hidden.shape[:-1], dtype=torch.float32, device=dev) if want_max else None
+    need = lib().orthrus_lm_head_workspace_bytes(rows, H, V)
+    if ws is None:
+        ws = workspace(dev, need, "lm_head")
+    st = lib().orthrus_lm_head_argmax(_ptr(hidden), _ptr(weight), _ptr(tok), _ptr(mx), rows, H, V, _ptr(ws),
+                                      ws.numel(), _stream(stream))
+    _check(st, "orthrus_lm_head_argmax")
+    return tok, mx
+
+
+def lm_head_greedy_accept(hidden, weight, draft_tokens, *, want_ar_tokens=True, ws=None, stream=None):
+    """orthrus_lm_head_greedy_accept over the AR view's hidden states
+    [B, K, H]: returns (accept_len [B], next_token [B], ar_tokens [B, K] or
+    None)."""
+    dev = _gpu(hidden, weight, draft_tokens)
+    _lm_check(hidden, weight)
+    if hidden.dim() != 3 or draft_tokens.dtype != torch.int32 or tuple(draft_tokens.shape) != hidden.shape[:2]:
+        raise OrthrusError("hidden must be [B, K, H] and draft_tokens int32 [B, K]")
+    B, K, H = hidden.shape
+    V = weight.shape[0]
+    acc = torch.empty(B, dtype=torch.int32, device=dev)
+    nxt = torch.empty(B, dtype=torch.int32, device=dev)
+    g = torch.empty((B, K), dtype=torch.int32, device=dev) if want_ar_tokens else None
+    need = lib().orthrus_lm_head_workspace_bytes(B * K, H, V)
+    if ws is None:
+        ws = workspace(dev, need, "lm_head")
+    st = lib().orthrus_lm_head_greedy_accept(_ptr(hidden), _ptr(weight), _ptr(draft_tokens), _ptr(acc), _ptr(nxt),
+                                             _ptr(g), B, K, H, V, _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "orthrus_lm_head_greedy_accept")
+    return acc, nxt, g
 
 
 def kv_append(k_cache, v_cache, k_blk, v_blk, page_table, ctx_lens, accept_len, *, new_ctx_lens=None,

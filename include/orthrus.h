@@ -2,7 +2,7 @@
  * orthrus.h -- C ABI of the MI355X (gfx950) hot path of one Orthrus
  * dual-view decode step: block attention over a shared paged KV cache,
  * greedy consensus (argmax + longest-prefix accept), its sampling form at
- * temperature T > 0, and KV append.
+ * temperature T > 0, the LM head with a fused argmax, and KV append.
  *
  * Semantics follow the Orthrus explainer page for "Orthrus: Memory-Efficient
  * Parallel Token Generation via Dual-View Diffusion" (gist.science, arXiv
@@ -35,6 +35,7 @@
  *   ar_logits, draft_logits [B, K, V]        fp32
  *   draft_tokens    [B, K]                   int32
  *   u_accept [B, K], u_resample [B]          fp32
+ *   hidden [rows, H], weight [V, H]          bf16 (LM head)
  *   accept_len, next_token, new_ctx_lens [B] int32
  *   ar_tokens, slots[B, K]                   int32
  * Logical position p of sequence b lives in page page_table[b][p / P], slot
@@ -176,6 +177,37 @@ orthrus_status orthrus_sample_accept(const float* ar_logits, const float* draft_
                                      const float* u_resample, float temperature, int32_t* accept_len,
                                      int32_t* next_token, int32_t batch, int32_t block_k, int32_t vocab,
                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of the workspace the LM-head calls need for `rows` hidden rows: one
+ * 8-byte key per (row, 128-entry vocabulary tile).  0 for an invalid shape.
+ * The workspace needs no initialisation. */
+size_t orthrus_lm_head_workspace_bytes(int32_t rows, int32_t hidden_size, int32_t vocab);
+
+/* Greedy tokens straight from final hidden states: the vocabulary projection
+ * of each view (explainer §2.3: the drafts and the AR targets are the two
+ * heads' predictions over the vocabulary) with its argmax fused, so the
+ * logits are never stored.
+ *   logits[m, v] = sum_k hidden[m, k] * weight[v, k]  (bf16 operands, fp32
+ *                  accumulation; no bias or scaling)
+ *   tokens[m]    = lowest v attaining the maximum (-0.0 ties with +0.0;
+ *                  inputs must not produce NaN)
+ *   max_logits[m]= that maximum (optional, may be NULL)
+ * hidden [rows, H] bf16, weight [V, H] bf16 (row-major, 16-byte aligned).
+ * H a multiple of 256 in [256, 65536]; 1 <= rows <= 2^24; V >= 1. */
+orthrus_status orthrus_lm_head_argmax(const void* hidden, const void* weight, int32_t* tokens,
+                                      float* max_logits, int32_t rows, int32_t hidden_size, int32_t vocab,
+                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Greedy consensus straight from the AR view's final hidden states [B, K, H]:
+ * the tokens g of orthrus_lm_head_argmax over its B*K rows, then
+ * accept_len / next_token / ar_tokens exactly as orthrus_greedy_accept
+ * defines them from g.  The workspace is that of
+ * orthrus_lm_head_workspace_bytes(B * K, H, V).  1 <= K <= 32. */
+orthrus_status orthrus_lm_head_greedy_accept(const void* hidden, const void* weight,
+                                             const int32_t* draft_tokens, int32_t* accept_len,
+                                             int32_t* next_token, int32_t* ar_tokens, int32_t batch,
+                                             int32_t block_k, int32_t hidden_size, int32_t vocab,
+                                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* Commit the accepted block rows to the shared cache (explainer §2.3: the
  * cache keeps only the committed positions).

@@ -24,7 +24,7 @@ def declared_entry_points():
 
 def test_exports_every_declared_symbol():
     names = declared_entry_points()
-    assert len(names) == 12
+    assert len(names) == 15
     assert set(names) == set(B.SIGNATURES)
     lib = B.lib()
     for n in names:
@@ -148,6 +148,30 @@ def test_sample_accept_validation():
     assert call(wsb=need - 1) == 4
     assert call(ws=None, wsb=need) == 4
     assert call(ws=ctypes.c_void_p(4096 + 8), wsb=need) == 4   # 16-byte alignment
+
+
+def test_lm_head_validation():
+    lib = B.lib()
+    A16 = ctypes.c_void_p(4096 * 16)
+    ok = dict(h=A16, w=A16, tok=FAKE, rows=32, H=4096, V=151936, ws=FAKE, wsb=1 << 30)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return lib.orthrus_lm_head_argmax(a["h"], a["w"], a["tok"], None, a["rows"], a["H"], a["V"], a["ws"],
+                                          a["wsb"], None)
+
+    assert call(h=None) == 1 and call(w=None) == 1 and call(tok=None) == 1
+    assert call(H=4000) == 2 and call(H=0) == 2 and call(H=128) == 2 and call(rows=0) == 2 and call(V=0) == 2
+    assert call(h=ctypes.c_void_p(4096 * 16 + 8)) == 2          # 16-byte alignment
+    # one 8-byte key per (row, 128-entry vocabulary tile)
+    need = lib.orthrus_lm_head_workspace_bytes(32, 4096, 151936)
+    assert need == 32 * 1187 * 8
+    assert lib.orthrus_lm_head_workspace_bytes(32, 4000, 151936) == 0
+    assert call(wsb=need - 1) == 4 and call(ws=None) == 4
+    acc = lib.orthrus_lm_head_greedy_accept
+    assert acc(A16, A16, None, FAKE, FAKE, None, 1, 32, 4096, 151936, FAKE, need, None) == 1
+    assert acc(A16, A16, FAKE, FAKE, FAKE, None, 1, 33, 4096, 151936, FAKE, need, None) == 2
+    assert acc(A16, A16, FAKE, FAKE, FAKE, None, 2, 32, 4096, 151936, FAKE, need, None) == 4   # needs 64 rows
 
 
 def test_binding_refuses_cpu_tensors():

@@ -1,0 +1,171 @@
+"""Parity of the LM head with fused argmax (and the greedy accept fed by it)
+through the C ABI with the fp64 CPU oracle.
+
+Tokens are integers, so the bar is equality.  Two kinds of input:
+
+* planted: weight rows +-1 and each hidden row a copy of its target row, so
+  every logit is an integer of magnitude <= H (exact in fp32 whatever the
+  summation order) and the target is the unique maximum (Cauchy-Schwarz).
+  Tokens must equal the targets bit-exactly at every size, including the
+  Qwen3-8B head (H 4096, V 151936); duplicated winner rows test the
+  lowest-index tie rule exactly;
+* random (N(0, 1) hidden, N(0, 9/H) weights): the kernel accumulates in
+  fp32, the oracle in fp64.  A row whose fp64 gap between the two largest
+  logits is within the accumulation bound 1e-5 * max_v sum_k |h_k w_vk| may
+  resolve either way; such rows are checked to pick a logit within that bound
+  of the maximum, and at most one per case may be excused.  max_logits is
+  within the bound of the fp64 maximum.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from diffusion_drafted_verification_amd import inputs as I
+from oracle import orthrus_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+REL = 1e-5
+
+
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def ob():
+    from diffusion_drafted_verification_amd import orthrus
+    return orthrus
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def oracle_logits(h, w, vslice=16384):
+    """fp64 logits of the oracle, called on slices of the vocabulary (each
+    logit is still one whole dot product) to bound host memory."""
+    return np.concatenate([O.lm_head_logits(h, w[v0:v0 + vslice]) for v0 in range(0, w.shape[0], vslice)], axis=-1)
+
+
+def abs_bound(h, w, vslice=16384):
+    ha = np.abs(O._f64(h))
+    return REL * np.max(np.concatenate([ha @ np.abs(O._f64(w[v0:v0 + vslice])).T
+                                        for v0 in range(0, w.shape[0], vslice)], axis=-1), axis=-1)
+
+
+def check_random(rows, H, V, seed):
+    d = dev()
+    h, w, _ = I.make_lm_head_inputs(rows, H, V, seed=seed)
+    tok, mx = ob().lm_head_argmax(h.to(d), w.to(d), want_max=True)
+    torch.cuda.synchronize()
+    tok, mx = tok.cpu().numpy(), mx.cpu().numpy().astype(np.float64)
+    lg = oracle_logits(h, w)
+    ref = O.greedy_argmax(lg)
+    eb = abs_bound(h, w)
+    top = lg.max(axis=-1)
+    assert np.all(np.abs(mx - top) <= eb), (np.abs(mx - top).max(), eb.min())
+    bad = np.flatnonzero(tok != ref)
+    for m in bad:
+        assert 0 <= tok[m] < V
+        assert lg[m, tok[m]] >= top[m] - 2 * eb[m], (m, tok[m], ref[m], lg[m, tok[m]], top[m])
+    assert len(bad) <= 1, bad
+    return tok
+
+
+@pytest.mark.parametrize("rows,H,V", [(1, 256, 1000), (7, 512, 5003), (32, 1024, 20000), (33, 256, 777),
+                                      (64, 2048, 10007), (100, 512, 3001), (130, 256, 4099), (257, 512, 2000)])
+def test_lm_head_random_vs_oracle(rows, H, V):
+    """Row counts 1..257 cover one 32-row group, 64-row groups and several
+    128-row groups with ragged tails; vocabularies from 777 to 20000 cover
+    ragged 128-row tiles."""
+    say("lm_head random", rows, H, V)
+    check_random(rows, H, V, seed=rows + V)
+
+
+def test_lm_head_qwen3_8b_random():
+    say("lm_head qwen3-8b random")
+    check_random(32, I.QWEN3_8B_HIDDEN, I.QWEN3_VOCAB, seed=1)
+
+
+@pytest.mark.parametrize("rows", [1, 32, 64, 96, 512])
+def test_lm_head_planted_qwen3_8b(rows):
+    """Planted targets at the Qwen3-8B head, bit-exact; the maximum is H."""
+    say("lm_head planted", rows)
+    d = dev()
+    h, w, t = I.make_lm_head_inputs(rows, I.QWEN3_8B_HIDDEN, I.QWEN3_VOCAB, seed=rows, planted=True, device=d)
+    tok, mx = ob().lm_head_argmax(h, w, want_max=True)
+    torch.cuda.synchronize()
+    assert torch.equal(tok, t)
+    assert torch.all(mx == float(I.QWEN3_8B_HIDDEN))
+
+
+def test_lm_head_planted_ties_resolve_to_lowest_index():
+    """A copy of the winner row placed before it (in another tile, in the
+    same 128-row tile, in the same 32-row wave slice, in the other lane half
+    of the same accumulator) or after it: the token is the lower index of the
+    pair, exactly, and the maximum is H."""
+    say("lm_head ties")
+    d = dev()
+    H, V = 1024, 10000
+    _, w, _ = I.make_lm_head_inputs(1, H, V, seed=5, planted=True, device=d)
+    cases = [(5000, 17), (5000, 4990), (5000, 4997), (5000, 4996), (5000, 6000), (9999, 9998), (130, 129),
+             (0, 9999)]
+    for winner, copy in cases:
+        wi = w.clone()
+        wi[copy] = w[winner]
+        h = w[winner:winner + 1].clone()
+        tok, mx = ob().lm_head_argmax(h, wi, want_max=True)
+        torch.cuda.synchronize()
+        assert tok.item() == min(winner, copy) and mx.item() == float(H), (winner, copy, tok.item())
+
+
+def test_lm_head_greedy_accept_planted():
+    """The AR view's hidden states planted at known greedy tokens; drafts
+    agree on a geometric prefix: accept_len, next_token and ar_tokens equal
+    the planted values and the oracle's."""
+    say("lm_head accept planted")
+    d = dev()
+    B, K, H, V = 4, 32, 2048, 30011
+    h, w, t = I.make_lm_head_inputs(B * K, H, V, seed=9, planted=True, device=d)
+    t = t.view(B, K).cpu()
+    pre = np.array([0, 11, 32, 5])
+    drafts = I.make_drafts(t, pre, V, seed=9).to(d)
+    acc, nxt, g = ob().lm_head_greedy_accept(h.view(B, K, H), w, drafts)
+    torch.cuda.synchronize()
+    assert torch.equal(g.cpu(), t) and acc.cpu().tolist() == pre.tolist()
+    ra, rn, rg = O.lm_head_greedy_accept(h.view(B, K, H).cpu(), w.cpu(), drafts.cpu())
+    assert np.array_equal(acc.cpu().numpy(), ra) and np.array_equal(nxt.cpu().numpy(), rn)
+    assert np.array_equal(g.cpu().numpy(), rg)
+
+
+def test_lm_head_greedy_accept_matches_argmax_then_accept():
+    """At the Qwen3-8B head with random inputs, the fused accept equals
+    orthrus_lm_head_argmax followed by the same prefix rule (on the GPU's own
+    tokens: the fused path must take identical decisions)."""
+    say("lm_head accept random")
+    d = dev()
+    B, K = 2, 32
+    h, w, _ = I.make_lm_head_inputs(B * K, I.QWEN3_8B_HIDDEN, I.QWEN3_VOCAB, seed=3, device=d)
+    tok, _ = ob().lm_head_argmax(h, w)
+    g0 = tok.view(B, K).cpu()
+    drafts = I.make_drafts(g0, np.array([7, 32]), I.QWEN3_VOCAB, seed=3).to(d)
+    acc, nxt, g = ob().lm_head_greedy_accept(h.view(B, K, -1), w, drafts)
+    torch.cuda.synchronize()
+    assert torch.equal(g.cpu(), g0) and acc.cpu().tolist() == [7, 32]
+    assert nxt.cpu().tolist() == [g0[0, 7].item(), g0[1, 31].item()]
+
+
+def test_lm_head_workspace_reuse_and_determinism():
+    say("lm_head workspace reuse")
+    d = dev()
+    ws = torch.full((ob().lib().orthrus_lm_head_workspace_bytes(130, 512, 20000),), 0x5A, dtype=torch.uint8,
+                    device=d)
+    for rows, H, V, s in [(130, 512, 20000, 1), (3, 256, 900, 2), (64, 1024, 20000, 3)]:
+        h, w, _ = I.make_lm_head_inputs(rows, H, V, seed=s, device=d)
+        a, am = ob().lm_head_argmax(h, w, want_max=True, ws=ws)
+        b, bm = ob().lm_head_argmax(h, w, want_max=True)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b) and torch.equal(am, bm)
