@@ -213,7 +213,7 @@ def sample_accept_timing(torch, ob, I, use_graph, temperature=1.0):
 
 def lm_head_timing(torch, ob, I, use_graph):
     """LM head with fused argmax (orthrus_lm_head_greedy_accept) over the
-    Qwen3-8B head: bf16 weight [151936, 4096] (1.24 GB, larger than the
+    Qwen3-8B head: bf16 weight [151936, 4096], packed once (1.24 GB, larger than the
     256 MB Infinity Cache, so every call streams it from HBM) and the AR
     view's hidden states [B, 32, 4096], at B = 1, 4 and 16.  Algorithmic
     bytes per call: the weight once plus the hidden states; flops:
@@ -221,6 +221,8 @@ def lm_head_timing(torch, ob, I, use_graph):
     d = torch.device("cuda:0")
     H, V, K = I.QWEN3_8B_HIDDEN, I.QWEN3_VOCAB, 32
     _, w, _ = I.make_lm_head_inputs(1, H, V, seed=0, workload="qwen3_8b_8k", device=d)
+    head = ob.PackedLmHead(w)   # packed once, as at model load
+    del w
     out = {}
     for bs in (1, 4, 16):
         h, _, _ = I.make_lm_head_inputs(bs * K, H, 1, seed=bs, workload="qwen3_8b_8k", device=d)
@@ -228,7 +230,7 @@ def lm_head_timing(torch, ob, I, use_graph):
         drafts = torch.zeros((bs, K), dtype=torch.int32, device=d)
         ws = torch.empty(ob.lib().orthrus_lm_head_workspace_bytes(bs * K, H, V), dtype=torch.uint8, device=d)
         n = 4
-        fn = lambda: [ob.lm_head_greedy_accept(h, w, drafts, ws=ws) for _ in range(n)]
+        fn = lambda: [ob.lm_head_greedy_accept(h, head, drafts, ws=ws) for _ in range(n)]
         fn()
         rep = capture(torch, fn) if use_graph else fn
         ms = time_region(torch, rep, 5, 2) / n
@@ -240,7 +242,7 @@ def lm_head_timing(torch, ob, I, use_graph):
                           "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
                           "frac_mfma_bf16": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
         del h, ws, rep
-    del w
+    del head
     torch.cuda.empty_cache()
     return {"kernel": "orthrus_lm_head_greedy_accept (lm_head_tiles + lm_head_finish)", "hidden": H,
             "vocab": V, "block_k": K, **out}

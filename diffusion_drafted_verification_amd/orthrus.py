@@ -47,6 +47,8 @@ SIGNATURES = {
     "orthrus_greedy_accept": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
     "orthrus_sample_accept_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "orthrus_sample_accept": (_i32, [_vp, _vp, _vp, _vp, _vp, _f32, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
+    "orthrus_lm_head_packed_bytes": (_sz, [_i32, _i32]),
+    "orthrus_lm_head_pack_weight": (_i32, [_vp, _vp, _i32, _i32, _vp]),
     "orthrus_lm_head_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "orthrus_lm_head_argmax": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
     "orthrus_lm_head_greedy_accept": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp]),
@@ -224,19 +226,38 @@ def sample_accept(ar_logits, draft_logits, draft_tokens, u_accept, u_resample, t
     return acc, nxt
 
 
-def _lm_check(hidden, weight):
-    if hidden.dtype != torch.bfloat16 or weight.dtype != torch.bfloat16:
-        raise OrthrusError("hidden and weight must be bf16")
-    if weight.dim() != 2 or hidden.shape[-1] != weight.shape[1]:
-        raise OrthrusError("weight must be [V, H] with H = hidden.shape[-1]")
+class PackedLmHead:
+    """An LM-head weight [V, H] bf16 repacked once (orthrus_lm_head_pack_weight)
+    into the layout the LM-head calls stream."""
+
+    def __init__(self, weight, stream=None):
+        dev = _gpu(weight)
+        if weight.dtype != torch.bfloat16 or weight.dim() != 2:
+            raise OrthrusError("weight must be bf16 [V, H]")
+        self.vocab, self.hidden = int(weight.shape[0]), int(weight.shape[1])
+        nbytes = lib().orthrus_lm_head_packed_bytes(self.hidden, self.vocab)
+        if nbytes == 0:
+            raise OrthrusError("unsupported LM-head shape (H must be a multiple of 256 in [256, 65536])")
+        self.packed = torch.empty(nbytes // 2, dtype=torch.bfloat16, device=dev)
+        st = lib().orthrus_lm_head_pack_weight(_ptr(weight), _ptr(self.packed), self.hidden, self.vocab,
+                                               _stream(stream))
+        _check(st, "orthrus_lm_head_pack_weight")
 
 
-def lm_head_argmax(hidden, weight, *, want_max=False, ws=None, stream=None):
-    """orthrus_lm_head_argmax over hidden [..., H]: returns (tokens [...]
-    int32, max_logits [...] fp32 or None)."""
-    dev = _gpu(hidden, weight)
-    _lm_check(hidden, weight)
-    H, V = weight.shape[1], weight.shape[0]
+def _lm_check(hidden, head):
+    if not isinstance(head, PackedLmHead):
+        raise OrthrusError("the LM-head calls take a PackedLmHead")
+    if hidden.dtype != torch.bfloat16 or hidden.shape[-1] != head.hidden:
+        raise OrthrusError("hidden must be bf16 [..., H] with the head's H")
+
+
+def lm_head_argmax(hidden, head, *, want_max=False, ws=None, stream=None):
+    """orthrus_lm_head_argmax over hidden [..., H] with a PackedLmHead:
+    returns (tokens [...] int32, max_logits [...] fp32 or None)."""
+    dev = _gpu(hidden, head.packed)
+    _lm_check(hidden, head)
+    H, V = head.hidden, head.vocab
+    weight = head.packed
     rows = hidden.numel() // H
     tok = torch.empty(hidden.shape[:-1], dtype=torch.int32, device=dev)
     mx = torch.empty(hidden.shape[:-1], dtype=torch.float32, device=dev) if want_max else None
@@ -249,16 +270,17 @@ def lm_head_argmax(hidden, weight, *, want_max=False, ws=None, stream=None):
     return tok, mx
 
 
-def lm_head_greedy_accept(hidden, weight, draft_tokens, *, want_ar_tokens=True, ws=None, stream=None):
+def lm_head_greedy_accept(hidden, head, draft_tokens, *, want_ar_tokens=True, ws=None, stream=None):
     """orthrus_lm_head_greedy_accept over the AR view's hidden states
-    [B, K, H]: returns (accept_len [B], next_token [B], ar_tokens [B, K] or
-    None)."""
-    dev = _gpu(hidden, weight, draft_tokens)
-    _lm_check(hidden, weight)
+    [B, K, H] with a PackedLmHead: returns (accept_len [B], next_token [B],
+    ar_tokens [B, K] or None)."""
+    dev = _gpu(hidden, head.packed, draft_tokens)
+    _lm_check(hidden, head)
     if hidden.dim() != 3 or draft_tokens.dtype != torch.int32 or tuple(draft_tokens.shape) != hidden.shape[:2]:
         raise OrthrusError("hidden must be [B, K, H] and draft_tokens int32 [B, K]")
     B, K, H = hidden.shape
-    V = weight.shape[0]
+    V = head.vocab
+    weight = head.packed
     acc = torch.empty(B, dtype=torch.int32, device=dev)
     nxt = torch.empty(B, dtype=torch.int32, device=dev)
     g = torch.empty((B, K), dtype=torch.int32, device=dev) if want_ar_tokens else None

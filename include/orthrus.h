@@ -35,7 +35,8 @@
  *   ar_logits, draft_logits [B, K, V]        fp32
  *   draft_tokens    [B, K]                   int32
  *   u_accept [B, K], u_resample [B]          fp32
- *   hidden [rows, H], weight [V, H]          bf16 (LM head)
+ *   hidden [rows, H], weight [V, H]          bf16 (LM head; the calls take the
+ *                                            weight packed once)
  *   accept_len, next_token, new_ctx_lens [B] int32
  *   ar_tokens, slots[B, K]                   int32
  * Logical position p of sequence b lives in page page_table[b][p / P], slot
@@ -178,6 +179,21 @@ orthrus_status orthrus_sample_accept(const float* ar_logits, const float* draft_
                                      int32_t* next_token, int32_t batch, int32_t block_k, int32_t vocab,
                                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of the packed LM-head weight: ceil(V / 32) * 32 * H * 2.  0 for an
+ * invalid shape (H a multiple of 256 in [256, 65536], V >= 1). */
+size_t orthrus_lm_head_packed_bytes(int32_t hidden_size, int32_t vocab);
+
+/* Repack an LM-head weight [V, H] bf16 (row-major) into the layout the
+ * LM-head calls stream, once per weight.  For vocabulary tile t (rows
+ * 32t .. 32t+31), k-step s (hidden elements 16s .. 16s+15) and lane l in
+ * [0, 64), the 16 bytes at byte offset ((t * H/16 + s) * 64 + l) * 16 hold
+ * weight[32t + l % 32][16s + 8 (l / 32) .. 16s + 8 (l / 32) + 7], zero for
+ * rows >= V.  Each wave of the LM-head kernel then reads its 32-row tile as
+ * one sequential stream.  weight and packed are 16-byte aligned device
+ * buffers that must not overlap. */
+orthrus_status orthrus_lm_head_pack_weight(const void* weight, void* packed, int32_t hidden_size, int32_t vocab,
+                                           void* stream);
+
 /* Bytes of the workspace the LM-head calls need for `rows` hidden rows: one
  * 8-byte key per (row, 128-entry vocabulary tile).  0 for an invalid shape.
  * The workspace needs no initialisation. */
@@ -192,9 +208,10 @@ size_t orthrus_lm_head_workspace_bytes(int32_t rows, int32_t hidden_size, int32_
  *   tokens[m]    = lowest v attaining the maximum (-0.0 ties with +0.0;
  *                  inputs must not produce NaN)
  *   max_logits[m]= that maximum (optional, may be NULL)
- * hidden [rows, H] bf16, weight [V, H] bf16 (row-major, 16-byte aligned).
+ * hidden [rows, H] bf16 (row-major); packed_weight is the weight [V, H] in
+ * the layout of orthrus_lm_head_pack_weight; both 16-byte aligned.
  * H a multiple of 256 in [256, 65536]; 1 <= rows <= 2^24; V >= 1. */
-orthrus_status orthrus_lm_head_argmax(const void* hidden, const void* weight, int32_t* tokens,
+orthrus_status orthrus_lm_head_argmax(const void* hidden, const void* packed_weight, int32_t* tokens,
                                       float* max_logits, int32_t rows, int32_t hidden_size, int32_t vocab,
                                       void* workspace, size_t workspace_bytes, void* stream);
 
@@ -203,7 +220,7 @@ orthrus_status orthrus_lm_head_argmax(const void* hidden, const void* weight, in
  * accept_len / next_token / ar_tokens exactly as orthrus_greedy_accept
  * defines them from g.  The workspace is that of
  * orthrus_lm_head_workspace_bytes(B * K, H, V).  1 <= K <= 32. */
-orthrus_status orthrus_lm_head_greedy_accept(const void* hidden, const void* weight,
+orthrus_status orthrus_lm_head_greedy_accept(const void* hidden, const void* packed_weight,
                                              const int32_t* draft_tokens, int32_t* accept_len,
                                              int32_t* next_token, int32_t* ar_tokens, int32_t batch,
                                              int32_t block_k, int32_t hidden_size, int32_t vocab,

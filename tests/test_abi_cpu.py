@@ -24,7 +24,7 @@ def declared_entry_points():
 
 def test_exports_every_declared_symbol():
     names = declared_entry_points()
-    assert len(names) == 15
+    assert len(names) == 17
     assert set(names) == set(B.SIGNATURES)
     lib = B.lib()
     for n in names:
@@ -168,6 +168,12 @@ def test_lm_head_validation():
     assert need == 32 * 1187 * 8
     assert lib.orthrus_lm_head_workspace_bytes(32, 4000, 151936) == 0
     assert call(wsb=need - 1) == 4 and call(ws=None) == 4
+    assert lib.orthrus_lm_head_packed_bytes(4096, 151936) == 151936 * 4096 * 2
+    assert lib.orthrus_lm_head_packed_bytes(256, 33) == 64 * 256 * 2          # padded to 32-row tiles
+    assert lib.orthrus_lm_head_packed_bytes(100, 33) == 0
+    assert lib.orthrus_lm_head_pack_weight(None, A16, 4096, 100, None) == 1
+    assert lib.orthrus_lm_head_pack_weight(A16, A16, 4000, 100, None) == 2
+    assert lib.orthrus_lm_head_pack_weight(A16, ctypes.c_void_p(4096 * 16 + 4), 4096, 100, None) == 2
     acc = lib.orthrus_lm_head_greedy_accept
     assert acc(A16, A16, None, FAKE, FAKE, None, 1, 32, 4096, 151936, FAKE, need, None) == 1
     assert acc(A16, A16, FAKE, FAKE, FAKE, None, 1, 33, 4096, 151936, FAKE, need, None) == 2

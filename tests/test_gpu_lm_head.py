@@ -59,7 +59,7 @@ def abs_bound(h, w, vslice=16384):
 def check_random(rows, H, V, seed):
     d = dev()
     h, w, _ = I.make_lm_head_inputs(rows, H, V, seed=seed)
-    tok, mx = ob().lm_head_argmax(h.to(d), w.to(d), want_max=True)
+    tok, mx = ob().lm_head_argmax(h.to(d), ob().PackedLmHead(w.to(d)), want_max=True)
     torch.cuda.synchronize()
     tok, mx = tok.cpu().numpy(), mx.cpu().numpy().astype(np.float64)
     lg = oracle_logits(h, w)
@@ -96,7 +96,7 @@ def test_lm_head_planted_qwen3_8b(rows):
     say("lm_head planted", rows)
     d = dev()
     h, w, t = I.make_lm_head_inputs(rows, I.QWEN3_8B_HIDDEN, I.QWEN3_VOCAB, seed=rows, planted=True, device=d)
-    tok, mx = ob().lm_head_argmax(h, w, want_max=True)
+    tok, mx = ob().lm_head_argmax(h, ob().PackedLmHead(w), want_max=True)
     torch.cuda.synchronize()
     assert torch.equal(tok, t)
     assert torch.all(mx == float(I.QWEN3_8B_HIDDEN))
@@ -117,7 +117,7 @@ def test_lm_head_planted_ties_resolve_to_lowest_index():
         wi = w.clone()
         wi[copy] = w[winner]
         h = w[winner:winner + 1].clone()
-        tok, mx = ob().lm_head_argmax(h, wi, want_max=True)
+        tok, mx = ob().lm_head_argmax(h, ob().PackedLmHead(wi), want_max=True)
         torch.cuda.synchronize()
         assert tok.item() == min(winner, copy) and mx.item() == float(H), (winner, copy, tok.item())
 
@@ -133,7 +133,7 @@ def test_lm_head_greedy_accept_planted():
     t = t.view(B, K).cpu()
     pre = np.array([0, 11, 32, 5])
     drafts = I.make_drafts(t, pre, V, seed=9).to(d)
-    acc, nxt, g = ob().lm_head_greedy_accept(h.view(B, K, H), w, drafts)
+    acc, nxt, g = ob().lm_head_greedy_accept(h.view(B, K, H), ob().PackedLmHead(w), drafts)
     torch.cuda.synchronize()
     assert torch.equal(g.cpu(), t) and acc.cpu().tolist() == pre.tolist()
     ra, rn, rg = O.lm_head_greedy_accept(h.view(B, K, H).cpu(), w.cpu(), drafts.cpu())
@@ -149,10 +149,11 @@ def test_lm_head_greedy_accept_matches_argmax_then_accept():
     d = dev()
     B, K = 2, 32
     h, w, _ = I.make_lm_head_inputs(B * K, I.QWEN3_8B_HIDDEN, I.QWEN3_VOCAB, seed=3, device=d)
-    tok, _ = ob().lm_head_argmax(h, w)
+    head = ob().PackedLmHead(w)
+    tok, _ = ob().lm_head_argmax(h, head)
     g0 = tok.view(B, K).cpu()
     drafts = I.make_drafts(g0, np.array([7, 32]), I.QWEN3_VOCAB, seed=3).to(d)
-    acc, nxt, g = ob().lm_head_greedy_accept(h.view(B, K, -1), w, drafts)
+    acc, nxt, g = ob().lm_head_greedy_accept(h.view(B, K, -1), head, drafts)
     torch.cuda.synchronize()
     assert torch.equal(g.cpu(), g0) and acc.cpu().tolist() == [7, 32]
     assert nxt.cpu().tolist() == [g0[0, 7].item(), g0[1, 31].item()]
@@ -165,7 +166,24 @@ def test_lm_head_workspace_reuse_and_determinism():
                     device=d)
     for rows, H, V, s in [(130, 512, 20000, 1), (3, 256, 900, 2), (64, 1024, 20000, 3)]:
         h, w, _ = I.make_lm_head_inputs(rows, H, V, seed=s, device=d)
-        a, am = ob().lm_head_argmax(h, w, want_max=True, ws=ws)
-        b, bm = ob().lm_head_argmax(h, w, want_max=True)
+        head = ob().PackedLmHead(w)
+        a, am = ob().lm_head_argmax(h, head, want_max=True, ws=ws)
+        b, bm = ob().lm_head_argmax(h, head, want_max=True)
         torch.cuda.synchronize()
         assert torch.equal(a, b) and torch.equal(am, bm)
+
+
+@pytest.mark.parametrize("V,H", [(1, 256), (33, 256), (1000, 512), (4099, 1024)])
+def test_lm_head_pack_layout(V, H):
+    """The packed weight is bit-exactly the layout the header defines: tile t,
+    k-step s, lane l hold weight[32 t + l % 32][16 s + 8 (l / 32) + j], zero
+    past the vocabulary (built here with numpy reshapes)."""
+    say("lm_head pack", V, H)
+    d = dev()
+    _, w, _ = I.make_lm_head_inputs(1, H, V, seed=V, device=d)
+    got = ob().PackedLmHead(w).packed.cpu().view(torch.int16).numpy()
+    T = (V + 31) // 32
+    wp = np.zeros((T * 32, H), dtype=np.int16)
+    wp[:V] = w.cpu().view(torch.int16).numpy()
+    want = wp.reshape(T, 32, H // 16, 2, 8).transpose(0, 2, 3, 1, 4).reshape(-1)
+    assert got.shape == want.shape and np.array_equal(got, want)
