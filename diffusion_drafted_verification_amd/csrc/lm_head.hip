@@ -19,7 +19,7 @@
 // (32 rows x 32 bytes per load instruction) tops out near 5.0 TB/s.
 //
 // lm_head_tiles: one work-group of 4 waves per (128-row vocabulary tile,
-// group of up to MT x 32 hidden rows).  Each wave streams its 32-row packed
+// group of MT x 32 hidden rows: 32 for up to 32 rows, else 64).  Each wave streams its 32-row packed
 // tile straight from HBM into MFMA A-operand registers (no reuse, so no
 // LDS), double-buffered by phase of KP hidden elements.  The hidden rows of
 // the phase are staged once per work-group in LDS (XOR chunk swizzle,
@@ -33,7 +33,7 @@
 // several groups, the later groups find the weight tile in that XCD's L2.
 //
 // lm_head_finish: one work-group per group of rows reduces each row's tile
-// keys (all loads of a lane issued before the reduction), writes the tokens
+// keys (32 threads per row, all loads issued before the reduction), writes the tokens
 // and, for the accept entry point, compares them with the drafts (wave
 // ballot: first mismatch) exactly as the greedy consensus does.
 #include "orthrus_device.h"
@@ -44,8 +44,8 @@ namespace orthrus {
 constexpr int kLmWaves = 4;
 constexpr int kLmThreads = kLmWaves * kWave;
 constexpr int kLmTileN = kLmWaves * 32;  // vocabulary rows per tile
-constexpr int kLmFinWaves = 16;
-constexpr int kLmFinThreads = kLmFinWaves * kWave;
+constexpr int kLmFinThreads = 1024;  // 32 rows x 32 threads
+constexpr int kFinBatch = 40;         // tile keys per thread in flight
 
 struct LmArgs {
   const bf16* h;               // [M, H]
@@ -208,49 +208,44 @@ __device__ __forceinline__ unsigned long long lm_max_u64(unsigned long long x, u
   return x > y ? x : y;
 }
 
-__device__ __forceinline__ unsigned long long lm_wave_max_u64(unsigned long long k) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)k, off, kWave);
-    const uint32_t hi = __shfl_xor((uint32_t)(k >> 32), off, kWave);
-    k = lm_max_u64(k, ((unsigned long long)hi << 32) | lo);
-  }
-  return k;
-}
-
-// one work-group per group of R rows (one sequence's K rows for the accept
-// entry point); wave w reduces rows w and w + 16
+// one work-group per group of R <= 32 rows (one sequence's K rows for the
+// accept entry point): 32 threads per row, each loading up to kFinBatch of
+// the row's tile keys at once (one memory round trip for the Qwen3 head's
+// 1187 tiles), then a max over the row's 32 threads
 __global__ void __launch_bounds__(kLmFinThreads) lm_head_finish(LmArgs a) {
   __shared__ int32_t gtok[32];
-  const int grp = blockIdx.x;
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  for (int i = wave; i < a.R; i += kLmFinWaves) {
-    const int m = grp * a.R + i;
-    if (m >= a.M) break;
+  const int grp = blockIdx.x, tid = threadIdx.x;
+  const int i = tid / 32, sub = tid % 32;
+  const int m = grp * a.R + i;
+  const bool live = i < a.R && m < a.M;
+  unsigned long long best = 0;
+  if (live) {
     const unsigned long long* keys = a.part + (size_t)m * a.ntiles;
-    unsigned long long k0 = 0, k1 = 0, k2 = 0, k3 = 0;
-    int q = lane;
-    for (; q + 3 * kWave < a.ntiles; q += 4 * kWave) {
-      const unsigned long long x0 = keys[q], x1 = keys[q + kWave], x2 = keys[q + 2 * kWave],
-                               x3 = keys[q + 3 * kWave];
-      k0 = lm_max_u64(k0, x0);
-      k1 = lm_max_u64(k1, x1);
-      k2 = lm_max_u64(k2, x2);
-      k3 = lm_max_u64(k3, x3);
+    for (int q0 = 0; q0 < a.ntiles; q0 += 32 * kFinBatch) {
+      unsigned long long x[kFinBatch];
+#pragma unroll
+      for (int j = 0; j < kFinBatch; ++j)  // past the end: the last key again (a max ignores repeats)
+        x[j] = keys[min(q0 + sub + 32 * j, a.ntiles - 1)];
+#pragma unroll
+      for (int j = 0; j < kFinBatch; ++j) best = lm_max_u64(best, x[j]);
     }
-    for (; q < a.ntiles; q += kWave) k0 = lm_max_u64(k0, keys[q]);
-    const unsigned long long best = lm_wave_max_u64(lm_max_u64(lm_max_u64(k0, k1), lm_max_u64(k2, k3)));
+  }
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) {
+    const uint32_t lo = __shfl_xor((uint32_t)best, off, kWave);
+    const uint32_t hi = __shfl_xor((uint32_t)(best >> 32), off, kWave);
+    best = lm_max_u64(best, ((unsigned long long)hi << 32) | lo);
+  }
+  if (live && sub == 0) {
     const int32_t tok = (int32_t)(0xffffffffu - (uint32_t)(best & 0xffffffffu));
-    if (lane == 0) {
-      gtok[i] = tok;
-      if (a.tokens) a.tokens[m] = tok;
-      if (a.maxv) a.maxv[m] = lm_from_order_bits((uint32_t)(best >> 32));
-    }
+    gtok[i] = tok;
+    if (a.tokens) a.tokens[m] = tok;
+    if (a.maxv) a.maxv[m] = lm_from_order_bits((uint32_t)(best >> 32));
   }
   if (!a.drafts) return;
   __syncthreads();
-  if (wave != 0) return;
-  const int K = a.R, b = grp;
+  if (tid >= kWave) return;
+  const int lane = tid, K = a.R, b = grp;
   bool miss = false;
   int32_t gt = 0;
   if (lane < K) {
@@ -289,7 +284,7 @@ static bool lm_shape_ok(long rows, int hidden, int vocab) {
   if (rows < 1 || vocab < 1 || hidden < 256 || hidden > 65536 || hidden % 256 != 0) return false;
   const long ntiles = (vocab + (long)kLmTileN - 1) / kLmTileN;
   const long tiles8 = (ntiles + 7) / 8 * 8;
-  const long mgroups = (rows + 127) / 128;  // the smallest row-group size used is 32 (MT = 1) for rows <= 32
+  const long mgroups = (rows + 63) / 64;
   return tiles8 * mgroups * 4 <= 0x7fffffffL && rows <= (1L << 24);
 }
 
@@ -308,15 +303,16 @@ static orthrus_status lm_launch_tiles(const LmArgs& a, hipStream_t s) {
 static orthrus_status lm_run(LmArgs a, hipStream_t s, int finish_groups) {
   a.ntiles = (a.V + kLmTileN - 1) / kLmTileN;
   orthrus_status st;
+  // 32 rows: one group, deep phases.  More rows: 64-row groups with shallow
+  // phases (two waves per SIMD fit); the groups of one weight tile run on
+  // one XCD, so after the first group the tile mostly comes from L2 (measured
+  // faster than 128-row groups, whose registers allow one wave per SIMD)
   if (a.M <= 32) {
     a.mgroups = 1;
     st = lm_launch_tiles<1, 256>(a, s);
-  } else if (a.M <= 64) {
-    a.mgroups = 1;
-    st = lm_launch_tiles<2, 256>(a, s);
   } else {
-    a.mgroups = (a.M + 127) / 128;
-    st = lm_launch_tiles<4, 128>(a, s);
+    a.mgroups = (a.M + 63) / 64;
+    st = lm_launch_tiles<2, 128>(a, s);
   }
   if (st != ORTHRUS_OK) return st;
   hipLaunchKernelGGL(lm_head_finish, dim3((unsigned)finish_groups), dim3(kLmFinThreads), 0, s, a);

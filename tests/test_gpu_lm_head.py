@@ -78,9 +78,9 @@ def check_random(rows, H, V, seed):
 @pytest.mark.parametrize("rows,H,V", [(1, 256, 1000), (7, 512, 5003), (32, 1024, 20000), (33, 256, 777),
                                       (64, 2048, 10007), (100, 512, 3001), (130, 256, 4099), (257, 512, 2000)])
 def test_lm_head_random_vs_oracle(rows, H, V):
-    """Row counts 1..257 cover one 32-row group, 64-row groups and several
-    128-row groups with ragged tails; vocabularies from 777 to 20000 cover
-    ragged 128-row tiles."""
+    """Row counts 1..257 cover one 32-row group and one to five 64-row
+    groups with ragged tails; vocabularies from 777 to 20000 cover ragged
+    128-row tiles."""
     say("lm_head random", rows, H, V)
     check_random(rows, H, V, seed=rows + V)
 
