@@ -168,6 +168,44 @@ def block_attn(q, k_cache, v_cache, k_blk, v_blk, page_table, ctx_lens, mode,
     return out
 
 
+def prefill_attn(q, k_cache, v_cache, k, v, page_table, ctx_lens, prompt_lens, softmax_scale=None,
+                 page_size=16, batches=None, heads=None):
+    """Causal attention of a prompt by the frozen AR head (§2.1: its keys and
+    values are what fill the shared cache; the prompt is processed causally,
+    as any AR prefill).
+
+    Shapes: q [B, S, Hq, D]; k, v [B, S, Hkv, D] (the prompt's own keys and
+    values); k_cache/v_cache [num_pages, Hkv, P, D] holding the L_b =
+    ctx_lens[b] positions already cached before the prompt; page_table
+    [B, max_pages]; prompt_lens [B] <= S.  Returns fp64 [B, S, Hq, D]: for
+    sequence b, query head h (KV head h*Hkv//Hq) and prompt row i <
+    prompt_lens[b], the softmax-weighted sum over cached positions 0..L_b-1
+    and prompt rows 0..i.  Rows i >= prompt_lens[b] (padding) and rows or
+    heads outside `batches`/`heads` are NaN.
+    """
+    q = _f64(q)
+    kp = _f64(k)
+    vp = _f64(v)
+    pt = _i64(page_table)
+    lens = _i64(ctx_lens)
+    plens = _i64(prompt_lens)
+    B, S, Hq, D = q.shape
+    Hkv = kp.shape[2]
+    scale = 1.0 / np.sqrt(D) if softmax_scale is None else float(softmax_scale)
+    out = np.full((B, S, Hq, D), np.nan)
+    for b in (range(B) if batches is None else batches):
+        L, n = int(lens[b]), int(plens[b])
+        for h in (range(Hq) if heads is None else heads):
+            g = h * Hkv // Hq
+            keys = np.concatenate([gather_context(k_cache, pt[b], L, g, page_size), kp[b, :n, g]])
+            vals = np.concatenate([gather_context(v_cache, pt[b], L, g, page_size), vp[b, :n, g]])
+            for i in range(n):
+                s = scale * (keys[:L + i + 1] @ q[b, i, h])
+                w = np.exp(s - s.max())
+                out[b, i, h] = (w @ vals[:L + i + 1]) / w.sum()
+    return out
+
+
 def greedy_argmax(logits):
     """g[..., ] = the lowest vocabulary index attaining the row maximum.
 
@@ -332,3 +370,29 @@ def kv_append(k_cache, v_cache, k_blk, v_blk, page_table, ctx_lens, accept_len, 
             slots[b, r] = page * page_size + slot
         new_lens[b] = L + n
     return kc, vc, new_lens, slots
+
+
+def kv_write(k_cache, v_cache, k, v, page_table, ctx_lens, n_rows, page_size=16):
+    """Write a prompt's keys and values into the shared cache (the prefill
+    that builds K_AR, V_AR, §2.1): rows r < n_rows[b] of k/v [B, S, Hkv, D] go
+    to logical position L_b + r, i.e. page page_table[b][(L_b+r)//P], slot
+    (L_b+r) % P, for every KV head; nothing else changes.
+
+    Returns (k_cache', v_cache', new_ctx_lens = L + n) with the caches as
+    fresh numpy copies of the element storage (bf16 as int16 bit patterns).
+    """
+    kc = _raw(k_cache).copy()
+    vc = _raw(v_cache).copy()
+    kr = _raw(k)
+    vr = _raw(v)
+    pt = _i64(page_table)
+    lens = _i64(ctx_lens)
+    n = _i64(n_rows)
+    for b in range(kr.shape[0]):
+        L = int(lens[b])
+        for r in range(int(n[b])):
+            pos = L + r
+            page = int(pt[b, pos // page_size])
+            kc[page, :, pos % page_size, :] = kr[b, r]
+            vc[page, :, pos % page_size, :] = vr[b, r]
+    return kc, vc, lens + n

@@ -682,3 +682,106 @@ def test_lm_head_greedy_accept_from_planted_hidden_states():
     acc, nxt, g = O.lm_head_greedy_accept(h, w, drafts)
     assert list(acc) == pre and np.array_equal(g, t)
     assert list(nxt) == [t[0, 0], t[1, 5], t[2, 7]]
+
+
+# ---------------------------------------------------------------------------
+# prefill (causal attention of a prompt over the paged cache) and KV write
+# ---------------------------------------------------------------------------
+
+def _rand_cache(rng, n_pages, Hkv, D, P=16):
+    return rng.normal(size=(n_pages, Hkv, P, D)), rng.normal(size=(n_pages, Hkv, P, D))
+
+
+def test_prefill_short_prompt_is_the_causal_block():
+    """A prompt of S <= 32 rows is exactly the AR verify pass's causal block
+    of K = S rows (block_attn in AR_CAUSAL, pinned on its own)."""
+    rng = np.random.default_rng(31)
+    B, S, Hq, Hkv, D = 2, 13, 4, 2, 16
+    kc, vc = _rand_cache(rng, 20, Hkv, D)
+    pt = rng.permutation(20).reshape(2, 10)
+    lens = np.array([37, 0])
+    q = rng.normal(size=(B, S, Hq, D))
+    k = rng.normal(size=(B, S, Hkv, D))
+    v = rng.normal(size=(B, S, Hkv, D))
+    got = O.prefill_attn(q, kc, vc, k, v, pt, lens, [S, S])
+    want = O.block_attn(q, kc, vc, k, v, pt, lens, O.AR_CAUSAL)
+    assert np.allclose(got, want, rtol=0, atol=1e-12)
+
+
+def test_prefill_dense_brute_force():
+    """Identity pages and one contiguous sequence: the output equals dense
+    causal attention over [cached context ; prompt] with an explicit
+    lower-triangular mask (scipy softmax)."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(32)
+    L, S, Hq, Hkv, D = 21, 40, 2, 1, 8
+    n_pages = -(-(L + S) // 16)
+    ctx_k = rng.normal(size=(L, D))
+    ctx_v = rng.normal(size=(L, D))
+    kc = np.zeros((n_pages, 1, 16, D))
+    vc = np.zeros((n_pages, 1, 16, D))
+    kc.reshape(-1, D)[:L] = ctx_k
+    vc.reshape(-1, D)[:L] = ctx_v
+    q = rng.normal(size=(1, S, Hq, D))
+    k = rng.normal(size=(1, S, Hkv, D))
+    v = rng.normal(size=(1, S, Hkv, D))
+    got = O.prefill_attn(q, kc, vc, k, v, np.arange(n_pages)[None], [L], [S])
+    K_all = np.concatenate([ctx_k, k[0, :, 0]])
+    V_all = np.concatenate([ctx_v, v[0, :, 0]])
+    mask = np.arange(L + S)[None, :] <= (L + np.arange(S))[:, None]
+    for h in range(Hq):
+        sc = np.where(mask, (q[0, :, h] @ K_all.T) / np.sqrt(D), -np.inf)
+        assert np.allclose(got[0, :, h], softmax(sc, axis=1) @ V_all, rtol=0, atol=1e-12)
+
+
+def test_prefill_in_two_chunks_equals_one_pass():
+    """Chunked prefill: the prompt's second part, run after the first part's
+    keys and values were written to the cache (kv_write), gives the same rows
+    as one pass over the whole prompt; the first row of an empty-context
+    prompt is its own value."""
+    rng = np.random.default_rng(33)
+    B, S1, S2, Hq, Hkv, D = 2, 19, 30, 4, 2, 8
+    kc, vc = _rand_cache(rng, 24, Hkv, D)
+    pt = rng.permutation(24).reshape(2, 12)
+    lens = np.array([50, 0])
+    S = S1 + S2
+    q = rng.normal(size=(B, S, Hq, D))
+    k = rng.normal(size=(B, S, Hkv, D))
+    v = rng.normal(size=(B, S, Hkv, D))
+    whole = O.prefill_attn(q, kc, vc, k, v, pt, lens, [S, S])
+    kc1, vc1, lens1 = O.kv_write(kc, vc, k[:, :S1], v[:, :S1], pt, lens, [S1, S1])
+    assert list(lens1) == [50 + S1, S1]
+    part2 = O.prefill_attn(q[:, S1:], kc1, vc1, k[:, S1:], v[:, S1:], pt, lens1, [S2, S2])
+    assert np.allclose(part2, whole[:, S1:], rtol=0, atol=1e-12)
+    for h in range(Hq):
+        assert np.allclose(whole[1, 0, h], v[1, 0, h * Hkv // Hq], rtol=0, atol=1e-15)
+
+
+def test_prefill_padding_rows_are_unset():
+    rng = np.random.default_rng(34)
+    kc, vc = _rand_cache(rng, 4, 1, 8)
+    q = rng.normal(size=(1, 10, 1, 8))
+    kv = rng.normal(size=(1, 10, 1, 8))
+    out = O.prefill_attn(q, kc, vc, kv, kv, [[0, 1, 2, 3]], [5], [7])
+    assert np.isfinite(out[0, :7]).all() and np.isnan(out[0, 7:]).all()
+
+
+def test_kv_write_writes_exactly_the_prompt_rows():
+    rng = np.random.default_rng(35)
+    B, S, Hkv, D = 2, 40, 2, 4
+    kc = np.full((16, Hkv, 16, D), -7.0)
+    vc = np.full((16, Hkv, 16, D), -9.0)
+    pt = rng.permutation(16).reshape(2, 8)
+    lens = np.array([3, 60])
+    k = rng.normal(size=(B, S, Hkv, D))
+    v = rng.normal(size=(B, S, Hkv, D))
+    kc2, vc2, nl = O.kv_write(kc, vc, k, v, pt, lens, [40, 17])
+    assert list(nl) == [43, 77]
+    written = np.zeros(kc.shape[:1] + kc.shape[2:3], dtype=bool)   # [page, slot]
+    for b, (L, n) in enumerate([(3, 40), (60, 17)]):
+        for r in range(n):
+            pos = L + r
+            page, slot = pt[b, pos // 16], pos % 16
+            assert np.array_equal(kc2[page, :, slot], k[b, r]) and np.array_equal(vc2[page, :, slot], v[b, r])
+            written[page, slot] = True
+    assert (kc2.transpose(0, 2, 1, 3)[~written] == -7.0).all() and (vc2.transpose(0, 2, 1, 3)[~written] == -9.0).all()
