@@ -19,11 +19,15 @@ peak.  `cpu_baseline` = the fp64 oracle on a bounded sample of the same step
 on the host cores.  `sample_accept` = the sampled consensus at temperature 1
 (orthrus_sample_accept over both heads' [B, 32, 151936] fp32 logits) timed
 on its own at B = 1 and 16; it is not part of the greedy step above.
+`lm_head` = the LM head with fused argmax and greedy accept at the Qwen3-8B
+head (B = 1, 4, 16); `prefill` = the prompt prefill of one layer (2k and 8k
+prompts).  Neither is part of the step above either.
 """
 
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -51,6 +55,7 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--no-sample", action="store_true", help="skip the sampled-consensus timing")
     p.add_argument("--no-lm-head", action="store_true", help="skip the LM-head timing")
+    p.add_argument("--no-prefill", action="store_true", help="skip the prompt-prefill timing")
     p.add_argument("--no-long-context", action="store_true",
                    help="skip the 36-layer step at batch 4, 32768 cached tokens")
     p.add_argument("--copy-probe-mib", type=int, default=0,
@@ -248,6 +253,38 @@ def lm_head_timing(torch, ob, I, use_graph):
             "vocab": V, "block_k": K, **out}
 
 
+def prefill_timing(torch, ob, I, use_graph):
+    """Prompt prefill (orthrus_prefill: cache write plus causal attention) of
+    one layer at the Qwen3-8B attention shape (Hq 32, Hkv 8, D 128, bf16),
+    B = 1: a 2048-token prompt with an empty cache, a 2048-token prompt after
+    8192 cached tokens, and an 8192-token prompt.  Algorithmic flops: QK^T
+    and PV over the causal set, 4 * Hq * D * sum_i (L + i + 1)."""
+    d = torch.device("cuda:0")
+    Hq, Hkv, D = 32, 8, 128
+    out = {}
+    for L, S in ((0, 2048), (8192, 2048), (0, 8192)):
+        x = I.make_prefill_inputs([L], [S], Hq, Hkv, D, seed=1, device=d)
+        ws = torch.empty(max(256, ob.lib().orthrus_prefill_workspace_bytes(
+            ctypes.byref(ob.make_desc(x["q"][:, :32], x["k_cache"], x["page_table"], L)), S)),
+            dtype=torch.uint8, device=d)
+        o = torch.empty_like(x["q"])
+        nl = torch.empty(1, dtype=torch.int32, device=d)
+        fn = lambda: ob.prefill(x["q"], x["k"], x["v"], x["k_cache"], x["v_cache"], x["page_table"], x["ctx_lens"],
+                                x["prompt_lens"], S, o, new_ctx_lens=nl, max_ctx_len=L, ws=ws)
+        fn()
+        rep = capture(torch, fn) if use_graph else fn
+        ms = time_region(torch, rep, 10, 2)
+        flops = 4.0 * Hq * D * sum(L + i + 1 for i in range(S))
+        tf = flops / (ms * 1e-3) / 1e12
+        out[f"L{L}_S{S}"] = {"us_per_call": round(ms * 1e3, 1), "tflops": round(tf, 1),
+                             "frac_mfma_bf16": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                             "prompt_tokens_per_s": round(S / (ms * 1e-3), 1)}
+        del x, ws, o, rep
+        torch.cuda.empty_cache()
+    return {"kernel": "orthrus_prefill (prefill_setup + prefill_kv_write + attn_stream AR_CAUSAL)",
+            "shape": "B1 Hq32/Hkv8 D128 bf16, one layer", **out}
+
+
 def cpu_baseline(step, I, seconds):
     """The fp64 oracle, as is, on one layer of the step (both views, accept,
     append) at the same shapes; repeated for about `seconds`."""
@@ -384,6 +421,13 @@ def main():
         torch.cuda.empty_cache()
         lmhead = lm_head_timing(torch, ob, I, use_graph)
 
+    pre = None
+    if not args.no_prefill:
+        log("prefill")
+        step = None
+        torch.cuda.empty_cache()
+        pre = prefill_timing(torch, ob, I, use_graph)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline")
@@ -400,7 +444,7 @@ def main():
                        "graph": use_graph, "parallelism": "none (1 GPU)"},
             "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
             "roofline": roof, "cpu_baseline": cpu, "sweep": sweep or None, "long_context_step": longctx,
-            "sample_accept": sample, "lm_head": lmhead}
+            "sample_accept": sample, "lm_head": lmhead, "prefill": pre}
     print(json.dumps(line), flush=True)
 
 

@@ -23,7 +23,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB_NAME = "liborthrus_gfx950.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["block_attn.hip", "greedy_accept.hip", "kv_append.hip", "sample_accept.hip", "lm_head.hip"]
+SOURCES = ["block_attn.hip", "greedy_accept.hip", "kv_append.hip", "sample_accept.hip", "lm_head.hip", "prefill.hip"]
 ARCH = "gfx950"
 
 

@@ -265,3 +265,28 @@ def make_lm_head_inputs(rows, hidden, vocab, seed=0, workload="", planted=False,
                       device=device, dtype=torch.int64)
     h = w[t].clone()
     return h, w, t.to(torch.int32)
+
+
+def make_prefill_inputs(ctx_lens, prompt_lens, n_q_heads, n_kv_heads, head_dim, dtype=torch.bfloat16, seed=0,
+                        device="cpu", shuffle=True):
+    """A prompt of prompt_lens[b] rows after ctx_lens[b] cached tokens: q
+    [B, S, Hq, D] and the prompt's k, v [B, S, Hkv, D] with S = max prompt
+    rounded up to 32 (rows past the prompt are padding), a paged cache
+    [num_pages, Hkv, 16, D] whose pages hold N(0, 1) values everywhere (the
+    positions the prompt will occupy start with stale values), and a page
+    table with room for L_b + S tokens.  Returns a dict of tensors plus
+    `max_prompt` and `max_ctx_len`."""
+    lens = np.asarray(ctx_lens, dtype=np.int32)
+    plens = np.asarray(prompt_lens, dtype=np.int32)
+    B = len(lens)
+    mp = int(plens.max())
+    S = (mp + 31) // 32 * 32
+    table, num_pages = make_page_table(lens, S, PAGE_SIZE, shuffle, seed=seed + 77)
+    s = lambda name: _seed(seed, "prefill", 0, name)
+    return dict(q=_randn((B, S, n_q_heads, head_dim), dtype, device, s("q")),
+                k=_randn((B, S, n_kv_heads, head_dim), dtype, device, s("k_blk")),
+                v=_randn((B, S, n_kv_heads, head_dim), dtype, device, s("v_blk")),
+                k_cache=_randn((num_pages, n_kv_heads, PAGE_SIZE, head_dim), dtype, device, s("k_cache")),
+                v_cache=_randn((num_pages, n_kv_heads, PAGE_SIZE, head_dim), dtype, device, s("v_cache")),
+                page_table=torch.from_numpy(table).to(device), ctx_lens=torch.from_numpy(lens).to(device),
+                prompt_lens=torch.from_numpy(plens).to(device), max_prompt=mp, max_ctx_len=int(lens.max()))

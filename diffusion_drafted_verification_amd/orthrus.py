@@ -54,6 +54,8 @@ SIGNATURES = {
     "orthrus_lm_head_greedy_accept": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp]),
     "orthrus_kv_append": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _DESC_P, _vp]),
     "orthrus_kv_append_layers": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _DESC_P, _vp]),
+    "orthrus_prefill_workspace_bytes": (_sz, [_DESC_P, _i32]),
+    "orthrus_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _DESC_P, _vp, _sz, _vp]),
     "orthrus_copy_probe": (_i32, [_vp, _vp, _sz, _vp]),
 }
 
@@ -356,6 +358,34 @@ def kv_append_layers(layers, page_table, ctx_lens, accept_len, *, new_ctx_lens=N
                                         ctypes.byref(desc), _stream(stream))
     _check(st, "orthrus_kv_append_layers")
     return new_ctx_lens, slots
+
+
+def prefill(q, k, v, k_cache, v_cache, page_table, ctx_lens, prompt_lens, max_prompt, out=None, *,
+            new_ctx_lens=None, max_ctx_len=None, softmax_scale=None, split_tokens=0, ws=None, stream=None):
+    """orthrus_prefill (writes the prompt rows into the caches in place):
+    q [B, S, Hq, D], k/v [B, S, Hkv, D] with S = max_prompt rounded up to a
+    multiple of 32.  Returns (out [B, S, Hq, D], new_ctx_lens [B])."""
+    dev = _gpu(q, k, v, k_cache, v_cache, page_table, ctx_lens, prompt_lens, out, new_ctx_lens)
+    B, S = q.shape[0], q.shape[1]
+    if S != (int(max_prompt) + 31) // 32 * 32 or tuple(k.shape[:2]) != (B, S) or tuple(v.shape) != tuple(k.shape):
+        raise OrthrusError("q/k/v must be [B, S, ...] with S = max_prompt rounded up to a multiple of 32")
+    if page_table.dtype != torch.int32 or ctx_lens.dtype != torch.int32 or prompt_lens.dtype != torch.int32:
+        raise OrthrusError("page_table, ctx_lens and prompt_lens must be int32")
+    if out is None:
+        out = torch.empty_like(q)
+    if new_ctx_lens is None:
+        new_ctx_lens = torch.empty(B, dtype=torch.int32, device=dev)
+    if max_ctx_len is None:   # the largest context the table leaves room for before the prompt
+        max_ctx_len = page_table.shape[1] * PAGE_SIZE - S
+    desc = make_desc(q[:, :32], k_cache, page_table, max_ctx_len, softmax_scale, split_tokens)
+    need = lib().orthrus_prefill_workspace_bytes(ctypes.byref(desc), int(max_prompt))
+    if ws is None:
+        ws = workspace(dev, need, "prefill")
+    st = lib().orthrus_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+                               _ptr(ctx_lens), _ptr(prompt_lens), int(max_prompt), _ptr(out), _ptr(new_ctx_lens),
+                               ctypes.byref(desc), _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "orthrus_prefill")
+    return out, new_ctx_lens
 
 
 def copy_probe(dst, src, stream=None):

@@ -2,7 +2,8 @@
  * orthrus.h -- C ABI of the MI355X (gfx950) hot path of one Orthrus
  * dual-view decode step: block attention over a shared paged KV cache,
  * greedy consensus (argmax + longest-prefix accept), its sampling form at
- * temperature T > 0, the LM head with a fused argmax, and KV append.
+ * temperature T > 0, the LM head with a fused argmax, KV append and the
+ * prompt prefill that fills the cache.
  *
  * Semantics follow the Orthrus explainer page for "Orthrus: Memory-Efficient
  * Parallel Token Generation via Dual-View Diffusion" (gist.science, arXiv
@@ -251,6 +252,36 @@ orthrus_status orthrus_kv_append_layers(const uint64_t* k_cache_ptrs, const uint
                                         const int32_t* page_table, const int32_t* ctx_lens,
                                         const int32_t* accept_len, int32_t* new_ctx_lens, int32_t* slots,
                                         const orthrus_attn_desc* desc, void* stream);
+
+/* Bytes of the workspace orthrus_prefill needs: the virtual page-table rows
+ * and context lengths of the prompt's 32-row chunks plus the block-attention
+ * workspace of that virtual batch.  0 for an invalid shape.  The workspace
+ * needs no initialisation; it must be 256-byte aligned. */
+size_t orthrus_prefill_workspace_bytes(const orthrus_attn_desc* desc, int32_t max_prompt);
+
+/* Prompt prefill by the frozen AR head (explainer §2.1: the prompt's keys
+ * and values fill the shared cache that both views read).  For sequence b
+ * with L = ctx_lens[b] tokens already cached and n = prompt_lens[b] prompt
+ * rows (0 <= n <= max_prompt):
+ *   - rows r < n of k/v are written bit-exactly to logical positions L + r of
+ *     k_cache/v_cache (through page_table; nothing else is written);
+ *   - out[b, i, h] for i < n = softmax(scale * q . k) . v over cached
+ *     positions 0 .. L-1 and prompt rows 0 .. i (causal), KV head
+ *     h * Hkv / Hq, fp32 accumulation; rows i >= n are unspecified;
+ *   - new_ctx_lens[b] = L + n (optional, may be NULL; must not alias
+ *     ctx_lens).
+ * q, out [B, S, Hq, D] and k, v [B, S, Hkv, D] in the storage dtype, with
+ * S = max_prompt rounded up to a multiple of 32 (rows past n are padding
+ * the caller allocates).  desc is as for orthrus_block_attn with
+ * max_ctx_len bounding every L and block_k ignored;
+ * max_ctx_len + S <= max_pages_per_seq * P.  The prompt's 32-row chunks run
+ * as AR_CAUSAL blocks of orthrus_block_attn over B * S / 32 virtual
+ * sequences, after the cache write, on `stream`. */
+orthrus_status orthrus_prefill(const void* q, const void* k, const void* v, void* k_cache, void* v_cache,
+                               const int32_t* page_table, const int32_t* ctx_lens, const int32_t* prompt_lens,
+                               int32_t max_prompt, void* out, int32_t* new_ctx_lens,
+                               const orthrus_attn_desc* desc, void* workspace, size_t workspace_bytes,
+                               void* stream);
 
 /* Measurement helper: streams `bytes` (a multiple of 16) from src to dst with
  * plain 16-byte loads and stores.  Used to calibrate hardware counters and to

@@ -24,7 +24,7 @@ def declared_entry_points():
 
 def test_exports_every_declared_symbol():
     names = declared_entry_points()
-    assert len(names) == 17
+    assert len(names) == 19
     assert set(names) == set(B.SIGNATURES)
     lib = B.lib()
     for n in names:
@@ -178,6 +178,28 @@ def test_lm_head_validation():
     assert acc(A16, A16, None, FAKE, FAKE, None, 1, 32, 4096, 151936, FAKE, need, None) == 1
     assert acc(A16, A16, FAKE, FAKE, FAKE, None, 1, 33, 4096, 151936, FAKE, need, None) == 2
     assert acc(A16, A16, FAKE, FAKE, FAKE, None, 2, 32, 4096, 151936, FAKE, need, None) == 4   # needs 64 rows
+
+
+def test_prefill_validation():
+    lib = B.lib()
+    d = good_desc(max_ctx_len=4096, max_pages_per_seq=514)      # capacity 8224 positions
+    wsb = lib.orthrus_prefill_workspace_bytes(ctypes.byref(d), 4096)
+    # 128 virtual sequences: their page-table rows and lengths, each region
+    # rounded up to 256 bytes, then the block-attention workspace of the
+    # virtual batch
+    vd = good_desc(batch=128, block_k=32, max_ctx_len=4096 + 4096 - 32, max_pages_per_seq=514)
+    up = lambda x: -(-x // 256) * 256
+    assert wsb == up(128 * 514 * 4) + up(128 * 4) + lib.orthrus_block_attn_workspace_bytes(ctypes.byref(vd))
+    assert lib.orthrus_prefill_workspace_bytes(ctypes.byref(d), 4200) == 0      # 4096 + 4224 > 8224
+    assert lib.orthrus_prefill_workspace_bytes(ctypes.byref(d), 0) == 0
+    W = ctypes.c_void_p(4096 * 256)
+    call = lambda desc, mp, ws=W, wsb=wsb, q=FAKE: lib.orthrus_prefill(
+        q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, mp, FAKE, None, ctypes.byref(desc), ws, wsb, None)
+    assert call(d, 4096, q=None) == 1
+    assert call(d, 4200) == 2 and call(d, 0) == 2
+    assert call(good_desc(head_dim=80, max_ctx_len=0), 32) == 3
+    assert call(d, 4096, wsb=wsb - 1) == 4 and call(d, 4096, ws=None) == 4
+    assert call(d, 4096, ws=ctypes.c_void_p(4096 * 256 + 16)) == 4          # 256-byte alignment
 
 
 def test_binding_refuses_cpu_tensors():
