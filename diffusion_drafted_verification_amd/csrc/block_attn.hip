@@ -232,7 +232,9 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_main(AttnArgs a) {
   const int BH = a.B * a.Hkv;
   const int bg = blockIdx.x % BH;
   const int s = blockIdx.x / BH;
-  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  // sequences in reverse order: where later sequences carry longer contexts
+  // (the chunks of a prompt prefill) the longest work-groups start first
+  const int b = a.B - 1 - bg / a.Hkv, g = bg % a.Hkv;
   const int tid = threadIdx.x;
   const int p_begin = s * a.split;
   const int page_base = p_begin >> 4;
@@ -868,7 +870,9 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_stream(AttnArgs a) {
   const int BH = a.B * a.Hkv;
   const int bg = blockIdx.x % BH;
   const int s = blockIdx.x / BH;
-  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  // sequences in reverse order: where later sequences carry longer contexts
+  // (the chunks of a prompt prefill) the longest work-groups start first
+  const int b = a.B - 1 - bg / a.Hkv, g = bg % a.Hkv;
   const int tid = threadIdx.x;
   const int p_begin = s * a.split;
   const int page_base = p_begin >> 4;

@@ -90,6 +90,10 @@ static orthrus_status prefill_desc(const orthrus_attn_desc* d, int32_t max_promp
   *C = *S / kChunk;
   if ((long)d->batch * *C > 0x7fffffffL / 64) return ORTHRUS_ERR_SHAPE;
   *vd = *d;
+  // automatic split: the longest allowed (the virtual batch of chunks already
+  // fills the GPU, and measured on the Qwen3-8B shape, fewer splits beat the
+  // extra combine pass: 2k prompt after 8k cached, 412 -> 371 us)
+  if (vd->split_tokens == 0) vd->split_tokens = 8192;
   vd->block_k = kChunk;
   vd->batch = d->batch * *C;
   const long vmax = (long)d->max_ctx_len + *S - kChunk;

@@ -273,8 +273,8 @@ size_t orthrus_prefill_workspace_bytes(const orthrus_attn_desc* desc, int32_t ma
  * q, out [B, S, Hq, D] and k, v [B, S, Hkv, D] in the storage dtype, with
  * S = max_prompt rounded up to a multiple of 32 (rows past n are padding
  * the caller allocates).  desc is as for orthrus_block_attn with
- * max_ctx_len bounding every L and block_k ignored;
- * max_ctx_len + S <= max_pages_per_seq * P.  The prompt's 32-row chunks run
+ * max_ctx_len bounding every L and block_k ignored (split_tokens 0 selects
+ * 8192, the fewest splits); max_ctx_len + S <= max_pages_per_seq * P.  The prompt's 32-row chunks run
  * as AR_CAUSAL blocks of orthrus_block_attn over B * S / 32 virtual
  * sequences, after the cache write, on `stream`. */
 orthrus_status orthrus_prefill(const void* q, const void* k, const void* v, void* k_cache, void* v_cache,

@@ -186,8 +186,8 @@ def test_prefill_validation():
     wsb = lib.orthrus_prefill_workspace_bytes(ctypes.byref(d), 4096)
     # 128 virtual sequences: their page-table rows and lengths, each region
     # rounded up to 256 bytes, then the block-attention workspace of the
-    # virtual batch
-    vd = good_desc(batch=128, block_k=32, max_ctx_len=4096 + 4096 - 32, max_pages_per_seq=514)
+    # virtual batch (automatic split: 8192 positions)
+    vd = good_desc(batch=128, block_k=32, max_ctx_len=4096 + 4096 - 32, max_pages_per_seq=514, split_tokens=8192)
     up = lambda x: -(-x // 256) * 256
     assert wsb == up(128 * 514 * 4) + up(128 * 4) + lib.orthrus_block_attn_workspace_bytes(ctypes.byref(vd))
     assert lib.orthrus_prefill_workspace_bytes(ctypes.byref(d), 4200) == 0      # 4096 + 4224 > 8224
