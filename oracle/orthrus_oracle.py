@@ -43,6 +43,10 @@ Readings of points the pages leave open (each one is listed in the design doc):
 * argmax ties go to the lowest index; -0.0 equals +0.0 (IEEE compare);
 * the LM head is a plain linear map hidden @ weight^T with weight stored as
   [V, H] (no bias, no logit scaling or soft-cap);
+* multi-step denoising (a variant the pages name without its re-mask rule)
+  uses low-confidence remasking: each step unmasks the most confident
+  still-masked positions, confidence = the greedy token's softmax
+  probability;
 * at temperature T > 0 a draft is accepted when u * q[x] < p[x] (p, q the
   AR and diffusion softmaxes at T; u a given uniform), and the correction at
   the first rejection is drawn from max(p - q, 0) by inverse CDF with a
@@ -275,6 +279,42 @@ def lm_head_greedy_accept(hidden, weight, draft_tokens):
     [B, K, H]: greedy_accept of lm_head_logits.  Returns (accept_len [B],
     next_token [B], g [B, K])."""
     return greedy_accept(lm_head_logits(hidden, weight), draft_tokens)
+
+
+def denoise_confidence(logits):
+    """Greedy token and its confidence per row: the token is greedy_argmax
+    and the confidence is its softmax probability,
+    max_v softmax(x)_v = 1 / sum_v exp(x_v - max x)."""
+    x = _f64(logits)
+    m = x.max(axis=-1, keepdims=True)
+    return greedy_argmax(x), 1.0 / np.exp(x - m).sum(axis=-1)
+
+
+def denoise_select(confidence, masked, n_unmask):
+    """One step of low-confidence remasking over a block: among the
+    positions still masked, the n_unmask[b] most confident are unmasked (ties
+    go to the lower position); every other masked position stays masked and
+    unmasked positions stay unmasked.  Returns the new mask [B, K] (bool)."""
+    c = _f64(confidence)
+    m = np.asarray(masked, dtype=bool)
+    n = _i64(n_unmask)
+    out = m.copy()
+    for b in range(c.shape[0]):
+        cand = [i for i in range(c.shape[1]) if m[b, i]]
+        order = sorted(cand, key=lambda i: (-c[b, i], i))
+        for i in order[:max(int(n[b]), 0)]:
+            out[b, i] = False
+    return out
+
+
+def lm_head_denoise_step(hidden, weight, masked, n_unmask):
+    """One multi-step-denoising update from the diffusion view's final hidden
+    states [B, K, H]: the LM-head logits give every position's greedy token
+    and confidence, then denoise_select unmasks the n_unmask[b] most confident
+    masked positions.  Returns (tokens [B, K], confidence [B, K],
+    new_mask [B, K])."""
+    tok, conf = denoise_confidence(lm_head_logits(hidden, weight))
+    return tok, conf, denoise_select(conf, masked, n_unmask)
 
 
 def softmax_t(logits, temperature):

@@ -785,3 +785,65 @@ def test_kv_write_writes_exactly_the_prompt_rows():
             assert np.array_equal(kc2[page, :, slot], k[b, r]) and np.array_equal(vc2[page, :, slot], v[b, r])
             written[page, slot] = True
     assert (kc2.transpose(0, 2, 1, 3)[~written] == -7.0).all() and (vc2.transpose(0, 2, 1, 3)[~written] == -9.0).all()
+
+
+# ---------------------------------------------------------------------------
+# multi-step denoising: confidence and low-confidence remasking
+# ---------------------------------------------------------------------------
+
+def test_denoise_confidence_closed_forms():
+    """Equal logits give 1/V; two logits give the logistic function of their
+    gap; a shift of every logit changes nothing; a dominant logit tends to 1."""
+    rng = np.random.default_rng(41)
+    tok, conf = O.denoise_confidence(np.zeros((2, 3, 50)))
+    assert np.allclose(conf, 1 / 50) and (tok == 0).all()
+    d = rng.normal(size=20)
+    x = np.stack([d, np.zeros(20)], axis=-1)
+    _, c2 = O.denoise_confidence(x)
+    assert np.allclose(c2, 1 / (1 + np.exp(-np.abs(d))), rtol=1e-13)
+    y = rng.normal(size=(4, 6, 30))
+    t1, c1 = O.denoise_confidence(y)
+    t3, c3 = O.denoise_confidence(y + 123.25)
+    assert np.array_equal(t1, t3) and np.allclose(c1, c3, rtol=1e-12)
+    y[0, 0, 7] = 60.0
+    t4, c4 = O.denoise_confidence(y)
+    assert t4[0, 0] == 7 and c4[0, 0] >= 1 - 1e-15
+
+
+def test_denoise_select_brute_force():
+    """For tiny blocks, the unmasked set is the subset of the masked positions
+    of size min(n, #masked) with the largest total confidence under a strict
+    order (confidence, then lower position), checked over every subset."""
+    from itertools import combinations
+    rng = np.random.default_rng(42)
+    for _ in range(60):
+        K = 6
+        conf = rng.choice([0.1, 0.2, 0.3, 0.5], size=(1, K))        # ties on purpose
+        masked = rng.random((1, K)) < 0.7
+        n = int(rng.integers(0, K + 2))
+        new = O.denoise_select(conf, masked, [n])
+        cand = list(np.flatnonzero(masked[0]))
+        k = min(n, len(cand))
+        key = lambda i: (conf[0, i], -i)
+        best = max(combinations(cand, k), key=lambda sub: sorted((key(i) for i in sub), reverse=True))
+        want = masked[0].copy()
+        want[list(best)] = False
+        assert np.array_equal(new[0], want), (conf, masked, n)
+        assert not (new & ~masked).any()                # never re-masks an unmasked position
+
+
+def test_denoise_loop_unmasks_everything_on_schedule():
+    """T steps of a linear schedule (the per-step counts sum to K) leave no
+    position masked, and each step unmasks exactly its count."""
+    rng = np.random.default_rng(43)
+    B, K, H, V, T = 2, 32, 16, 40, 5
+    w = rng.normal(size=(V, H))
+    masked = np.ones((B, K), dtype=bool)
+    sched = [(t + 1) * K // T - t * K // T for t in range(T)]
+    assert sum(sched) == K
+    for t in range(T):
+        h = rng.normal(size=(B, K, H))
+        _, _, new = O.lm_head_denoise_step(h, w, masked, [sched[t]] * B)
+        assert (masked.sum(1) - new.sum(1) == sched[t]).all()
+        masked = new
+    assert not masked.any()
