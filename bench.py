@@ -246,10 +246,23 @@ def lm_head_timing(torch, ob, I, use_graph):
                           "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
                           "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
                           "frac_mfma_bf16": round(flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
-        del h, ws, rep
+        # the multi-step denoising update on the same rows (argmax plus the
+        # softmax statistics in the epilogue, then the remasking)
+        masked = torch.ones((bs, K), dtype=torch.uint8, device=d)
+        nun = torch.full((bs,), 8, dtype=torch.int32, device=d)
+        nm = torch.empty_like(masked)
+        wsd = torch.empty(ob.lib().orthrus_lm_head_denoise_workspace_bytes(bs * K, H, V), dtype=torch.uint8,
+                          device=d)
+        fnd = lambda: [ob.lm_head_denoise_step(h, head, masked, nun, new_masked=nm, ws=wsd) for _ in range(n)]
+        fnd()
+        repd = capture(torch, fnd) if use_graph else fnd
+        msd = time_region(torch, repd, 5, 2) / n
+        out[f"bs{bs}"]["denoise_step_us"] = round(msd * 1e3, 2)
+        del h, ws, rep, repd, wsd
     del head
     torch.cuda.empty_cache()
-    return {"kernel": "orthrus_lm_head_greedy_accept (lm_head_tiles + lm_head_finish)", "hidden": H,
+    return {"kernel": "orthrus_lm_head_greedy_accept (lm_head_tiles + lm_head_finish); denoise_step_us: "
+                      "orthrus_lm_head_denoise_step on the same rows", "hidden": H,
             "vocab": V, "block_k": K, **out}
 
 

@@ -41,14 +41,23 @@
 
 namespace orthrus {
 
+typedef float lm_f32x2 __attribute__((ext_vector_type(2)));
+
 constexpr int kLmWaves = 4;
 constexpr int kLmThreads = kLmWaves * kWave;
 constexpr int kLmTileN = kLmWaves * 32;  // vocabulary rows per tile
 constexpr int kLmFinThreads = 1024;  // 32 rows x 32 threads
 constexpr int kFinBatch = 40;         // tile keys per thread in flight
+constexpr int kFinPairs = 20;         // (max, sum) pairs per thread in flight
+constexpr float kLog2e = 1.4426950408889634f;
 
 struct LmArgs {
   const bf16* h;               // [M, H]
+  lm_f32x2* ms;                   // [M, ntiles] (tile max, sum of exp(logit - max)) or nullptr
+  const uint8_t* masked;       // denoise: [M] 1 = position still masked
+  const int32_t* n_unmask;     // denoise: [M / R]
+  float* conf;                 // denoise: [M] greedy token's softmax probability
+  uint8_t* masked_out;         // denoise: [M]
   const u32x4* w;              // packed weight: [ceil(V / 32)][H / 16][64 lanes] 16-byte fragments
   unsigned long long* part;    // [M, ntiles] tile keys
   const int32_t* drafts;       // [M] (accept) or nullptr
@@ -86,6 +95,7 @@ __global__ void __launch_bounds__(kLmThreads) lm_head_tiles(LmArgs a) {
   __shared__ u32x4 hs[2][ROWS * CH];
   __shared__ float rv[kLmWaves][32];
   __shared__ int ri[kLmWaves][32];
+  __shared__ float rs[kLmWaves][32];
 
   // block -> (tile, row group): the row groups of one tile share an XCD
   const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
@@ -187,18 +197,40 @@ __global__ void __launch_bounds__(kLmThreads) lm_head_tiles(LmArgs a) {
       }
     }
     lm_keep(bv, bi, __shfl_xor(bv, 32, kWave), __shfl_xor(bi, 32, kWave));
+    // softmax statistics of the tile (denoise): the sum of exp(logit - max)
+    // over the wave's 32 rows, then merged over the four waves
+    float se = 0.f;
+    if (a.ms) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int nn = nbase + 8 * (e >> 2) + 4 * g + (e & 3);
+        se += nn < a.V ? __builtin_amdgcn_exp2f((acc[mt][e] - bv) * kLog2e) : 0.f;
+      }
+      se += __shfl_xor(se, 32, kWave);
+    }
     if (g == 0) {
       rv[wave][c32] = bv;
       ri[wave][c32] = bi;
+      rs[wave][c32] = se;
     }
     __syncthreads();
     if (wave == 0 && g == 0) {
+      const float wmax0 = bv;
 #pragma unroll
       for (int w = 1; w < kLmWaves; ++w) lm_keep(bv, bi, rv[w][c32], ri[w][c32]);
       const int m = m0 + mt * 32 + c32;
-      if (m < a.M)
+      if (m < a.M) {
         a.part[(size_t)m * a.ntiles + tile] =
             ((unsigned long long)lm_order_bits(bv) << 32) | (unsigned long long)(0xffffffffu - (uint32_t)bi);
+        if (a.ms) {
+          // waves whose rows are all past V hold (-inf, 0) and add nothing
+          float tot = se * __builtin_amdgcn_exp2f((wmax0 - bv) * kLog2e);
+#pragma unroll
+          for (int w = 1; w < kLmWaves; ++w)
+            tot += rv[w][c32] == -INFINITY ? 0.f : rs[w][c32] * __builtin_amdgcn_exp2f((rv[w][c32] - bv) * kLog2e);
+          a.ms[(size_t)m * a.ntiles + tile] = lm_f32x2{bv, tot};
+        }
+      }
     }
     __syncthreads();
   }
@@ -214,6 +246,7 @@ __device__ __forceinline__ unsigned long long lm_max_u64(unsigned long long x, u
 // 1187 tiles), then a max over the row's 32 threads
 __global__ void __launch_bounds__(kLmFinThreads) lm_head_finish(LmArgs a) {
   __shared__ int32_t gtok[32];
+  __shared__ float gconf[32];
   const int grp = blockIdx.x, tid = threadIdx.x;
   const int i = tid / 32, sub = tid % 32;
   const int m = grp * a.R + i;
@@ -236,16 +269,66 @@ __global__ void __launch_bounds__(kLmFinThreads) lm_head_finish(LmArgs a) {
     const uint32_t hi = __shfl_xor((uint32_t)(best >> 32), off, kWave);
     best = lm_max_u64(best, ((unsigned long long)hi << 32) | lo);
   }
+  const float vmax = lm_from_order_bits((uint32_t)(best >> 32));
+  // denoise: the token's probability 1 / sum_t s_t exp(m_t - M) from the
+  // tiles' (max m_t, sum s_t) pairs, merged online (M, the largest m_t, is
+  // the greedy token's logit), independently of the keys above
+  float conf = 0.f;
+  if (a.ms) {
+    float pm = -INFINITY, ps = 0.f;
+    if (live) {
+      const lm_f32x2* pairs = a.ms + (size_t)m * a.ntiles;
+      for (int q0 = 0; q0 < a.ntiles; q0 += 32 * kFinPairs) {
+        lm_f32x2 y[kFinPairs];
+#pragma unroll
+        for (int j = 0; j < kFinPairs; ++j) y[j] = pairs[min(q0 + sub + 32 * j, a.ntiles - 1)];
+        float bm = pm;
+#pragma unroll
+        for (int j = 0; j < kFinPairs; ++j) bm = fmaxf(bm, y[j][0]);
+        float bs = ps * __builtin_amdgcn_exp2f((pm - bm) * kLog2e);
+#pragma unroll
+        for (int j = 0; j < kFinPairs; ++j)  // the clamped repeats are dropped here
+          bs += q0 + sub + 32 * j < a.ntiles ? y[j][1] * __builtin_amdgcn_exp2f((y[j][0] - bm) * kLog2e) : 0.f;
+        pm = bm;
+        ps = bs;
+      }
+    }
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) {
+      const float om = __shfl_xor(pm, off, kWave), os = __shfl_xor(ps, off, kWave);
+      const float mm = fmaxf(pm, om);
+      ps = (pm == -INFINITY ? 0.f : ps * __builtin_amdgcn_exp2f((pm - mm) * kLog2e)) +
+           (om == -INFINITY ? 0.f : os * __builtin_amdgcn_exp2f((om - mm) * kLog2e));
+      pm = mm;
+    }
+    conf = 1.f / ps;
+  }
   if (live && sub == 0) {
     const int32_t tok = (int32_t)(0xffffffffu - (uint32_t)(best & 0xffffffffu));
     gtok[i] = tok;
+    gconf[i] = conf;
     if (a.tokens) a.tokens[m] = tok;
-    if (a.maxv) a.maxv[m] = lm_from_order_bits((uint32_t)(best >> 32));
+    if (a.maxv) a.maxv[m] = vmax;
+    if (a.conf) a.conf[m] = conf;
   }
-  if (!a.drafts) return;
+  if (!a.drafts && !a.masked) return;
   __syncthreads();
   if (tid >= kWave) return;
   const int lane = tid, K = a.R, b = grp;
+  if (a.masked) {
+    // low-confidence remasking: the n most confident masked positions are
+    // unmasked; rank = masked positions ahead in (confidence desc, position)
+    const bool mk = lane < K && a.masked[b * K + lane] != 0;
+    const unsigned long long mbits = __ballot(mk);
+    int rank = 0;
+    const float ci = lane < K ? gconf[lane] : 0.f;
+    for (int j = 0; j < K; ++j) {
+      const float cj = gconf[j];
+      rank += ((mbits >> j) & 1) && (cj > ci || (cj == ci && j < lane));
+    }
+    if (lane < K) a.masked_out[b * K + lane] = mk && rank >= a.n_unmask[b] ? 1 : 0;
+    return;
+  }
   bool miss = false;
   int32_t gt = 0;
   if (lane < K) {
@@ -292,6 +375,9 @@ static size_t lm_workspace(long rows, int vocab) {
   const long ntiles = (vocab + (long)kLmTileN - 1) / kLmTileN;
   return (size_t)rows * ntiles * sizeof(unsigned long long);
 }
+
+// denoise: the keys, then the (max, sum) pairs
+static size_t lm_denoise_workspace(long rows, int vocab) { return 2 * lm_workspace(rows, vocab); }
 
 template <int MT, int KP>
 static orthrus_status lm_launch_tiles(const LmArgs& a, hipStream_t s) {
@@ -390,6 +476,42 @@ extern "C" orthrus_status orthrus_lm_head_greedy_accept(const void* hidden, cons
   a.tokens = ar_tokens;
   a.accept_len = accept_len;
   a.next_token = next_token;
+  a.M = (int)rows;
+  a.H = hidden_size;
+  a.V = vocab;
+  a.R = block_k;
+  return lm_run(a, (hipStream_t)stream, batch);
+}
+
+extern "C" size_t orthrus_lm_head_denoise_workspace_bytes(int32_t rows, int32_t hidden_size, int32_t vocab) {
+  if (!lm_shape_ok(rows, hidden_size, vocab)) return 0;
+  return lm_denoise_workspace(rows, vocab);
+}
+
+extern "C" orthrus_status orthrus_lm_head_denoise_step(const void* hidden, const void* packed_weight,
+                                                       const uint8_t* masked, const int32_t* n_unmask,
+                                                       int32_t* tokens, float* confidence, uint8_t* new_masked,
+                                                       int32_t batch, int32_t block_k, int32_t hidden_size,
+                                                       int32_t vocab, void* workspace, size_t workspace_bytes,
+                                                       void* stream) {
+  if (!hidden || !packed_weight || !masked || !n_unmask || !tokens || !new_masked) return ORTHRUS_ERR_NULL;
+  if (batch < 1 || block_k < 1 || block_k > 32) return ORTHRUS_ERR_SHAPE;
+  const long rows = (long)batch * block_k;
+  if (!lm_shape_ok(rows, hidden_size, vocab)) return ORTHRUS_ERR_SHAPE;
+  if (!lm_aligned(hidden) || !lm_aligned(packed_weight)) return ORTHRUS_ERR_SHAPE;
+  if (!workspace || workspace_bytes < lm_denoise_workspace(rows, vocab) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 7))
+    return ORTHRUS_ERR_WORKSPACE;
+  LmArgs a = {};
+  a.h = (const bf16*)hidden;
+  a.w = (const u32x4*)packed_weight;
+  a.part = (unsigned long long*)workspace;
+  a.ms = (lm_f32x2*)((char*)workspace + lm_workspace(rows, vocab));
+  a.masked = masked;
+  a.n_unmask = n_unmask;
+  a.tokens = tokens;
+  a.conf = confidence;
+  a.masked_out = new_masked;
   a.M = (int)rows;
   a.H = hidden_size;
   a.V = vocab;

@@ -50,6 +50,9 @@ SIGNATURES = {
     "orthrus_lm_head_packed_bytes": (_sz, [_i32, _i32]),
     "orthrus_lm_head_pack_weight": (_i32, [_vp, _vp, _i32, _i32, _vp]),
     "orthrus_lm_head_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "orthrus_lm_head_denoise_workspace_bytes": (_sz, [_i32, _i32, _i32]),
+    "orthrus_lm_head_denoise_step": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz,
+                                            _vp]),
     "orthrus_lm_head_argmax": (_i32, [_vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
     "orthrus_lm_head_greedy_accept": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp]),
     "orthrus_kv_append": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _DESC_P, _vp]),
@@ -358,6 +361,32 @@ def kv_append_layers(layers, page_table, ctx_lens, accept_len, *, new_ctx_lens=N
                                         ctypes.byref(desc), _stream(stream))
     _check(st, "orthrus_kv_append_layers")
     return new_ctx_lens, slots
+
+
+def lm_head_denoise_step(hidden, head, masked, n_unmask, *, new_masked=None, ws=None, stream=None):
+    """orthrus_lm_head_denoise_step over the diffusion view's hidden states
+    [B, K, H] with a PackedLmHead; masked uint8 [B, K], n_unmask int32 [B].
+    Returns (tokens [B, K] int32, confidence [B, K] fp32, new_masked [B, K]
+    uint8; new_masked may be `masked` itself)."""
+    dev = _gpu(hidden, head.packed, masked, n_unmask, new_masked)
+    _lm_check(hidden, head)
+    if hidden.dim() != 3 or masked.dtype != torch.uint8 or tuple(masked.shape) != hidden.shape[:2] \
+            or n_unmask.dtype != torch.int32 or tuple(n_unmask.shape) != hidden.shape[:1]:
+        raise OrthrusError("hidden [B, K, H], masked uint8 [B, K], n_unmask int32 [B]")
+    B, K, H = hidden.shape
+    V = head.vocab
+    tok = torch.empty((B, K), dtype=torch.int32, device=dev)
+    conf = torch.empty((B, K), dtype=torch.float32, device=dev)
+    if new_masked is None:
+        new_masked = torch.empty_like(masked)
+    need = lib().orthrus_lm_head_denoise_workspace_bytes(B * K, H, V)
+    if ws is None:
+        ws = workspace(dev, need, "lm_head_denoise")
+    st = lib().orthrus_lm_head_denoise_step(_ptr(hidden), _ptr(head.packed), _ptr(masked), _ptr(n_unmask),
+                                            _ptr(tok), _ptr(conf), _ptr(new_masked), B, K, H, V, _ptr(ws),
+                                            ws.numel(), _stream(stream))
+    _check(st, "orthrus_lm_head_denoise_step")
+    return tok, conf, new_masked
 
 
 def prefill(q, k, v, k_cache, v_cache, page_table, ctx_lens, prompt_lens, max_prompt, out=None, *,

@@ -227,6 +227,31 @@ orthrus_status orthrus_lm_head_greedy_accept(const void* hidden, const void* pac
                                              int32_t block_k, int32_t hidden_size, int32_t vocab,
                                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of the workspace orthrus_lm_head_denoise_step needs for `rows`
+ * hidden rows: per (row, 128-entry vocabulary tile) one 8-byte argmax key
+ * and one (max, sum) pair of floats.  0 for an invalid shape.  The
+ * workspace needs no initialisation. */
+size_t orthrus_lm_head_denoise_workspace_bytes(int32_t rows, int32_t hidden_size, int32_t vocab);
+
+/* One step of multi-step denoising for the diffusion view (explainer §2.3
+ * names the iterated variant; its re-mask rule is not given there, so this
+ * is low-confidence remasking), fused into the LM head: from the final
+ * hidden states [B, K, H] of the block and the packed weight,
+ *   tokens[b, i]     = greedy token of row i (as orthrus_lm_head_argmax)
+ *   confidence[b, i] = its softmax probability 1 / sum_v exp(logit_v - max)
+ *                      (optional, may be NULL)
+ *   new_masked[b, i] = masked[b, i] unless row i is among the n_unmask[b]
+ *                      most confident rows with masked != 0 (ties to the
+ *                      lower row), which become 0.
+ * The logits are never stored.  masked / new_masked are uint8 [B, K]
+ * (nonzero = still masked) and may alias; n_unmask is int32 [B].
+ * 1 <= K <= 32; shapes as for orthrus_lm_head_argmax. */
+orthrus_status orthrus_lm_head_denoise_step(const void* hidden, const void* packed_weight, const uint8_t* masked,
+                                            const int32_t* n_unmask, int32_t* tokens, float* confidence,
+                                            uint8_t* new_masked, int32_t batch, int32_t block_k,
+                                            int32_t hidden_size, int32_t vocab, void* workspace,
+                                            size_t workspace_bytes, void* stream);
+
 /* Commit the accepted block rows to the shared cache (explainer §2.3: the
  * cache keeps only the committed positions).
  *   n_b = min(max(accept_len[b], 0) + 1, K); for r < n_b and every KV head,

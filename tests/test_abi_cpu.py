@@ -24,7 +24,7 @@ def declared_entry_points():
 
 def test_exports_every_declared_symbol():
     names = declared_entry_points()
-    assert len(names) == 19
+    assert len(names) == 21
     assert set(names) == set(B.SIGNATURES)
     lib = B.lib()
     for n in names:
@@ -174,6 +174,12 @@ def test_lm_head_validation():
     assert lib.orthrus_lm_head_pack_weight(None, A16, 4096, 100, None) == 1
     assert lib.orthrus_lm_head_pack_weight(A16, A16, 4000, 100, None) == 2
     assert lib.orthrus_lm_head_pack_weight(A16, ctypes.c_void_p(4096 * 16 + 4), 4096, 100, None) == 2
+    dn = lib.orthrus_lm_head_denoise_workspace_bytes(64, 4096, 151936)
+    assert dn == 64 * 1187 * 16                                               # key + (max, sum) per tile
+    den = lib.orthrus_lm_head_denoise_step
+    assert den(A16, A16, FAKE, FAKE, FAKE, None, None, 2, 32, 4096, 151936, FAKE, dn, None) == 1
+    assert den(A16, A16, FAKE, FAKE, FAKE, None, FAKE, 2, 33, 4096, 151936, FAKE, dn, None) == 2
+    assert den(A16, A16, FAKE, FAKE, FAKE, None, FAKE, 2, 32, 4096, 151936, FAKE, dn - 1, None) == 4
     acc = lib.orthrus_lm_head_greedy_accept
     assert acc(A16, A16, None, FAKE, FAKE, None, 1, 32, 4096, 151936, FAKE, need, None) == 1
     assert acc(A16, A16, FAKE, FAKE, FAKE, None, 1, 33, 4096, 151936, FAKE, need, None) == 2
