@@ -233,9 +233,11 @@ orthrus_status orthrus_lm_head_greedy_accept(const void* hidden, const void* pac
  * workspace needs no initialisation. */
 size_t orthrus_lm_head_denoise_workspace_bytes(int32_t rows, int32_t hidden_size, int32_t vocab);
 
-/* One step of multi-step denoising for the diffusion view (explainer §2.3
- * names the iterated variant; its re-mask rule is not given there, so this
- * is low-confidence remasking), fused into the LM head: from the final
+/* One step of multi-step denoising for the diffusion view (the agentlenshq
+ * Orthrus-Qwen3 blog, training and implementation details, and the warokai
+ * guide, advanced settings, name the iterated variant; its re-mask rule is
+ * not given, so this is low-confidence remasking), fused into the LM head:
+ * from the final
  * hidden states [B, K, H] of the block and the packed weight,
  *   tokens[b, i]     = greedy token of row i (as orthrus_lm_head_argmax)
  *   confidence[b, i] = its softmax probability 1 / sum_v exp(logit_v - max)
