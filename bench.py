@@ -334,7 +334,7 @@ def cpu_baseline(step, I, seconds):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; --gpus must be 1", "n_gpus": args.gpus}))
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
