@@ -76,11 +76,11 @@ class Step:
         w = I.WORKLOADS[workload]
         self.B, self.K, self.Hq, self.Hkv, self.D = batch, w["block_k"], w["n_q_heads"], w["n_kv_heads"], w["head_dim"]
         self.layers, self.split = layers, split_tokens
-        lens = [ctx] * batch
+        lens = [int(c) for c in ctx] if hasattr(ctx, "__len__") else [ctx] * batch
         table, n_pages = I.make_page_table(lens, self.K, 16, shuffle=True, seed=seed)
         self.page_table = torch.from_numpy(table).to(d)
         self.ctx_lens = torch.tensor(lens, dtype=torch.int32, device=d)
-        self.max_ctx = ctx
+        self.max_ctx = max(lens)
         self.L = []
         for l in range(layers):
             a = I.make_attn_inputs(workload, seed=seed, layer=l, device=d, ctx_lens=lens, batch=batch)
@@ -147,7 +147,7 @@ def time_region(torch, fn, iters, warmup):
     return e0.elapsed_time(e1) / iters  # ms
 
 
-def attn_only_ms(torch, step, mode, use_graph, iters=20, warmup=3, min_calls=16):
+def attn_only_ms(torch, step, mode, use_graph, iters=20, warmup=3, min_calls=16, spread=None):
     """Average time of one block-attention call (main + combine kernels).
     One replay runs at least `min_calls` calls, cycling through the layers
     (the other layers' KV read between two calls on one layer exceeds the
@@ -156,7 +156,17 @@ def attn_only_ms(torch, step, mode, use_graph, iters=20, warmup=3, min_calls=16)
     n = max(step.layers, min_calls)
     fn = lambda: [step.attn(c % step.layers, mode) for c in range(n)]
     rep = capture(torch, fn) if use_graph else fn
-    return time_region(torch, rep, iters, warmup) / n
+    ms = time_region(torch, rep, iters, warmup) / n
+    if spread is not None:   # per-call time of each replay, timed on its own
+        st = torch.cuda.current_stream()
+        for _ in range(iters):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            rep()
+            e1.record(st)
+            torch.cuda.synchronize()
+            spread.append(e0.elapsed_time(e1) / n)
+    return ms
 
 
 TRAFFIC_FILE = os.path.join("diffusion_drafted_verification_amd", "traffic_counters.json")
@@ -184,6 +194,21 @@ def measured_traffic(root, batch, ctx):
         return None
     w = d.get("workloads", {}).get(f"b{batch}_ctx{ctx}")
     return None if w is None else int(w["hbm_bytes_per_call"])
+
+
+def achievable_gbs(torch, ob, mib=1024):
+    """Measured achievable HBM rates over `mib` MiB (4x the Infinity Cache):
+    the library's read-only streaming probe (bytes read / time) and its
+    plain streaming copy (bytes read + written / time)."""
+    n = mib << 20
+    src = torch.ones(n // 4, dtype=torch.int32, device="cuda:0")
+    dst = torch.empty_like(src)
+    sink = torch.empty(4 << 20, dtype=torch.uint8, device="cuda:0")
+    ms_read = time_region(torch, lambda: ob.read_probe(src, sink), 10, 3)
+    ms_copy = time_region(torch, lambda: ob.copy_probe(dst, src), 10, 3)
+    del src, dst, sink
+    torch.cuda.empty_cache()
+    return round(n / (ms_read * 1e-3) / 1e9, 1), round(2 * n / (ms_copy * 1e-3) / 1e9, 1)
 
 
 def sample_accept_timing(torch, ob, I, use_graph, temperature=1.0):
@@ -324,7 +349,19 @@ def cpu_baseline(step, I, seconds):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next(l.split(":", 1)[1].strip() for l in fh if l.startswith("model name"))
+    except Exception:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        blas = ", ".join(sorted({f"{t.get('internal_api')} {t.get('version')}" for t in threadpool_info()}))
+    except Exception:
+        blas = "unknown"
     return {"value": round(kv / el / 1e9, 4), "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model, "blas": blas,
             "sample": f"{reps} x one layer of the step (DIFF + AR block attention over {step.max_ctx} cached "
                       f"tokens x B{step.B}, accept over 32x151936, append) in {el:.1f} s; "
                       f"same shapes and inputs as the GPU step",
@@ -368,10 +405,14 @@ def main():
     value = kv_step / (ms * 1e-3) / 1e9
 
     log("timing attention calls")
-    ms_diff = attn_only_ms(torch, step, ob.DIFF_BIDIR, use_graph)
-    ms_ar = attn_only_ms(torch, step, ob.AR_CAUSAL, use_graph)
+    spread = []
+    ms_diff = attn_only_ms(torch, step, ob.DIFF_BIDIR, use_graph, spread=spread)
+    ms_ar = attn_only_ms(torch, step, ob.AR_CAUSAL, use_graph, spread=spread)
     ms_call = 0.5 * (ms_diff + ms_ar)
     achieved = step.kv_bytes_call / (ms_call * 1e-3) / 1e9
+    pct = lambda q: round(sorted(spread)[min(len(spread) - 1, int(q * len(spread)))] * 1e3, 3)
+    log("achievable read and copy rates")
+    read_gbs, copy_gbs = achievable_gbs(torch, ob)
     flops = 2 * 2 * step.B * step.K * step.Hq * step.D * (args.ctx + step.K)
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -379,7 +420,10 @@ def main():
             "kernel": "block_attn call (attn_stream + attn_combine)", "us_per_call": round(ms_call * 1e3, 3),
             "us_diff": round(ms_diff * 1e3, 3), "us_ar": round(ms_ar * 1e3, 3),
             "bytes_per_call": step.kv_bytes_call, "split_tokens": split,
-            "mfma_tflops": round(flops / (ms_call * 1e-3) / 1e12, 1)}
+            "mfma_tflops": round(flops / (ms_call * 1e-3) / 1e12, 1),
+            "us_per_call_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
+            "achievable_read_gbs": read_gbs, "achievable_copy_gbs": copy_gbs,
+            "frac_of_achievable_read": round(achieved / read_gbs, 4)}
 
     sweep = {}
     if not args.no_sweep:
@@ -396,6 +440,18 @@ def main():
                                 "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
             del s2
             torch.cuda.empty_cache()
+        # the ragged batch: 16 sequences with L_b ~ U[1024, 16384]
+        lens = I.draw_ctx_lens("qwen3_8b_ragged16", seed=0, batch=16)
+        layers = max(2, math.ceil(1.0 * 2**30 / (int(sum(lens)) * 4096)))
+        s2 = Step(ob, I, torch, 16, lens, layers, 0, seed=1)
+        t = 0.5 * (attn_only_ms(torch, s2, ob.DIFF_BIDIR, use_graph, iters=10) +
+                   attn_only_ms(torch, s2, ob.AR_CAUSAL, use_graph, iters=10))
+        gbs = s2.kv_bytes_call / (t * 1e-3) / 1e9
+        sweep["ragged16"] = {"us_per_call": round(t * 1e3, 2), "kv_gbs": round(gbs, 1),
+                             "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "cached_tokens": int(sum(lens)),
+                             "max_ctx": int(max(lens))}
+        del s2
+        torch.cuda.empty_cache()
         step = None
 
     longctx = None

@@ -5,7 +5,8 @@
 // logical positions ctx_len .. ctx_len + n - 1.  One work-group per
 // (sequence, block row); 16-byte copies of the Hkv x D row of K and of V.
 //
-// Also the library's plain streaming copy, used as a measurement probe.
+// Also the library's plain streaming copy and read, used as measurement
+// probes.
 #include "orthrus_device.h"
 #include "orthrus_host.h"
 
@@ -71,6 +72,24 @@ __global__ void __launch_bounds__(256) copy_probe_kernel(u32x4* __restrict__ dst
                                                          size_t n) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   for (size_t k = (size_t)blockIdx.x * blockDim.x + threadIdx.x; k < n; k += stride) dst[k] = src[k];
+}
+
+// read-only stream: every 16-byte unit of src once (16 loads in flight per
+// thread), folded by XOR into one 16-byte value per thread of sink
+constexpr int kReadBlocks = 1024;
+
+__global__ void __launch_bounds__(256) read_probe_kernel(const u32x4* __restrict__ src, size_t n,
+                                                         u32x4* __restrict__ sink) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x * 16;
+  u32x4 acc = {0, 0, 0, 0};
+  for (size_t b = (size_t)blockIdx.x * blockDim.x * 16 + threadIdx.x; b < n; b += stride) {
+    u32x4 v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = b + (size_t)blockDim.x * i < n ? src[b + (size_t)blockDim.x * i] : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc ^= v[i];
+  }
+  sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 
 static orthrus_status append_launch(AppendArgs& a, const orthrus_attn_desc& d, int n_layers,
@@ -158,4 +177,15 @@ extern "C" const char* orthrus_status_str(orthrus_status s) {
     case ORTHRUS_ERR_LAUNCH: return "the HIP runtime reported a launch error";
   }
   return "unknown status";
+}
+
+extern "C" orthrus_status orthrus_read_probe(const void* src, size_t bytes, void* sink, size_t sink_bytes,
+                                             void* stream) {
+  if (!src || !sink) return ORTHRUS_ERR_NULL;
+  if (bytes == 0 || bytes % 16 != 0) return ORTHRUS_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(sink)) & 15) return ORTHRUS_ERR_SHAPE;
+  if (sink_bytes < (size_t)kReadBlocks * 256 * 16) return ORTHRUS_ERR_WORKSPACE;
+  hipLaunchKernelGGL(read_probe_kernel, dim3(kReadBlocks), dim3(256), 0, (hipStream_t)stream, (const u32x4*)src,
+                     bytes / 16, (u32x4*)sink);
+  return hipGetLastError() == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_LAUNCH;
 }

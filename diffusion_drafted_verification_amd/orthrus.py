@@ -60,6 +60,7 @@ SIGNATURES = {
     "orthrus_prefill_workspace_bytes": (_sz, [_DESC_P, _i32]),
     "orthrus_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _DESC_P, _vp, _sz, _vp]),
     "orthrus_copy_probe": (_i32, [_vp, _vp, _sz, _vp]),
+    "orthrus_read_probe": (_i32, [_vp, _sz, _vp, _sz, _vp]),
 }
 
 _lib = None
@@ -421,3 +422,12 @@ def copy_probe(dst, src, stream=None):
     _gpu(dst, src)
     n = src.numel() * src.element_size()
     _check(lib().orthrus_copy_probe(_ptr(dst), _ptr(src), n, _stream(stream)), "orthrus_copy_probe")
+
+
+def read_probe(src, sink, stream=None):
+    """orthrus_read_probe: reads all of src once (sink >= 4 MiB receives
+    meaningless XOR folds)."""
+    _gpu(src, sink)
+    n = src.numel() * src.element_size()
+    m = sink.numel() * sink.element_size()
+    _check(lib().orthrus_read_probe(_ptr(src), n, _ptr(sink), m, _stream(stream)), "orthrus_read_probe")

@@ -315,6 +315,12 @@ orthrus_status orthrus_prefill(const void* q, const void* k, const void* v, void
  * measure the achievable HBM rate; not part of the decode step. */
 orthrus_status orthrus_copy_probe(void* dst, const void* src, size_t bytes, void* stream);
 
+/* Measurement helper: reads `bytes` (a multiple of 16) of src once with
+ * 16-byte loads, 16 in flight per thread, and stores one XOR fold per thread
+ * into sink (sink_bytes >= 4 MiB; its contents are meaningless).  Measures the
+ * achievable HBM read rate; not part of the decode step. */
+orthrus_status orthrus_read_probe(const void* src, size_t bytes, void* sink, size_t sink_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,7 @@ def declared_entry_points():
 
 def test_exports_every_declared_symbol():
     names = declared_entry_points()
-    assert len(names) == 21
+    assert len(names) == 22
     assert set(names) == set(B.SIGNATURES)
     lib = B.lib()
     for n in names:
@@ -121,6 +121,9 @@ def test_accept_and_append_validation():
                                         ctypes.byref(d), None) == 2
     assert lib.orthrus_copy_probe(FAKE, FAKE, 17, None) == 2
     assert lib.orthrus_copy_probe(None, FAKE, 16, None) == 1
+    assert lib.orthrus_read_probe(FAKE, 17, FAKE, 4 << 20, None) == 2
+    assert lib.orthrus_read_probe(FAKE, 16, FAKE, (4 << 20) - 1, None) == 4
+    assert lib.orthrus_read_probe(None, 16, FAKE, 4 << 20, None) == 1
 
 
 def test_sample_accept_validation():

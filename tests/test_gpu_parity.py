@@ -529,6 +529,23 @@ def test_lossless_loop_on_gpu():
     assert noisy == ref[:48]
 
 
+@pytest.mark.parametrize("units", [1, 1000, 1 << 20, (1 << 20) + 7])
+def test_read_probe_reads_every_unit_once(units):
+    """Each 16-byte unit of src is folded into exactly one thread's sink
+    value, so the XOR over the sink equals the XOR over src (padding loads
+    contribute zero)."""
+    say("read probe", units)
+    d = dev()
+    g = torch.Generator(device="cpu").manual_seed(units)
+    src = torch.randint(-2**31, 2**31 - 1, (units, 4), generator=g, dtype=torch.int32)
+    sink = torch.empty(4 << 20, dtype=torch.uint8, device=d)
+    K_().read_probe(src.to(d), sink)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(sink.cpu().view(torch.int32).view(-1, 4).numpy(), axis=0)
+    want = np.bitwise_xor.reduce(src.numpy(), axis=0)
+    assert np.array_equal(got, want)
+
+
 def test_copy_probe():
     say("copy probe")
     d = dev()
