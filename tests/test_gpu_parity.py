@@ -553,3 +553,70 @@ def test_copy_probe():
     dst = torch.empty_like(src)
     K_().copy_probe(dst, src)
     assert torch.equal(dst, src)
+
+
+def test_lossless_loop_with_prefill_and_lm_head_on_gpu():
+    """The same toy dual-view loop with the prompt cached by orthrus_prefill
+    and the consensus taken straight from final hidden states by the packed
+    LM head (orthrus_lm_head_greedy_accept): perfect and noisy drafts commit
+    exactly the tokens of one-token-at-a-time greedy decoding through the
+    same calls.  (fp32 toy attention, bf16 LM head; the projections are
+    test scaffolding.)"""
+    say("lossless loop: prefill + lm head")
+    d = dev()
+    ob = K_()
+    r = torch.Generator().manual_seed(9)
+    V, dm, Hq, Hkv, D, K = 300, 256, 4, 1, 64, 8
+    emb = torch.randn(V, dm, generator=r).to(d)
+    pos = (torch.randn(512, dm, generator=r) * 0.5).to(d)
+    wq = torch.randn(dm, Hq * D, generator=r).to(d) / math.sqrt(dm)
+    wk = torch.randn(dm, Hkv * D, generator=r).to(d) / math.sqrt(dm)
+    wv = torch.randn(dm, Hkv * D, generator=r).to(d) / math.sqrt(dm)
+    wo = torch.randn(Hq * D, dm, generator=r).to(d) / math.sqrt(Hq * D)
+    head = ob.PackedLmHead((torch.randn(V, dm, generator=r) * 3 / math.sqrt(dm)).to(torch.bfloat16).to(d))
+    n_pages = 40
+    table = torch.randperm(n_pages, generator=r).int().view(1, -1).to(d)
+
+    def qkv(tokens, start):
+        x = emb[tokens] + pos[start:start + len(tokens)]
+        T = len(tokens)
+        return (x, (x @ wq).view(1, T, Hq, D).contiguous(), (x @ wk).view(1, T, Hkv, D).contiguous(),
+                (x @ wv).view(1, T, Hkv, D).contiguous())
+
+    def run(prompt, n_new, Kb, drafter):
+        kc = torch.zeros(n_pages, Hkv, 16, D, device=d)
+        vc = torch.zeros_like(kc)
+        ctx = prompt[:-1]
+        S = (len(ctx) + 31) // 32 * 32
+        _, q, k, v = qkv(torch.tensor(ctx + [0] * (S - len(ctx)), device=d), 0)
+        zero = torch.zeros(1, dtype=torch.int32, device=d)
+        _, L = ob.prefill(q, k, v, kc, vc, table, zero, torch.tensor([len(ctx)], dtype=torch.int32, device=d),
+                          len(ctx), max_ctx_len=0)
+        anchor, out, steps = prompt[-1], [], 0
+        while len(out) < n_new:
+            Lh = int(L.item())
+            drafts = drafter(out, Kb)
+            block = torch.tensor([anchor] + drafts[:Kb - 1], device=d)
+            x, q, k, v = qkv(block, Lh)
+            att = ob.block_attn(q, kc, vc, k, v, table, L, AR, max_ctx_len=n_pages * 16 - Kb)
+            hid = (x + att.view(Kb, Hq * D) @ wo).to(torch.bfloat16).view(1, Kb, dm).contiguous()
+            acc, nxt, g = ob.lm_head_greedy_accept(hid, head, torch.tensor([drafts], dtype=torch.int32, device=d))
+            a_h, nxt_h, g_h = int(acc.item()), int(nxt.item()), g[0].tolist()
+            assert 0 <= a_h <= Kb and 0 <= nxt_h < V and all(0 <= t < V for t in g_h)
+            n = min(a_h + 1, Kb)
+            out.extend(g_h[:n])
+            L, _ = ob.kv_append(kc, vc, k, v, table, L, acc, max_ctx_len=n_pages * 16 - Kb)
+            anchor = nxt_h
+            steps += 1
+        return out[:n_new], steps
+
+    prompt = [3, 17, 5, 60, 2, 99, 250, 31, 7, 1, 44, 120, 8, 8, 200, 63, 11, 5, 290, 17, 3, 70, 150, 4, 9, 12,
+              13, 140, 141, 6, 30, 31, 32, 33, 77]
+    ref, s1 = run(prompt, 60, 1, lambda out, Kb: [0] * Kb)
+    assert s1 == 60
+    perfect, s2 = run(prompt, 48, K, lambda out, Kb: (ref + [0] * 64)[len(out):len(out) + Kb])
+    assert perfect == ref[:48] and s2 == 48 // K
+    rnd = np.random.default_rng(2)
+    noisy, _ = run(prompt, 48, K, lambda out, Kb: [t if rnd.random() < 0.7 else int(rnd.integers(V))
+                                                    for t in (ref + [0] * 64)[len(out):len(out) + Kb]])
+    assert noisy == ref[:48]
