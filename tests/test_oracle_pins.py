@@ -17,6 +17,7 @@ overhead).
 
 import itertools
 import math
+import os
 
 import numpy as np
 import pytest
@@ -492,24 +493,41 @@ def test_dual_view_loop_is_lossless(source):
 # workload arithmetic
 # ---------------------------------------------------------------------------
 
-def test_block_kv_overhead_is_4p5_mib():
-    """P-13: one K = 32 block of bf16 K/V over Qwen3-8B's 36 layers (8 KV
-    heads, D 128) is 4,718,592 B = 4.5 MiB, the O(1) overhead the pages
-    quote: the block K/V is a transient K-row buffer, not a second cache."""
+def page_figures():
+    """The figures the pages print (tests/golden/page_figures.txt, each line
+    with its citation)."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "page_figures.txt")
+    out = {}
+    for line in open(path):
+        if line.strip() and not line.startswith("#"):
+            name, value = line.split()[:2]
+            out[name] = float(value)
+    return out
+
+
+def test_block_kv_overhead_is_the_pages_figure():
+    """P-13: one block of K = 32 rows of bf16 K/V over Qwen3-8B's 36 layers
+    (8 KV heads, D 128) is 4,718,592 B, exactly the O(1) overhead the pages
+    print (about 4.5 MiB): the block K/V is a transient K-row buffer, not a
+    second cache."""
     from diffusion_drafted_verification_amd import inputs as I
-    n = I.block_kv_bytes_per_step(32, 36, 8, 128, 2)
-    assert n == 4718592 == int(4.5 * 2**20)
+    f = page_figures()
+    n = I.block_kv_bytes_per_step(int(f["block_k"]), 36, 8, 128, 2)
+    assert n == 4718592 == int(f["kv_overhead_mib"] * 2**20)
 
 
 def test_step_accounting_geometric_prefix():
-    """P-14: every step commits >= 1 token; with the Geometric(mean 11.7)
-    agreement prefix capped at 32, the mean commit is 1 + 11.7 (1 - (11.7/
-    12.7)^31) = 11.78 within sampling error."""
+    """P-14: every step commits >= 1 token; with the Geometric agreement
+    prefix at the pages' mean acceptance length (11.7) capped at 32, the mean
+    commit is 1 + 11.7 (1 - (11.7/12.7)^31) = 11.78 within sampling error."""
     from diffusion_drafted_verification_amd import inputs as I
-    a = I.geometric_prefix(40000, 32, seed=5)
-    n = np.minimum(a + 1, 32)
-    assert n.min() >= 1 and a.max() <= 32
-    expect = 1 + 11.7 * (1 - (11.7 / 12.7) ** 31)
+    f = page_figures()
+    mu, K = f["mean_accept_math500"], int(f["block_k"])
+    assert mu == I.MEAN_ACCEPT
+    a = I.geometric_prefix(40000, K, seed=5)
+    n = np.minimum(a + 1, K)
+    assert n.min() >= 1 and a.max() <= K
+    expect = 1 + mu * (1 - (mu / (mu + 1)) ** (K - 1))
     assert abs(expect - 11.78) < 0.01
     assert abs(n.mean() - expect) < 4 * n.std() / math.sqrt(len(n))
 
