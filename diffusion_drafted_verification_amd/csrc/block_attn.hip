@@ -58,6 +58,7 @@ struct AttnArgs {
   float2* ws_ml;    // [B, Hq, s_max, 32]     (running max in log2 units, row sum)
   int B, K, Hq, Hkv, max_pages, num_pages, max_ctx, split, s_max;
   float c;          // softmax scale * log2(e)
+  int kv_once;      // the call reads each context K/V byte once: nontemporal stream
 };
 
 __device__ __forceinline__ int swap_bits23(int t) {
@@ -725,6 +726,25 @@ __device__ __forceinline__ void dma16(const void* src, char* dst) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
 }
 
+// The same with the nontemporal hint: context K/V that a call reads exactly
+// once streams past the caches (measured on the Qwen3-8B shape: 9 % faster
+// at batch 1, a few % at batch 4 to 16; slower where the data is re-read, as
+// across the chunks of a prefill).
+__device__ __forceinline__ void dma16_nt(const void* src, char* dst) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      (uint32_t)reinterpret_cast<uintptr_t>((ORTHRUS_LDS char*)dst));
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "{m0}"(lds) : "memory");
+}
+
+// a K/V stage load: one instruction either way (the hand-placed vmcnt
+// counts do not change); `once` is uniform (a kernel argument)
+__device__ __forceinline__ void dma16_kv(const void* src, char* dst, int once) {
+  if (once)
+    dma16_nt(src, dst);
+  else
+    dma16(src, dst);
+}
+
 // The same with 4 bytes per lane (lane l writes dst + 4 l).
 __device__ __forceinline__ void dma4(const void* src, char* dst) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane(
@@ -771,7 +791,7 @@ struct DmaPlan {
       const int page = slot == 0 ? pid0 : slot == 1 ? pid1 : slot == 2 ? pid2 : pid3;
       const char* base = (ten == 0 ? a.k_cache : a.v_cache) + (size_t)(page * a.Hkv + g) * (kPage * Lay::ROWB);
       char* dst = st + ten * Lay::TILEB + ii * 1024;
-      dma16(base + voff(wave, lane, k), dst);
+      dma16_kv(base + voff(wave, lane, k), dst, a.kv_once);
     }
   }
 
@@ -810,7 +830,7 @@ struct DmaPlan {
       else if (pos >= L && pos < p_end)
         src = blk + ((size_t)(b * a.K + (pos - L)) * a.Hkv + g) * Lay::ROWB + chunk * 16;
       char* dst = st + ten * Lay::TILEB + ii * 1024;
-      dma16(src, dst);
+      dma16_kv(src, dst, a.kv_once);
     }
   }
 
@@ -1286,11 +1306,10 @@ extern "C" int32_t orthrus_block_attn_split_tokens(const orthrus_attn_desc* desc
   return attn_split_tokens(*desc);
 }
 
-extern "C" orthrus_status orthrus_block_attn(const void* q, const void* k_cache, const void* v_cache,
-                                             const void* k_blk, const void* v_blk,
-                                             const int32_t* page_table, const int32_t* ctx_lens,
-                                             orthrus_mode mode, void* out, const orthrus_attn_desc* desc,
-                                             void* workspace, size_t workspace_bytes, void* stream) {
+orthrus_status orthrus::block_attn_run(const void* q, const void* k_cache, const void* v_cache, const void* k_blk,
+                                       const void* v_blk, const int32_t* page_table, const int32_t* ctx_lens,
+                                       orthrus_mode mode, void* out, const orthrus_attn_desc* desc, void* workspace,
+                                       size_t workspace_bytes, void* stream, bool kv_read_once) {
   orthrus_status st = validate_desc(desc);
   if (st != ORTHRUS_OK) return st;
   if (!q || !k_cache || !v_cache || !k_blk || !v_blk || !page_table || !ctx_lens || !out)
@@ -1330,6 +1349,7 @@ extern "C" orthrus_status orthrus_block_attn(const void* q, const void* k_cache,
   }
   const float scale = d.softmax_scale > 0.f ? d.softmax_scale : 1.f / sqrtf((float)d.head_dim);
   a.c = scale * kLog2e;
+  a.kv_once = kv_read_once ? 1 : 0;
   const int G = d.n_q_heads / d.n_kv_heads;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
@@ -1338,4 +1358,14 @@ extern "C" orthrus_status orthrus_block_attn(const void* q, const void* k_cache,
   else
     e = d.head_dim == 128 ? dispatch_g<float, 128>(a, G, mode, s) : dispatch_g<float, 64>(a, G, mode, s);
   return e == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_LAUNCH;
+}
+
+extern "C" orthrus_status orthrus_block_attn(const void* q, const void* k_cache, const void* v_cache,
+                                             const void* k_blk, const void* v_blk,
+                                             const int32_t* page_table, const int32_t* ctx_lens,
+                                             orthrus_mode mode, void* out, const orthrus_attn_desc* desc,
+                                             void* workspace, size_t workspace_bytes, void* stream) {
+  // a decode call reads every cached K/V byte once
+  return block_attn_run(q, k_cache, v_cache, k_blk, v_blk, page_table, ctx_lens, mode, out, desc, workspace,
+                        workspace_bytes, stream, true);
 }

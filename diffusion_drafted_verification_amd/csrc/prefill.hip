@@ -169,6 +169,7 @@ extern "C" orthrus_status orthrus_prefill(const void* q, const void* k, const vo
   if (hipGetLastError() != hipSuccess) return ORTHRUS_ERR_LAUNCH;
   hipLaunchKernelGGL(prefill_kv_write, dim3((unsigned)((long)a.B * S)), dim3(256), 0, s, a);
   if (hipGetLastError() != hipSuccess) return ORTHRUS_ERR_LAUNCH;
-  return orthrus_block_attn(q, k_cache, v_cache, k, v, a.vtable, a.vctx, ORTHRUS_AR_CAUSAL, out, &vd,
-                            w.attn_bytes ? ws + w.off_attn : nullptr, w.attn_bytes, stream);
+  // the chunks re-read the prompt's K/V through the caches: ordinary loads
+  return block_attn_run(q, k_cache, v_cache, k, v, a.vtable, a.vctx, ORTHRUS_AR_CAUSAL, out, &vd,
+                        w.attn_bytes ? ws + w.off_attn : nullptr, w.attn_bytes, stream, false);
 }
