@@ -440,18 +440,25 @@ def main():
                                 "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
             del s2
             torch.cuda.empty_cache()
-        # the ragged batch: 16 sequences with L_b ~ U[1024, 16384]
+        # the ragged batch: 16 sequences with L_b ~ U[1024, 16384], with the
+        # balanced split (chosen on the device from the lengths) and, for
+        # comparison, the automatic split sized from the longest context
         lens = I.draw_ctx_lens("qwen3_8b_ragged16", seed=0, batch=16)
         layers = max(2, math.ceil(1.0 * 2**30 / (int(sum(lens)) * 4096)))
-        s2 = Step(ob, I, torch, 16, lens, layers, 0, seed=1)
-        t = 0.5 * (attn_only_ms(torch, s2, ob.DIFF_BIDIR, use_graph, iters=10) +
-                   attn_only_ms(torch, s2, ob.AR_CAUSAL, use_graph, iters=10))
-        gbs = s2.kv_bytes_call / (t * 1e-3) / 1e9
+        ts = {}
+        for name, sp in (("balanced", ob.SPLIT_BALANCED), ("automatic", 0)):
+            s2 = Step(ob, I, torch, 16, lens, layers, sp, seed=1)
+            ts[name] = 0.5 * (attn_only_ms(torch, s2, ob.DIFF_BIDIR, use_graph, iters=10) +
+                              attn_only_ms(torch, s2, ob.AR_CAUSAL, use_graph, iters=10))
+            kv = s2.kv_bytes_call
+            del s2
+            torch.cuda.empty_cache()
+        t = ts["balanced"]
+        gbs = kv / (t * 1e-3) / 1e9
         sweep["ragged16"] = {"us_per_call": round(t * 1e3, 2), "kv_gbs": round(gbs, 1),
                              "frac_hbm": round(gbs / HBM_PEAK_GBS, 4), "cached_tokens": int(sum(lens)),
-                             "max_ctx": int(max(lens))}
-        del s2
-        torch.cuda.empty_cache()
+                             "max_ctx": int(max(lens)), "split": "balanced",
+                             "automatic_split_us_per_call": round(ts["automatic"] * 1e3, 2)}
         step = None
 
     longctx = None

@@ -59,7 +59,123 @@ struct AttnArgs {
   int B, K, Hq, Hkv, max_pages, num_pages, max_ctx, split, s_max;
   float c;          // softmax scale * log2(e)
   int kv_once;      // the call reads each context K/V byte once: nontemporal stream
+  // balanced split (streaming path): the split length is chosen per call from
+  // ctx_lens so that one round of Q work-groups per KV head covers the batch;
+  // the partial of unit (b, s) sits in slot P_b + s of its KV head's U slots
+  int bal, Q, U;
+  int2* ws_rec;     // balanced split: (splits, first slot) per sequence, for attn_combine
+  int s_hint;       // split count that sizes the combine's lane groups (a
+                    // batch with every length at max_ctx has this many)
 };
+
+constexpr int kBalMinTiles = 256 / kTile;        // shortest balanced split: 256 positions
+constexpr int kBalMaxTiles = kMaxSplit / kTile;  // longest: kMaxSplit
+
+// Inclusive prefix sum over the 64 lanes of a wave on the DPP paths (no LDS
+// round trip): shifts by 1, 2, 4, 8 within each 16-lane row, then the row
+// totals through the broadcasts of lanes 15 and 31.
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
+__device__ __forceinline__ int wave_total(int x) { return __builtin_amdgcn_readlane(wave_incl_scan(x), kWave - 1); }
+
+// ceil(T / t) for 0 <= T < 2^18 and 4 <= t <= 128 with rt ~ 1 / t (within a
+// few ulp): the float estimate is floor(T / t) or one less, and two exact
+// integer tests raise it to the ceiling.
+__device__ __forceinline__ int ceil_div_small(int T, int t, float rt) {
+  int q = (int)((float)T * rt);
+  q += q * t < T;
+  q += q * t < T;
+  return q;
+}
+
+// Splits of a sequence of T 64-position tiles at t tiles per split (an empty
+// context still makes one unit: the block keys).
+__device__ __forceinline__ int bal_splits(int T, int t, float rt) { return T > 0 ? ceil_div_small(T, t, rt) : 1; }
+
+// The balanced split of one call, computed identically by every wave that
+// needs it (lane l holds sequence B - 1 - l, so B <= 64): the smallest t in
+// [kBalMinTiles, kBalMaxTiles] with sum_b ceil(T_b / t) <= Q, or kBalMaxTiles
+// when none is.  t_guess (the split of a batch with every length at max_ctx)
+// is tested first: with equal lengths it is the answer.  Returns t; n and P
+// are this lane's split count and the exclusive prefix of the counts.
+struct BalSplit {
+  int t, n, P, L;
+};
+
+__device__ BalSplit balanced_split(const AttnArgs& a, int lane, int t_guess) {
+  const bool act = lane < a.B;
+  int L = act ? a.ctx_lens[a.B - 1 - lane] : 0;
+  L = L < 0 ? 0 : (L > a.max_ctx ? a.max_ctx : L);
+  const int T = (L + kTile - 1) / kTile;
+  auto count = [&](int t) { return wave_total(act ? bal_splits(T, t, __builtin_amdgcn_rcpf((float)t)) : 0); };
+  // Every length is at most max_ctx, so count(t_guess) <= Q unless t_guess
+  // is kBalMaxTiles, and the answer is at most t_guess.
+  int lo = kBalMinTiles, hi = t_guess;
+  if (hi == kBalMaxTiles && count(hi) > a.Q) {
+    lo = hi;
+  } else {
+    if (hi > lo) {
+      if (count(hi - 1) > a.Q) lo = hi;
+      else --hi;
+    }
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (count(mid) <= a.Q) hi = mid;
+      else lo = mid + 1;
+    }
+  }
+  BalSplit r;
+  r.t = lo;
+  r.n = act ? bal_splits(T, lo, __builtin_amdgcn_rcpf((float)lo)) : 0;
+  r.P = wave_incl_scan(r.n) - r.n;
+  r.L = L;
+  return r;
+}
+
+// Unit j of one KV head under the balanced split.  Units are numbered split
+// index first, then sequence (B - 1 down to 0): with equal lengths this is
+// the fixed split's work-group order.
+struct BalUnit {
+  int b, s, n, L, split, slot;
+  bool live;
+};
+
+__device__ BalUnit balanced_unit(const AttnArgs& a, int j, int lane) {
+  const BalSplit q = balanced_split(a, lane, a.split / kTile);
+  BalUnit u;
+  u.live = false;
+  int C = 0, s = 0;
+  uint64_t mask = 0;
+  for (;;) {
+    mask = __ballot(q.n > s);
+    const int c = __popcll(mask);
+    if (c == 0) return u;  // j is past the last unit
+    if (j < C + c) break;
+    C += c;
+    ++s;
+  }
+  const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+  const uint64_t sel = __ballot(q.n > s && rank == j - C);
+  const int ls = __ffsll((unsigned long long)sel) - 1;
+  u.b = a.B - 1 - ls;
+  u.s = s;
+  u.n = __builtin_amdgcn_readlane(q.n, ls);
+  u.L = __builtin_amdgcn_readlane(q.L, ls);
+  u.slot = __builtin_amdgcn_readlane(q.P, ls) + s;
+  u.split = q.t * kTile;
+  // a unit outside the batch or its partial slots would be an arithmetic
+  // slip: drop it rather than write out of range
+  u.live = ls >= 0 && ls < a.B && u.slot < a.U && u.s < u.n;
+  return u;
+}
 
 __device__ __forceinline__ int swap_bits23(int t) {
   return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1);
@@ -571,7 +687,7 @@ __global__ void __launch_bounds__(256) attn_combine(AttnArgs a) {
 // merge with xor shuffles: no LDS, no barrier.  A work-group covers 4 waves x
 // 64 / (SG D/8) consecutive rows of one (b, g); block id = chunk * (B Hkv) +
 // b Hkv + g as for attn_combine.
-template <int D, int SG, int SPL>
+template <int D, int SG, int SPL, bool BAL>
 __global__ void __launch_bounds__(256) attn_combine_bf16(AttnArgs a) {
   constexpr int C = D / 8;               // lanes per row and split group
   constexpr int RPW = kWave / (C * SG);  // rows per wave
@@ -586,11 +702,23 @@ __global__ void __launch_bounds__(256) attn_combine_bf16(AttnArgs a) {
   const bool live = rl < G * a.K;
   const int w = live ? rl / a.K : 0, i = live ? rl % a.K : 0;
   const int h = g * G + w;
-  int L = a.ctx_lens[b];
-  L = L < 0 ? 0 : (L > a.max_ctx ? a.max_ctx : L);
-  const int S_b = L > 0 ? (L + a.split - 1) / a.split : 1;
+  int S_b;
+  size_t base, sstride;  // row of split 0, rows between splits
+  if constexpr (BAL) {
+    const int2 rec = a.ws_rec[b];  // written by the attention kernel
+    S_b = rec.x;
+    const int P = rec.y;
+    if (P < 0 || P + S_b > a.U) return;  // an arithmetic slip: never read past the slots
+    base = ((size_t)(g * a.U + P) * G + w) * kRows + i;
+    sstride = (size_t)G * kRows;
+  } else {
+    int L = a.ctx_lens[b];
+    L = L < 0 ? 0 : (L > a.max_ctx ? a.max_ctx : L);
+    S_b = L > 0 ? (L + a.split - 1) / a.split : 1;
+    base = (size_t)(b * a.Hq + h) * a.s_max * kRows + i;
+    sstride = kRows;
+  }
   if (S_b <= 1) return;  // uniform over the work-group
-  const size_t base = (size_t)(b * a.Hq + h) * a.s_max * kRows + i;
 
   float M = -INFINITY, den = 0.f;
   float acc[8];
@@ -602,7 +730,7 @@ __global__ void __launch_bounds__(256) attn_combine_bf16(AttnArgs a) {
 #pragma unroll
     for (int j = 0; j < SPL; ++j) {
       const int sp = s0 + SG * j;
-      const size_t r = base + (size_t)(sp < S_b ? sp : 0) * kRows;
+      const size_t r = base + (size_t)(sp < S_b ? sp : 0) * sstride;
       ml[j] = a.ws_ml[r];
       x[j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(a.ws_p) + r * D * 2 + c * 16);
       if (sp >= S_b) ml[j].x = -INFINITY;
@@ -662,10 +790,13 @@ static hipError_t launch_combine(const AttnArgs& a, hipStream_t stream) {
       constexpr int SG = decltype(sg_tag)::value;
       constexpr int RPB = 4 * (kWave / ((D / 8) * SG));
       const int chunks = (rows + RPB - 1) / RPB;
-      hipLaunchKernelGGL((attn_combine_bf16<D, SG, 8>), dim3(chunks * a.B * a.Hkv), dim3(256), 0, stream, a);
+      if (a.bal)
+        hipLaunchKernelGGL((attn_combine_bf16<D, SG, 8, true>), dim3(chunks * a.B * a.Hkv), dim3(256), 0, stream, a);
+      else
+        hipLaunchKernelGGL((attn_combine_bf16<D, SG, 8, false>), dim3(chunks * a.B * a.Hkv), dim3(256), 0, stream, a);
     };
-    if (a.s_max > 16) go2(std::integral_constant<int, 4>());
-    else if (a.s_max > 8) go2(std::integral_constant<int, 2>());
+    if (a.s_hint > 16) go2(std::integral_constant<int, 4>());
+    else if (a.s_hint > 8) go2(std::integral_constant<int, 2>());
     else go2(std::integral_constant<int, 1>());
     return hipGetLastError();
   }
@@ -870,12 +1001,11 @@ __device__ __forceinline__ void barrier_no_fence() {
   asm volatile("" ::: "memory");
 }
 
-template <int D, int G, int MODE>
+template <int D, int G, int MODE, bool BAL>
 __global__ void __launch_bounds__(2 * kWave * G) attn_stream(AttnArgs a) {
   typedef StreamLayout<D> Lay;
   typedef DmaPlan<D, 2 * G> Plan;
   constexpr int NW = 2 * G;
-  constexpr int NT = kWave * NW;
   constexpr int KS = D / 16;
   constexpr int MB = D / 32;
   static_assert(4 * (MB / 2) * 16 * kWave * 4 <= Lay::STAGE, "exchange area: four waves per stage buffer");
@@ -889,13 +1019,16 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_stream(AttnArgs a) {
 
   const int BH = a.B * a.Hkv;
   const int bg = blockIdx.x % BH;
-  const int s = blockIdx.x / BH;
-  // sequences in reverse order: where later sequences carry longer contexts
-  // (the chunks of a prompt prefill) the longest work-groups start first
-  const int b = a.B - 1 - bg / a.Hkv, g = bg % a.Hkv;
+  const int g = bg % a.Hkv;
+  // the fixed split's unit: sequences in reverse order, so where later
+  // sequences carry longer contexts (the chunks of a prompt prefill) the
+  // longest work-groups start first.  Under the balanced split it is the unit
+  // of a batch whose lengths all equal max_ctx: its page ids are loaded
+  // before the lengths are known and kept when the guess holds.
+  int s = blockIdx.x / BH;
+  int b = a.B - 1 - bg / a.Hkv;
+  int split = a.split;
   const int tid = threadIdx.x;
-  const int p_begin = s * a.split;
-  const int page_base = p_begin >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
   const int i = lane & 31, hi = lane >> 5;
   const int hw = wave % G, sub = wave / G;
@@ -906,31 +1039,57 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_stream(AttnArgs a) {
   // by vmcnt), so the K/V DMA of those stages starts after one load latency.
   // The split's page table and the query rows reach LDS by DMA as well: no
   // load the compiler tracks with vmcnt is in flight behind the K/V stream,
-  // so the hand-placed vmcnt waits below stay exact.
+  // so the hand-placed vmcnt waits below stay exact (the balanced split's
+  // length loads are consumed before the first DMA).
   typedef const __attribute__((address_space(4))) int cint;
   constexpr int NPRO = (kRing - 1) * kTile / kPage;  // page ids of the prologue stages
-  int L = ((cint*)a.ctx_lens)[b];
-  const bool ids_ok = page_base + NPRO <= a.max_pages;
+  int L = BAL ? 0 : ((cint*)a.ctx_lens)[b];  // balanced: every length is read below
+  int page_base = (s * split) >> 4;
+  bool ids_ok;
   int pid[NPRO];  // raw; checked where used
-  if (ids_ok) {
-    cint* row = (cint*)(a.page_table + (size_t)b * a.max_pages + page_base);
+  auto load_ids = [&]() {
+    ids_ok = page_base + NPRO <= a.max_pages;
+    if (ids_ok) {
+      cint* row = (cint*)(a.page_table + (size_t)b * a.max_pages + page_base);
 #pragma unroll
-    for (int j = 0; j < NPRO; ++j) pid[j] = row[j];
+      for (int j = 0; j < NPRO; ++j) pid[j] = row[j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < NPRO; ++j) pid[j] = 0;
+    }
+  };
+  load_ids();
+  int S_b;
+  size_t part;        // this wave's partial slot (rows part * kRows ...)
+  int first_slot = 0;  // balanced split: slot of the sequence's split 0
+  if constexpr (BAL) {
+    const BalUnit u = balanced_unit(a, blockIdx.x / a.Hkv, lane);
+    if (!u.live) return;  // uniform over the work-group
+    const bool same = u.b == b && u.s * u.split == s * split;
+    b = u.b;
+    s = u.s;
+    split = u.split;
+    page_base = (s * split) >> 4;
+    if (!same) load_ids();
+    L = u.L;
+    S_b = u.n;
+    part = (size_t)(g * a.U + u.slot) * G + hw;
+    first_slot = u.slot - u.s;
   } else {
-#pragma unroll
-    for (int j = 0; j < NPRO; ++j) pid[j] = 0;
+    L = L < 0 ? 0 : (L > a.max_ctx ? a.max_ctx : L);
+    S_b = L > 0 ? (L + split - 1) / split : 1;
+    if (s >= S_b) return;
+    part = (size_t)(b * a.Hq + h) * a.s_max + s;
   }
-  L = L < 0 ? 0 : (L > a.max_ctx ? a.max_ctx : L);
+  const int p_begin = s * split;
   const int N = L + a.K;
-  const int S_b = L > 0 ? (L + a.split - 1) / a.split : 1;
-  if (s >= S_b) return;
-  const int p_end = s == S_b - 1 ? N : p_begin + a.split;
+  const int p_end = s == S_b - 1 ? N : p_begin + split;
   const int ntiles = (p_end - p_begin + kTile - 1) / kTile;
 
   // the split's page ids -> LDS (raw; checked where they are used); ids past
   // the table row are never used
   {
-    const int npt = min(a.split / kPage, a.max_pages - page_base);
+    const int npt = min(split / kPage, a.max_pages - page_base);
     const int* prow = a.page_table + (size_t)b * a.max_pages + page_base;
     for (int k = wave; k * kWave < npt; k += NW) {
       const int x = k * kWave + lane;
@@ -1119,6 +1278,10 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_stream(AttnArgs a) {
   // the same expression (sub 0's values first), so they agree bit for bit.
   wait_vmcnt<0>();
   __syncthreads();  // the ring is free
+  if constexpr (BAL) {
+    // sequence b's split count and first partial slot, for the combine
+    if (s == 0 && g == 0 && tid == 0) a.ws_rec[b] = make_int2(S_b, first_slot);
+  }
   constexpr int MH = MB / 2;
   constexpr int NC = MH * 4;                 // 16-byte chunks a lane hands over
   constexpr int XSH = NC == 8 ? 1 : 2;       // chunk swizzle: 16 lanes of a
@@ -1182,8 +1345,7 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_stream(AttnArgs a) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (bf16)x) | ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)y) << 16);
   };
   char* const row_out = S_b == 1 ? a.out + ((size_t)(b * a.K + i) * a.Hq + h) * D * 2
-                                 : reinterpret_cast<char*>(a.ws_p) +
-                                       (((size_t)(b * a.Hq + h) * a.s_max + s) * kRows + i) * D * 2;
+                                 : reinterpret_cast<char*>(a.ws_p) + (part * kRows + i) * D * 2;
 #pragma unroll
   for (int mm = 0; mm < MH; ++mm) {
     uint32_t pk[4][2];
@@ -1203,7 +1365,7 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_stream(AttnArgs a) {
   // ---- split context: the row statistics (max in log2 units, sum) go with
   // the normalised partial (bf16, O / l) to slot s; attn_combine merges.
   if (S_b > 1 && sub == 0 && hi == 0)
-    a.ws_ml[((size_t)(b * a.Hq + h) * a.s_max + s) * kRows + i] = make_float2(row_m, row_l);
+    a.ws_ml[part * kRows + i] = make_float2(row_m, row_l);
 }
 
 // ---------------------------------------------------------------------------
@@ -1240,21 +1402,74 @@ static bool attn_stream_path(const orthrus_attn_desc& d) {
   return d.dtype == ORTHRUS_BF16 && d.n_q_heads / d.n_kv_heads <= 4;
 }
 
+// How one call divides the cached context among work-groups.  With the
+// balanced split requested, several sequences (at most 64, fewer than 256
+// (b, KV head) pairs) and the streaming kernel, the split length is chosen on the device
+// from ctx_lens (balanced_split): the smallest multiple of 64 positions in
+// [256, kMaxSplit] that makes at most Q = ceil(256 / Hkv) units per KV head,
+// so one round of about 256 work-groups covers a ragged batch as evenly as
+// the 64-position tiles allow.  The host knows only max_ctx_len: its split
+// is the one a batch of that length everywhere gets, the partial slots are
+// sized for the worst case, and the grid has U slots per KV head (units past
+// the batch's last one exit at once).  Otherwise the split is fixed by the
+// host (attn_split_tokens).
+struct SplitPlan {
+  bool bal;
+  int split, s_max, s_hint, Q, U;
+};
+
+static SplitPlan attn_plan(const orthrus_attn_desc& d) {
+  SplitPlan p{false, attn_split_tokens(d), 0, 0, 0, 0};
+  p.s_max = attn_s_max(d, p.split);
+  p.s_hint = p.s_max;
+  if (d.split_tokens != ORTHRUS_SPLIT_BALANCED || !attn_stream_path(d) || d.batch < 2 || d.batch > 64 ||
+      d.batch * d.n_kv_heads >= 256 || d.max_ctx_len >= (1 << 24))  // tile counts stay exact in fp32
+    return p;
+  const long Tm = ((long)d.max_ctx_len + kTile - 1) / kTile;
+  if (ceil_div(Tm, kBalMinTiles) <= 1) return p;  // no sequence can be split
+  const int Q = ceil_div(256, d.n_kv_heads);
+  auto count = [&](int t) { return (long)d.batch * (Tm > 0 ? ceil_div(Tm, t) : 1); };
+  int lo = kBalMinTiles, hi = kBalMaxTiles;
+  if (count(hi) > Q) {
+    lo = hi;
+  } else {
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (count(mid) <= Q) hi = mid;
+      else lo = mid + 1;
+    }
+  }
+  p.bal = true;
+  p.split = lo * kTile;
+  p.Q = Q;
+  p.U = (int)(count(kBalMaxTiles) > Q ? count(kBalMaxTiles) : Q);
+  const int most = ceil_div(Tm, kBalMinTiles);
+  p.s_max = most < p.U - d.batch + 1 ? most : p.U - d.batch + 1;
+  p.s_hint = ceil_div(Tm, lo);
+  return p;
+}
+
 struct WsLayout {
-  size_t bytes, off_ml;
+  size_t bytes, off_ml, off_rec;
 };
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // partial outputs (bf16 on the streaming path, fp32 otherwise), then the row
-// statistics
+// statistics: [B, Hq, s_max, 32] rows under a fixed split, [Hkv, U, G, 32]
+// under the balanced one, which adds one (splits, first slot) pair per
+// sequence
 static WsLayout attn_ws_layout(const orthrus_attn_desc& d) {
-  WsLayout w{0, 0};
-  const int s_max = attn_s_max(d, attn_split_tokens(d));
-  if (s_max <= 1) return w;
-  const size_t rows = (size_t)d.batch * d.n_q_heads * s_max * kRows;
+  WsLayout w{0, 0, 0};
+  const SplitPlan p = attn_plan(d);
+  if (p.s_max <= 1) return w;
+  const size_t rows = p.bal ? (size_t)d.n_q_heads * p.U * kRows : (size_t)d.batch * d.n_q_heads * p.s_max * kRows;
   w.off_ml = align256(rows * d.head_dim * (attn_stream_path(d) ? 2 : 4));
   w.bytes = w.off_ml + rows * sizeof(float2);
+  if (p.bal) {
+    w.off_rec = align256(w.bytes);
+    w.bytes = w.off_rec + (size_t)d.batch * sizeof(int2);
+  }
   return w;
 }
 
@@ -1262,15 +1477,19 @@ size_t attn_workspace_bytes(const orthrus_attn_desc& d) { return attn_ws_layout(
 
 template <typename T, int D, int G>
 static hipError_t launch_attn(const AttnArgs& a, int mode, hipStream_t stream) {
-  const int grid = a.s_max * a.B * a.Hkv;
+  const int grid = a.bal ? a.U * a.Hkv : a.s_max * a.B * a.Hkv;
   // bf16 with up to 4 query heads per KV head: the LDS-DMA streaming kernel;
   // otherwise the register-staged kernel
   constexpr bool stream_path = sizeof(T) == 2 && G <= 4;
   if constexpr (stream_path) {
-    if (mode == ORTHRUS_DIFF_BIDIR)
-      hipLaunchKernelGGL((attn_stream<D, G, ORTHRUS_DIFF_BIDIR>), dim3(grid), dim3(2 * kWave * G), 0, stream, a);
-    else
-      hipLaunchKernelGGL((attn_stream<D, G, ORTHRUS_AR_CAUSAL>), dim3(grid), dim3(2 * kWave * G), 0, stream, a);
+    const dim3 blk(2 * kWave * G);
+    if (mode == ORTHRUS_DIFF_BIDIR) {
+      if (a.bal) hipLaunchKernelGGL((attn_stream<D, G, ORTHRUS_DIFF_BIDIR, true>), dim3(grid), blk, 0, stream, a);
+      else hipLaunchKernelGGL((attn_stream<D, G, ORTHRUS_DIFF_BIDIR, false>), dim3(grid), blk, 0, stream, a);
+    } else {
+      if (a.bal) hipLaunchKernelGGL((attn_stream<D, G, ORTHRUS_AR_CAUSAL, true>), dim3(grid), blk, 0, stream, a);
+      else hipLaunchKernelGGL((attn_stream<D, G, ORTHRUS_AR_CAUSAL, false>), dim3(grid), blk, 0, stream, a);
+    }
   } else {
     if (mode == ORTHRUS_DIFF_BIDIR)
       hipLaunchKernelGGL((attn_main<T, D, G, ORTHRUS_DIFF_BIDIR>), dim3(grid), dim3(2 * kWave * G), 0, stream, a);
@@ -1303,7 +1522,7 @@ extern "C" size_t orthrus_block_attn_workspace_bytes(const orthrus_attn_desc* de
 
 extern "C" int32_t orthrus_block_attn_split_tokens(const orthrus_attn_desc* desc) {
   if (validate_desc(desc) != ORTHRUS_OK) return 0;
-  return attn_split_tokens(*desc);
+  return attn_plan(*desc).split;
 }
 
 orthrus_status orthrus::block_attn_run(const void* q, const void* k_cache, const void* v_cache, const void* k_blk,
@@ -1336,16 +1555,23 @@ orthrus_status orthrus::block_attn_run(const void* q, const void* k_cache, const
   a.max_pages = d.max_pages_per_seq;
   a.num_pages = d.num_pages;
   a.max_ctx = d.max_ctx_len;
-  a.split = attn_split_tokens(d);
-  a.s_max = attn_s_max(d, a.split);
+  const SplitPlan plan = attn_plan(d);
+  a.split = plan.split;
+  a.s_max = plan.s_max;
+  a.bal = plan.bal ? 1 : 0;
+  a.Q = plan.Q;
+  a.U = plan.U;
+  a.s_hint = plan.s_hint;
   a.ws_o = nullptr;
   a.ws_p = nullptr;
   a.ws_ml = nullptr;
+  a.ws_rec = nullptr;
   if (need > 0) {
     const WsLayout wl = attn_ws_layout(d);
     if (attn_stream_path(d)) a.ws_p = (bf16*)workspace;
     else a.ws_o = (float*)workspace;
     a.ws_ml = (float2*)((char*)workspace + wl.off_ml);
+    if (plan.bal) a.ws_rec = (int2*)((char*)workspace + wl.off_rec);
   }
   const float scale = d.softmax_scale > 0.f ? d.softmax_scale : 1.f / sqrtf((float)d.head_dim);
   a.c = scale * kLog2e;

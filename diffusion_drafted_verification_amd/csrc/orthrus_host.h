@@ -22,7 +22,9 @@ inline orthrus_status validate_desc(const orthrus_attn_desc* d) {
   if (d->dtype != ORTHRUS_BF16 && d->dtype != ORTHRUS_F32) return ORTHRUS_ERR_UNSUPPORTED;
   if ((long)d->max_ctx_len + d->block_k > (long)d->max_pages_per_seq * d->page_size) return ORTHRUS_ERR_SHAPE;
   if ((long)d->max_ctx_len + d->block_k > (1L << 30)) return ORTHRUS_ERR_SHAPE;
-  if (d->split_tokens < 0 || d->split_tokens % 64 != 0 || d->split_tokens > 8192) return ORTHRUS_ERR_SHAPE;
+  if (d->split_tokens != ORTHRUS_SPLIT_BALANCED &&
+      (d->split_tokens < 0 || d->split_tokens % 64 != 0 || d->split_tokens > 8192))
+    return ORTHRUS_ERR_SHAPE;
   if (d->softmax_scale != d->softmax_scale) return ORTHRUS_ERR_SHAPE;  // NaN
   return ORTHRUS_OK;
 }

@@ -18,6 +18,7 @@ DIFF_BIDIR = 0
 AR_CAUSAL = 1
 BF16 = 0
 F32 = 1
+SPLIT_BALANCED = -1   # split_tokens: chosen on the device from ctx_lens (ragged batches)
 PAGE_SIZE = 16
 
 LIB_NAME = "liborthrus_gfx950.so"

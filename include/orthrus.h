@@ -64,6 +64,16 @@ typedef enum {
 
 typedef enum { ORTHRUS_BF16 = 0, ORTHRUS_F32 = 1 } orthrus_dtype;
 
+/* split_tokens value that asks for the balanced split of a ragged batch.
+ * With bf16 storage, Hq / Hkv <= 4, 2 <= batch <= 64, batch * Hkv < 256 and
+ * max_ctx_len < 2^24, the kernels read every ctx_lens[b] and take the
+ * smallest split (a multiple of 64 in [256, 8192]) that gives at most
+ * ceil(256 / Hkv) work-groups per KV head, so that one round of about 256
+ * work-groups covers the batch as evenly as 64-position tiles allow; the
+ * launch and the workspace are sized for the worst case that max_ctx_len
+ * allows.  Outside those bounds it means 0 (automatic). */
+#define ORTHRUS_SPLIT_BALANCED (-1)
+
 typedef enum {
   ORTHRUS_OK = 0,
   ORTHRUS_ERR_NULL = 1,        /* a required pointer is NULL                          */
@@ -85,8 +95,11 @@ typedef enum {
  *                       max_ctx_len + K <= max_pages_per_seq * P
  *   dtype               storage type of q, out, caches and block K/V
  *   softmax_scale       <= 0 selects 1 / sqrt(D)
- *   split_tokens        context positions per work-group; 0 = automatic,
- *                       otherwise a multiple of 64 in [64, 8192]          */
+ *   split_tokens        context positions per work-group: a multiple of 64
+ *                       in [64, 8192]; 0 = automatic (sized from
+ *                       max_ctx_len, the best choice when the lengths are
+ *                       equal); ORTHRUS_SPLIT_BALANCED = chosen on the device
+ *                       from ctx_lens (for ragged batches, see below)      */
 typedef struct {
   int32_t batch;
   int32_t block_k;
@@ -112,7 +125,9 @@ const char* orthrus_status_str(orthrus_status s);
 size_t orthrus_block_attn_workspace_bytes(const orthrus_attn_desc* desc);
 
 /* Context positions per work-group that orthrus_block_attn will use for
- * `desc` (the split length), or 0 for an invalid descriptor. */
+ * `desc` (the split length), or 0 for an invalid descriptor.  Under the
+ * balanced split it is the split of a batch whose lengths all equal
+ * max_ctx_len; the kernels choose the actual one from ctx_lens. */
 int32_t orthrus_block_attn_split_tokens(const orthrus_attn_desc* desc);
 
 /* Block attention of one decode step (explainer §2.1-§2.3).

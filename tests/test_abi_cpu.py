@@ -64,6 +64,7 @@ def attn(desc, ws=None, ws_bytes=0, mode=0, null_q=False):
     (dict(block_k=0), 2), (dict(block_k=33), 2), (dict(batch=0), 2), (dict(n_q_heads=12), 2),
     (dict(n_q_heads=48), 3), (dict(head_dim=96), 3), (dict(page_size=32), 3), (dict(dtype=7), 3),
     (dict(max_ctx_len=8193 - 32 + 16 * 514), 2), (dict(split_tokens=100), 2), (dict(split_tokens=16384), 2),
+    (dict(split_tokens=-2), 2),
     (dict(num_pages=0), 2), (dict(max_ctx_len=-1), 2)])
 def test_block_attn_rejects_bad_descriptors(kw, status):
     assert attn(good_desc(**kw)) == status
@@ -99,6 +100,49 @@ def test_split_and_workspace_arithmetic():
     assert lib.orthrus_block_attn_workspace_bytes(ctypes.byref(d32)) == rows32 * 128 * 4 + rows32 * 8
     d1 = good_desc(split_tokens=8192, max_ctx_len=100)      # one split: no workspace
     assert lib.orthrus_block_attn_workspace_bytes(ctypes.byref(d1)) == 0
+
+
+@pytest.mark.parametrize("batch,hq,hkv,max_ctx,split,units", [
+    (2, 32, 8, 8192, 512, 32),      # equal lengths keep the fixed split's shape: 2 x 16 splits per KV head
+    (4, 32, 8, 8192, 1024, 32),
+    (16, 32, 8, 8192, 4096, 32),
+    (3, 32, 8, 8192, 832, 32),      # 3 x 10 splits fit one 32-slot round (a 768 split would need 33)
+    (16, 32, 8, 16379, 8192, 32),   # the ragged batch's bound: its lengths pick the split on the device
+    (16, 32, 8, 200000, 8192, 400),  # 25 splits of 8192 each: more than one round
+    (64, 8, 2, 8192, 4096, 128)])
+def test_balanced_split_plan(batch, hq, hkv, max_ctx, split, units):
+    """Balanced split requested, several sequences, bf16 with Hq/Hkv <= 4:
+    the split that a batch with every length at max_ctx gets (the smallest
+    multiple of 64 in [256, 8192] giving at most ceil(256 / Hkv) work-groups
+    per KV head), and partial slots for `units` work-groups per KV head."""
+    lib = B.lib()
+    pages = -(-(max_ctx + 32) // 16)
+    d = good_desc(batch=batch, n_q_heads=hq, n_kv_heads=hkv, max_ctx_len=max_ctx, max_pages_per_seq=pages,
+                  num_pages=pages, split_tokens=B.SPLIT_BALANCED)
+    assert lib.orthrus_block_attn_split_tokens(ctypes.byref(d)) == split
+    rows = hq * units * 32
+    up = lambda x: -(-x // 256) * 256
+    # bf16 partials, row statistics, then one (splits, first slot) pair per sequence
+    assert lib.orthrus_block_attn_workspace_bytes(ctypes.byref(d)) == up(up(rows * 128 * 2) + rows * 8) + batch * 8
+
+
+def test_fixed_split_outside_the_balanced_case():
+    lib = B.lib()
+    up = lambda x: -(-x // 256) * 256
+    bal = B.SPLIT_BALANCED
+    for kw, split in [(dict(batch=16, split_tokens=1024), 1024),   # explicit split
+                      (dict(batch=16, split_tokens=0), 4096),      # automatic
+                      (dict(batch=3, split_tokens=0), 768),        # automatic: 11 splits (33 per KV head)
+                      (dict(batch=16, split_tokens=bal, dtype=1), 4096),   # fp32: no balanced split
+                      (dict(batch=1, split_tokens=bal), 256),      # one sequence
+                      (dict(batch=65, n_q_heads=8, n_kv_heads=2, max_ctx_len=4096, split_tokens=bal), 2048),
+                      (dict(batch=32, max_ctx_len=8192, split_tokens=bal), 4096)]:   # 256 (b, KV head) pairs
+        d = good_desc(**kw)
+        assert lib.orthrus_block_attn_split_tokens(ctypes.byref(d)) == split
+        s_max = -(-d.max_ctx_len // split)
+        rows = d.batch * d.n_q_heads * s_max * 32
+        want = 0 if s_max <= 1 else up(rows * 128 * (2 if d.dtype == 0 else 4)) + rows * 8
+        assert lib.orthrus_block_attn_workspace_bytes(ctypes.byref(d)) == want
 
 
 def test_accept_and_append_validation():

@@ -1,5 +1,6 @@
 """Every entry point works under HIP graph capture: a step that calls them all
-(block attention in both modes with split contexts, greedy and sampled
+(block attention in both modes with split contexts and with the balanced
+split, greedy and sampled
 consensus, the LM head's accept and denoising update, KV append into all
 layers, and a prompt prefill) is captured once and replayed three times,
 with unrelated eager work and synchronisations between the replays; every
@@ -44,11 +45,14 @@ def test_graph_replays_match_eager():
         for mode in (ob.DIFF_BIDIR, ob.AR_CAUSAL):
             outs.append(ob.block_attn(inp.q, inp.k_cache, inp.v_cache, inp.k_blk, inp.v_blk, inp.page_table,
                                       inp.ctx_lens, mode, max_ctx_len=3000, split_tokens=256))
-        outs += list(ob.greedy_accept(logits, drafts))
+        outs.append(ob.block_attn(inp.q, inp.k_cache, inp.v_cache, inp.k_blk, inp.v_blk, inp.page_table,
+                                  inp.ctx_lens, ob.AR_CAUSAL, max_ctx_len=3000, split_tokens=ob.SPLIT_BALANCED))
+        acc = ob.greedy_accept(logits, drafts)
+        outs += list(acc)
         outs += list(ob.sample_accept(ar, dr, sdrafts, ua, ur, 1.0))
         outs += list(ob.lm_head_greedy_accept(hid, head, drafts))
         outs += list(ob.lm_head_denoise_step(hid, head, masked, nun))
-        outs += list(ob.kv_append_layers(layers, inp.page_table, inp.ctx_lens, outs[2]))
+        outs += list(ob.kv_append_layers(layers, inp.page_table, inp.ctx_lens, acc[0]))
         outs += list(ob.prefill(pre["q"], pre["k"], pre["v"], pkc, pvc, pre["page_table"], pre["ctx_lens"],
                                 pre["prompt_lens"], pre["max_prompt"], max_ctx_len=pre["max_ctx_len"]))
         return outs

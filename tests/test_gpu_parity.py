@@ -174,7 +174,7 @@ def random_attn_case(n):
     B = int(rng.integers(1, 5))
     K = int(rng.choice([1, 2, 5, 16, 31, 32]))
     L = [int(rng.choice([0, 1, 15, 16, 17, 63, 64, 65, rng.integers(0, 2600)])) for _ in range(B)]
-    split = int(rng.choice([0, 0, 64, 128, 192, 256, 512, 4096]))
+    split = int(rng.choice([0, -1, 64, 128, 192, 256, 512, 4096]))   # -1: the balanced split
     extra = int(rng.integers(0, 40))
     table, n_pages = I.make_page_table(L, K, 16, shuffle=True, seed=n, extra_pages=extra)
     slack = int(rng.integers(0, 3))  # spare table columns: a looser max_ctx bound
@@ -226,6 +226,59 @@ def test_gpu_invariants():
     pt2 = torch.where(pt >= 0, relabel[pt.clamp(min=0)], pt).int()
     moved = I.AttnInputs(inp.q, kc2, vc2, inp.k_blk, inp.v_blk, pt2, inp.ctx_lens, inp.max_ctx_len)
     assert torch.equal(run(moved, AR), a1)
+
+
+def balanced_case(B, Hkv, lens, seed, max_ctx=None, G=4, D=128):
+    table, n_pages = I.make_page_table(lens, 32, 16, shuffle=True, seed=seed)
+    if max_ctx is not None:   # a looser bound: more table columns, all unused
+        cols = -(-(max_ctx + 32) // 16)
+        table = np.concatenate([table, np.full((B, cols - table.shape[1]), -1, dtype=np.int32)], axis=1)
+    g = torch.Generator().manual_seed(seed)
+    r = lambda *shape: torch.randn(*shape, generator=g).to(torch.bfloat16)
+    return I.AttnInputs(r(B, 32, G * Hkv, D), r(n_pages, Hkv, 16, D), r(n_pages, Hkv, 16, D), r(B, 32, Hkv, D),
+                        r(B, 32, Hkv, D), torch.from_numpy(table), torch.tensor(lens, dtype=torch.int32),
+                        max(lens) if max_ctx is None else max_ctx)
+
+
+@pytest.mark.parametrize("B,Hkv,lens,max_ctx", [
+    (2, 8, [0, 5000], None),                       # one sequence takes almost every unit
+    (3, 8, [5000, 0, 0], None),                    # most units exit at once
+    (5, 8, [1, 63, 64, 65, 4100], None),           # page and tile boundaries
+    (16, 8, [3000, 17, 0, 2500, 64, 999, 1800, 4096, 5, 1500, 3333, 128, 2047, 2049, 700, 1], None),
+    (40, 4, [(n * 997) % 2100 for n in range(40)], None),
+    (2, 8, [3000, 1200], 17 * 8192)])              # a loose bound: more slots than one round (U > Q)
+def test_balanced_split_ragged(B, Hkv, lens, max_ctx):
+    """Balanced split of a ragged batch (the split length is chosen on the
+    device from the context lengths): every sequence meets the bar against
+    the oracle, and a repeat gives identical bits."""
+    say("balanced split", B, Hkv, lens, max_ctx)
+    inp = balanced_case(B, Hkv, lens, seed=B * 31 + Hkv, max_ctx=max_ctx)
+    pick = None if B <= 5 else sorted({int(np.argmax(lens)), int(np.argmin(lens)), 3, B - 1})
+    bal = K_().SPLIT_BALANCED
+    for mode in (DIFF, AR):
+        out, _ = check_attn(inp, mode, split=bal, batches=pick, max_ctx=inp.max_ctx_len)
+        g = inp.to(dev())
+        again = K_().block_attn(g.q, g.k_cache, g.v_cache, g.k_blk, g.v_blk, g.page_table, g.ctx_lens, mode,
+                                max_ctx_len=inp.max_ctx_len, split_tokens=bal)
+        assert torch.equal(out, again)
+
+
+@pytest.mark.parametrize("B,L", [(2, 8192), (3, 8192), (4, 3000), (16, 2048)])
+def test_balanced_split_equal_lengths_match_fixed(B, L):
+    """With every length at max_ctx the balanced split chooses the host's
+    split and the same work-group order: identical bits to that split given
+    explicitly (only the partial slots' layout differs)."""
+    say("balanced vs fixed", B, L)
+    d = dev()
+    ob = K_()
+    x = I.make_attn_inputs("qwen3_8b_8k", ctx_lens=[L] * B, batch=B).to(d)
+    split = ob.lib().orthrus_block_attn_split_tokens(
+        ctypes.byref(ob.make_desc(x.q, x.k_cache, x.page_table, x.max_ctx_len, None, ob.SPLIT_BALANCED)))
+    assert split % 64 == 0
+    for mode in (DIFF, AR):
+        run = lambda sp: ob.block_attn(x.q, x.k_cache, x.v_cache, x.k_blk, x.v_blk, x.page_table, x.ctx_lens,
+                                       mode, max_ctx_len=x.max_ctx_len, split_tokens=sp)
+        assert torch.equal(run(ob.SPLIT_BALANCED), run(split))
 
 
 def test_ragged_with_loose_max_ctx():
