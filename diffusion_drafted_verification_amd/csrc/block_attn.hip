@@ -29,7 +29,11 @@
 //     partial (bf16 O / l on the streaming path, fp32 O otherwise, plus the
 //     row's max and sum) and a combine kernel merges them; the work-group
 //     order puts all splits of one (b, g) on one XCD so the partials stay in
-//     that XCD's L2.
+//     that XCD's L2;
+//   * the split length is fixed by the host from max_ctx_len, or, for a
+//     ragged batch that asks for it, chosen on the device from ctx_lens so
+//     that one round of about 256 work-groups covers the batch evenly (a
+//     separate instantiation of the streaming kernel and its combine).
 #include <type_traits>
 
 #include "orthrus_device.h"

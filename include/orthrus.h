@@ -120,7 +120,8 @@ const char* orthrus_status_str(orthrus_status s);
 
 /* Bytes of caller-provided scratch orthrus_block_attn needs for `desc`
  * (split-context partial results: bf16 for bf16 storage with Hq/Hkv <= 4,
- * fp32 otherwise, plus fp32 row statistics).  0 for an invalid descriptor or
+ * fp32 otherwise, plus fp32 row statistics; under the balanced split also one
+ * (splits, first slot) pair per sequence).  0 for an invalid descriptor or
  * when no sequence can be split.  The workspace needs no initialisation. */
 size_t orthrus_block_attn_workspace_bytes(const orthrus_attn_desc* desc);
 
