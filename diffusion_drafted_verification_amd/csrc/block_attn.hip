@@ -72,7 +72,7 @@ struct AttnArgs {
                     // batch with every length at max_ctx has this many)
 };
 
-constexpr int kBalMinTiles = 256 / kTile;        // shortest balanced split: 256 positions
+constexpr int kBalMinTiles = 320 / kTile;        // shortest automatic or balanced split: 320 positions
 constexpr int kBalMaxTiles = kMaxSplit / kTile;  // longest: kMaxSplit
 
 // Inclusive prefix sum over the 64 lanes of a wave on the DPP paths (no LDS
@@ -1378,21 +1378,37 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_stream(AttnArgs a) {
 
 static int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 
+// Work-groups per KV head of one round on 256 CUs.
+static int attn_round_slots(const orthrus_attn_desc& d) { return ceil_div(256, d.n_kv_heads); }
+
 int attn_split_tokens(const orthrus_attn_desc& d) {
   // splits partition the cached context (the last split also takes the K
   // block keys)
   const long Lm = d.max_ctx_len > 0 ? d.max_ctx_len : 1;
   const long l64 = ((Lm + kTile - 1) / kTile) * kTile;
   if (d.split_tokens > 0) return (int)(d.split_tokens < l64 ? d.split_tokens : l64);
-  // one work-group per CU and (b, g, split) unit at the longest context (one
-  // round of 256 work-groups), splits of 256..4096 positions
-  const int units = d.batch * d.n_kv_heads;
-  const int s_target = units >= 256 ? 1 : ceil_div(256, units);
-  long split = ((ceil_div(Lm, s_target) + kTile - 1) / kTile) * kTile;
-  if (split < 256) split = 256;
-  if (split > 4096) split = 4096;
-  if (split > l64) split = l64;
-  return (int)split;
+  // Automatic: the shortest split (in 64-position tiles, kBalMinTiles ..
+  // kBalMaxTiles) that keeps a batch of max_ctx_len contexts within one round
+  // of about 256 work-groups, B ceil(L / split) <= ceil(256 / Hkv) per KV
+  // head; the longest split when even that needs more.  Measured on MI355X
+  // (Qwen3-8B heads, 8192 tokens): at B1 320-position splits (208
+  // work-groups of 5 stages) beat 256 (256 of 4) by 6-9 %, and a second,
+  // partial round costs 25-35 % (B3, B6); from B8 up the full round is best.
+  const long Tm = (Lm + kTile - 1) / kTile;
+  const int Q = attn_round_slots(d);
+  auto count = [&](int t) { return (long)d.batch * ceil_div(Tm, t); };
+  int lo = kBalMinTiles, hi = kBalMaxTiles;
+  if (count(hi) > Q) {
+    lo = hi;
+  } else {
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (count(mid) <= Q) hi = mid;
+      else lo = mid + 1;
+    }
+  }
+  const long split = (long)lo * kTile;
+  return (int)(split < l64 ? split : l64);
 }
 
 static int attn_s_max(const orthrus_attn_desc& d, int split) {
@@ -1431,25 +1447,15 @@ static SplitPlan attn_plan(const orthrus_attn_desc& d) {
     return p;
   const long Tm = ((long)d.max_ctx_len + kTile - 1) / kTile;
   if (ceil_div(Tm, kBalMinTiles) <= 1) return p;  // no sequence can be split
-  const int Q = ceil_div(256, d.n_kv_heads);
-  auto count = [&](int t) { return (long)d.batch * (Tm > 0 ? ceil_div(Tm, t) : 1); };
-  int lo = kBalMinTiles, hi = kBalMaxTiles;
-  if (count(hi) > Q) {
-    lo = hi;
-  } else {
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (count(mid) <= Q) hi = mid;
-      else lo = mid + 1;
-    }
-  }
+  // the automatic split is the balanced one of a batch whose lengths all
+  // equal max_ctx_len: the device's search starts from it
   p.bal = true;
-  p.split = lo * kTile;
-  p.Q = Q;
-  p.U = (int)(count(kBalMaxTiles) > Q ? count(kBalMaxTiles) : Q);
+  p.Q = attn_round_slots(d);
+  const long most_units = (long)d.batch * ceil_div(Tm, kBalMaxTiles);
+  p.U = (int)(most_units > p.Q ? most_units : p.Q);
   const int most = ceil_div(Tm, kBalMinTiles);
   p.s_max = most < p.U - d.batch + 1 ? most : p.U - d.batch + 1;
-  p.s_hint = ceil_div(Tm, lo);
+  p.s_hint = ceil_div(Tm, p.split / kTile);
   return p;
 }
 

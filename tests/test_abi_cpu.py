@@ -103,7 +103,7 @@ def test_split_and_workspace_arithmetic():
 
 
 @pytest.mark.parametrize("batch,hq,hkv,max_ctx,split,units", [
-    (2, 32, 8, 8192, 512, 32),      # equal lengths keep the fixed split's shape: 2 x 16 splits per KV head
+    (2, 32, 8, 8192, 512, 32),      # 2 x 16 splits fill one 32-slot round per KV head
     (4, 32, 8, 8192, 1024, 32),
     (16, 32, 8, 8192, 4096, 32),
     (3, 32, 8, 8192, 832, 32),      # 3 x 10 splits fit one 32-slot round (a 768 split would need 33)
@@ -113,7 +113,7 @@ def test_split_and_workspace_arithmetic():
 def test_balanced_split_plan(batch, hq, hkv, max_ctx, split, units):
     """Balanced split requested, several sequences, bf16 with Hq/Hkv <= 4:
     the split that a batch with every length at max_ctx gets (the smallest
-    multiple of 64 in [256, 8192] giving at most ceil(256 / Hkv) work-groups
+    multiple of 64 in [320, 8192] giving at most ceil(256 / Hkv) work-groups
     per KV head), and partial slots for `units` work-groups per KV head."""
     lib = B.lib()
     pages = -(-(max_ctx + 32) // 16)
@@ -131,12 +131,14 @@ def test_fixed_split_outside_the_balanced_case():
     up = lambda x: -(-x // 256) * 256
     bal = B.SPLIT_BALANCED
     for kw, split in [(dict(batch=16, split_tokens=1024), 1024),   # explicit split
-                      (dict(batch=16, split_tokens=0), 4096),      # automatic
-                      (dict(batch=3, split_tokens=0), 768),        # automatic: 11 splits (33 per KV head)
+                      (dict(batch=16, split_tokens=0), 4096),      # automatic: 2 splits each, one round
+                      (dict(batch=3, split_tokens=0), 832),        # 10 splits each (11 would need 33 slots)
+                      (dict(batch=1, split_tokens=0), 320),        # the shortest automatic split
                       (dict(batch=16, split_tokens=bal, dtype=1), 4096),   # fp32: no balanced split
-                      (dict(batch=1, split_tokens=bal), 256),      # one sequence
-                      (dict(batch=65, n_q_heads=8, n_kv_heads=2, max_ctx_len=4096, split_tokens=bal), 2048),
-                      (dict(batch=32, max_ctx_len=8192, split_tokens=bal), 4096)]:   # 256 (b, KV head) pairs
+                      (dict(batch=1, split_tokens=bal), 320),      # one sequence
+                      (dict(batch=65, n_q_heads=8, n_kv_heads=2, max_ctx_len=4096, split_tokens=bal), 4096),
+                      (dict(batch=32, max_ctx_len=8192, split_tokens=bal), 8192),   # one split each
+                      (dict(batch=4, max_ctx_len=1000000, max_pages_per_seq=62503, num_pages=62503), 8192)]:
         d = good_desc(**kw)
         assert lib.orthrus_block_attn_split_tokens(ctypes.byref(d)) == split
         s_max = -(-d.max_ctx_len // split)
