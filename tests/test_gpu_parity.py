@@ -109,6 +109,40 @@ def test_qwen3_8b_32k_sampled():
         check_attn(inp, mode, batches=[0, 3], heads=[0, 5, 31])
 
 
+def test_qwen3_8b_32k_every_layer_of_a_step():
+    """The long-context step (B4, 32768 cached tokens, 36 layers with their own
+    seeded K/V): every layer, both views, meets the bar against the oracle on
+    sequences 0 and 3 and one KV head group per layer (the group rotates over
+    the 8 KV heads).  The oracle gets that head group's slice of the inputs,
+    since heads are independent."""
+    d = dev()
+    ob = K_()
+    for l in range(36):
+        x = I.make_attn_inputs("qwen3_8b_32k_b4", layer=l, device=d)
+        Hkv = x.k_cache.shape[1]
+        G = x.q.shape[2] // Hkv
+        g = l % Hkv
+        hs = slice(g * G, (g + 1) * G)
+        vmax = max(x.v_cache.float().abs().max().item(), x.v_blk.float().abs().max().item())
+        sub = [t.cpu() for t in (x.q[:, :, hs], x.k_cache[:, g:g + 1], x.v_cache[:, g:g + 1],
+                                 x.k_blk[:, :, g:g + 1], x.v_blk[:, :, g:g + 1], x.page_table, x.ctx_lens)]
+        for mode in (DIFF, AR):
+            say("32k step layer", l, "KV head", g, "mode", mode)
+            out = ob.block_attn(x.q, x.k_cache, x.v_cache, x.k_blk, x.v_blk, x.page_table, x.ctx_lens, mode,
+                                max_ctx_len=x.max_ctx_len)
+            torch.cuda.synchronize()
+            ref = O.block_attn(*sub, mode, batches=[0, 3])[[0, 3]]
+            got = out[[0, 3]][:, :, hs].float().cpu().numpy().astype(np.float64)
+            err = np.abs(got - ref)
+            assert np.isfinite(got).all()
+            assert err.max() <= TOL * vmax, (l, mode, err.max(), vmax)
+            for bi in range(2):
+                for hh in range(G):
+                    assert err[bi, :, hh].max() <= TOL * np.abs(ref[bi, :, hh]).max(), (l, mode, bi, hh)
+        del x, out
+        torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("mode", [DIFF, AR])
 @pytest.mark.parametrize("split", [64, 128, 256, 1024, 8192])
 def test_split_lengths_agree(mode, split):
