@@ -33,6 +33,10 @@
 // one tile (its row groups) are placed on one XCD so that, when the rows need
 // several groups, the later groups find the weight tile in that XCD's L2.
 //
+// lm_head_wide (more than 64 hidden rows): each wave streams two 32-row
+// tiles, so every hidden fragment read from LDS feeds two MFMAs; a
+// work-group covers 256 vocabulary rows and 64 hidden rows.
+//
 // lm_head_finish: one work-group per group of rows reduces each row's tile
 // keys (32 threads per row, all loads issued before the reduction), writes the tokens
 // and, for the accept entry point, compares them with the drafts (wave
@@ -237,6 +241,186 @@ __global__ void __launch_bounds__(kLmThreads) lm_head_tiles(LmArgs a) {
   }
 }
 
+// Wide variant for more hidden rows: each wave streams TWO 32-row weight
+// tiles and multiplies both by every hidden fragment it reads from LDS, so a
+// 16-byte LDS read feeds two MFMAs (the LDS traffic per product halves) and
+// MT row tiles of 32 share each weight fragment.  A work-group covers
+// kLmWideN = 256 vocabulary rows (one key per row and 256-row tile: the
+// launch sets ntiles accordingly).  At MT = 2, KP = 64 the weight double
+// buffer, the hidden staging and the four accumulator tiles fit two waves
+// per SIMD (the launch bound asks for that occupancy).
+constexpr int kLmWideN = kLmWaves * 64;
+
+// 16-byte chunk c of hidden row r in the LDS phase buffer: an XOR swizzle
+// that keeps the 32 rows x 2 chunks of one MFMA operand read on distinct
+// bank groups for 16 consecutive rows
+template <int CH>
+__device__ __forceinline__ int lm_swz(int r, int c) {
+  if constexpr (CH >= 16) return r * CH + (c ^ (r & 15));
+  else return r * CH + (c ^ ((r >> 1) & (CH - 1)));
+}
+
+template <int MT, int KP, bool NT>
+__global__ void __launch_bounds__(kLmThreads, 2) lm_head_wide(LmArgs a) {
+  constexpr int CH = KP / 8;     // 16-byte chunks of one hidden row per phase
+  constexpr int NW = KP / 16;    // MFMA k-steps per phase
+  constexpr int ROWS = MT * 32;  // hidden rows per work-group
+  constexpr int NA = ROWS * CH / kLmThreads;
+  static_assert(CH == 8 || CH == 16, "phase shape");
+  static_assert((ROWS * CH) % kLmThreads == 0, "phase shape");
+  __shared__ u32x4 hs[2][ROWS * CH];
+  __shared__ float rv[kLmWaves][32];
+  __shared__ int ri[kLmWaves][32];
+  __shared__ float rs[kLmWaves][32];
+
+  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+  const int tile = (local / a.mgroups) * 8 + xcd, mg = local % a.mgroups;
+  if (tile >= a.ntiles) return;  // uniform: padding of the tile count to 8
+
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int g = lane >> 5, c32 = lane & 31;
+  const int m0 = mg * ROWS;
+  const int nbase = tile * kLmWideN + wave * 64;  // vocabulary row of this wave's first tile
+  const int steps = a.H / 16;
+  const int last32 = (a.V - 1) / 32;
+  // 32-row tiles past the padded vocabulary read the last tile (in bounds);
+  // their rows are past V and are dropped below
+  const u32x4* wt0 = a.w + (size_t)min(nbase / 32, last32) * steps * kWave + lane;
+  const u32x4* wt1 = a.w + (size_t)min(nbase / 32 + 1, last32) * steps * kWave + lane;
+  const int P = a.H / KP;
+
+  auto load_w = [&](int p, u32x4(&wv)[2][NW]) {
+    const size_t o = (size_t)p * NW * kWave;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      wv[0][i] = NT ? __builtin_nontemporal_load(wt0 + o + i * kWave) : wt0[o + i * kWave];
+      wv[1][i] = NT ? __builtin_nontemporal_load(wt1 + o + i * kWave) : wt1[o + i * kWave];
+    }
+  };
+  auto load_h = [&](int p, u32x4(&hv)[NA]) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int q = tid + kLmThreads * i, r = q / CH, c = q % CH;
+      const int m = min(m0 + r, a.M - 1);  // rows past M repeat the last row and are dropped
+      hv[i] = ld16(a.h + (size_t)m * a.H + (size_t)p * KP + 8 * c);
+    }
+  };
+  auto store_h = [&](int buf, const u32x4(&hv)[NA]) {
+#pragma unroll
+    for (int i = 0; i < NA; ++i) {
+      const int q = tid + kLmThreads * i, r = q / CH, c = q % CH;
+      hs[buf][lm_swz<CH>(r, c)] = hv[i];
+    }
+  };
+  auto compute = [&](int buf, const u32x4(&wv)[2][NW], f32x16(&acc)[2][MT]) {
+#pragma unroll
+    for (int s = 0; s < NW; ++s) {
+      const bf16x8 a0 = __builtin_bit_cast(bf16x8, wv[0][s]);
+      const bf16x8 a1 = __builtin_bit_cast(bf16x8, wv[1][s]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, hs[buf][lm_swz<CH>(mt * 32 + c32, 2 * s + g)]);
+        acc[0][mt] = mfma_step(a0, bv, acc[0][mt]);
+        acc[1][mt] = mfma_step(a1, bv, acc[1][mt]);
+      }
+    }
+  };
+
+  f32x16 acc[2][MT];
+#pragma unroll
+  for (int v = 0; v < 2; ++v)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[v][mt][e] = 0.f;
+
+  u32x4 hv[NA], w0[2][NW], w1[2][NW];
+  load_h(0, hv);
+  load_w(0, w0);
+  store_h(0, hv);
+  __syncthreads();
+  for (int p = 0; p < P; p += 2) {
+    if (p + 1 < P) {
+      load_h(p + 1, hv);
+      load_w(p + 1, w1);
+    }
+    compute(0, w0, acc);
+    if (p + 1 < P) store_h(1, hv);
+    __syncthreads();
+    if (p + 1 >= P) break;
+    if (p + 2 < P) {
+      load_h(p + 2, hv);
+      load_w(p + 2, w0);
+    }
+    compute(1, w1, acc);
+    if (p + 2 < P) store_h(0, hv);
+    __syncthreads();
+  }
+
+  // argmax of the 256-row tile per hidden row: lane (c32, g) holds, for the
+  // wave's tile v, vocabulary rows nbase + 32 v + 8 (e / 4) + 4 g + e % 4;
+  // rows grow with v then e, so a strict compare keeps the lowest index
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int v = 0; v < 2; ++v)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int nn = nbase + 32 * v + 8 * (e >> 2) + 4 * g + (e & 3);
+        if (nn < a.V && acc[v][mt][e] > bv) {
+          bv = acc[v][mt][e];
+          bi = nn;
+        }
+      }
+    lm_keep(bv, bi, __shfl_xor(bv, 32, kWave), __shfl_xor(bi, 32, kWave));
+    float se = 0.f;
+    if (a.ms) {
+#pragma unroll
+      for (int v = 0; v < 2; ++v)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int nn = nbase + 32 * v + 8 * (e >> 2) + 4 * g + (e & 3);
+          se += nn < a.V ? __builtin_amdgcn_exp2f((acc[v][mt][e] - bv) * kLog2e) : 0.f;
+        }
+      se += __shfl_xor(se, 32, kWave);
+    }
+    if (g == 0) {
+      rv[wave][c32] = bv;
+      ri[wave][c32] = bi;
+      rs[wave][c32] = se;
+    }
+    __syncthreads();
+    if (wave == 0 && g == 0) {
+      const float wmax0 = bv;
+#pragma unroll
+      for (int w = 1; w < kLmWaves; ++w) lm_keep(bv, bi, rv[w][c32], ri[w][c32]);
+      const int m = m0 + mt * 32 + c32;
+      if (m < a.M) {
+        a.part[(size_t)m * a.ntiles + tile] =
+            ((unsigned long long)lm_order_bits(bv) << 32) | (unsigned long long)(0xffffffffu - (uint32_t)bi);
+        if (a.ms) {
+          float tot = se * __builtin_amdgcn_exp2f((wmax0 - bv) * kLog2e);
+#pragma unroll
+          for (int w = 1; w < kLmWaves; ++w)
+            tot += rv[w][c32] == -INFINITY ? 0.f : rs[w][c32] * __builtin_amdgcn_exp2f((rv[w][c32] - bv) * kLog2e);
+          a.ms[(size_t)m * a.ntiles + tile] = lm_f32x2{bv, tot};
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int MT, int KP, bool NT>
+static orthrus_status lm_launch_wide(LmArgs& a, hipStream_t s) {
+  a.ntiles = (a.V + kLmWideN - 1) / kLmWideN;
+  const long tiles8 = ((long)a.ntiles + 7) / 8 * 8;
+  hipLaunchKernelGGL((lm_head_wide<MT, KP, NT>), dim3((unsigned)(tiles8 * a.mgroups)), dim3(kLmThreads), 0, s, a);
+  return hipGetLastError() == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_LAUNCH;
+}
+
 __device__ __forceinline__ unsigned long long lm_max_u64(unsigned long long x, unsigned long long y) {
   return x > y ? x : y;
 }
@@ -390,13 +574,14 @@ static orthrus_status lm_launch_tiles(const LmArgs& a, hipStream_t s) {
 static orthrus_status lm_run(LmArgs a, hipStream_t s, int finish_groups) {
   a.ntiles = (a.V + kLmTileN - 1) / kLmTileN;
   orthrus_status st;
-  // 32 rows: one group, deep phases.  More rows: 64-row groups with shallow
-  // phases (two waves per SIMD fit); the groups of one weight tile run on
-  // one XCD, so after the first group the tile mostly comes from L2 (measured
-  // faster than 128-row groups, whose registers allow one wave per SIMD)
-  // One row group reads every weight byte once: nontemporal loads (measured
-  // about 15 % faster at 32 and 64 rows).  Several row groups share each
-  // weight tile through L2: ordinary loads.
+  // 32 rows: one group, deep phases.  64 rows: one 64-row group with shallow
+  // phases (two waves per SIMD fit).  One row group reads every weight byte
+  // once: nontemporal loads (measured about 15 % faster at 32 and 64 rows).
+  // More rows: 64-row groups of the wide kernel (two weight tiles per wave,
+  // 64-element phases; measured 5 % faster at 128 rows and 10 % at 512 than
+  // 64-row groups of the narrow one).  The groups of one weight tile run on
+  // one XCD, so after the first group the tile mostly comes from L2: ordinary
+  // loads.
   if (a.M <= 32) {
     a.mgroups = 1;
     st = lm_launch_tiles<1, 256, true>(a, s);
@@ -405,7 +590,7 @@ static orthrus_status lm_run(LmArgs a, hipStream_t s, int finish_groups) {
     st = lm_launch_tiles<2, 128, true>(a, s);
   } else {
     a.mgroups = (a.M + 63) / 64;
-    st = lm_launch_tiles<2, 128, false>(a, s);
+    st = lm_launch_wide<2, 64, false>(a, s);
   }
   if (st != ORTHRUS_OK) return st;
   hipLaunchKernelGGL(lm_head_finish, dim3((unsigned)finish_groups), dim3(kLmFinThreads), 0, s, a);

@@ -122,6 +122,28 @@ def test_lm_head_planted_ties_resolve_to_lowest_index():
         assert tok.item() == min(winner, copy) and mx.item() == float(H), (winner, copy, tok.item())
 
 
+def test_lm_head_planted_ties_many_rows():
+    """The same ties with more than 64 hidden rows (the wide kernel: two
+    32-row weight tiles per wave, 256-row key tiles): copies in the other tile
+    of the same wave, in the other lane half, in another wave of the same
+    256-row tile, and in another tile, before or after the winner.  Every row
+    must give the lower index of the pair, exactly."""
+    say("lm_head ties, many rows")
+    d = dev()
+    H, V, rows = 1024, 10000, 96
+    _, w, _ = I.make_lm_head_inputs(1, H, V, seed=6, planted=True, device=d)
+    # 5030 is row 38 of its wave's 64-row slice (second tile); 5000 is row 8 (first tile)
+    cases = [(5030, 5000), (5000, 5030), (5000, 4997), (5000, 4990), (5000, 5100), (5000, 4863), (9999, 9998),
+             (300, 44)]
+    for winner, copy in cases:
+        wi = w.clone()
+        wi[copy] = w[winner]
+        h = w[winner:winner + 1].repeat(rows, 1).contiguous()
+        tok, mx = ob().lm_head_argmax(h, ob().PackedLmHead(wi), want_max=True)
+        torch.cuda.synchronize()
+        assert torch.all(tok == min(winner, copy)) and torch.all(mx == float(H)), (winner, copy, tok.unique())
+
+
 def test_lm_head_greedy_accept_planted():
     """The AR view's hidden states planted at known greedy tokens; drafts
     agree on a geometric prefix: accept_len, next_token and ar_tokens equal
