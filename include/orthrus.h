@@ -67,7 +67,7 @@ typedef enum { ORTHRUS_BF16 = 0, ORTHRUS_F32 = 1 } orthrus_dtype;
 /* split_tokens value that asks for the balanced split of a ragged batch.
  * With bf16 storage, Hq / Hkv <= 4, 2 <= batch <= 64, batch * Hkv < 256 and
  * max_ctx_len < 2^24, the kernels read every ctx_lens[b] and take the
- * smallest split (a multiple of 64 in [256, 8192]) that gives at most
+ * smallest split (a multiple of 64 in [320, 8192]) that gives at most
  * ceil(256 / Hkv) work-groups per KV head, so that one round of about 256
  * work-groups covers the batch as evenly as 64-position tiles allow; the
  * launch and the workspace are sized for the worst case that max_ctx_len
@@ -96,10 +96,12 @@ typedef enum {
  *   dtype               storage type of q, out, caches and block K/V
  *   softmax_scale       <= 0 selects 1 / sqrt(D)
  *   split_tokens        context positions per work-group: a multiple of 64
- *                       in [64, 8192]; 0 = automatic (sized from
- *                       max_ctx_len, the best choice when the lengths are
- *                       equal); ORTHRUS_SPLIT_BALANCED = chosen on the device
- *                       from ctx_lens (for ragged batches, see below)      */
+ *                       in [64, 8192]; 0 = automatic (the shortest split,
+ *                       at least 320, that keeps a batch of max_ctx_len
+ *                       contexts within one round of ceil(256 / Hkv)
+ *                       work-groups per KV head; the best choice when the
+ *                       lengths are equal); ORTHRUS_SPLIT_BALANCED = chosen
+ *                       on the device from ctx_lens (ragged batches, below) */
 typedef struct {
   int32_t batch;
   int32_t block_k;
