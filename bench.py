@@ -48,7 +48,8 @@ def parse():
     p.add_argument("--batch", type=int, default=1)
     p.add_argument("--ctx", type=int, default=8192)
     p.add_argument("--layers", type=int, default=36)
-    p.add_argument("--split-tokens", type=int, default=0)
+    p.add_argument("--split-tokens", type=int, default=0,
+                   help="context positions per work-group: 0 automatic, -1 balanced, else a multiple of 64")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a graph")

@@ -162,7 +162,11 @@ def block_attn_workspace_bytes(desc):
 
 def block_attn(q, k_cache, v_cache, k_blk, v_blk, page_table, ctx_lens, mode, out=None, *, max_ctx_len=None,
                softmax_scale=None, split_tokens=0, ws=None, stream=None):
-    """orthrus_block_attn: out [B, K, Hq, D] in q's dtype."""
+    """orthrus_block_attn: out [B, K, Hq, D] in q's dtype.
+
+    split_tokens: 0 sizes the context split from max_ctx_len (equal lengths),
+    SPLIT_BALANCED lets the kernels choose it from ctx_lens (ragged batches),
+    and a multiple of 64 in [64, 8192] fixes it."""
     dev = _gpu(q, k_cache, v_cache, k_blk, v_blk, page_table, ctx_lens, out)
     if not (q.dtype == k_cache.dtype == v_cache.dtype == k_blk.dtype == v_blk.dtype):
         raise OrthrusError("q, caches and block K/V must share one dtype")
