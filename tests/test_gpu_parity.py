@@ -297,6 +297,19 @@ def test_balanced_split_ragged(B, Hkv, lens, max_ctx):
         assert torch.equal(out, again)
 
 
+@pytest.mark.parametrize("G,D", [(1, 64), (2, 64), (4, 64), (1, 128), (2, 128)])
+def test_balanced_split_group_sizes_and_head_dims(G, D):
+    """Every instantiation of the balanced-split kernels (query heads per KV
+    head G <= 4, head dim 64 or 128) on a ragged batch with an empty and a
+    page-boundary context, both modes, every sequence and head against the
+    oracle."""
+    say("balanced split G/D", G, D)
+    lens = [0, 700, 2049, 63, 1500]
+    inp = balanced_case(5, 2, lens, seed=100 + 10 * G + D, G=G, D=D)
+    for mode in (DIFF, AR):
+        check_attn(inp, mode, split=K_().SPLIT_BALANCED, max_ctx=inp.max_ctx_len)
+
+
 @pytest.mark.parametrize("B,L", [(2, 8192), (3, 8192), (4, 3000), (16, 2048)])
 def test_balanced_split_equal_lengths_match_fixed(B, L):
     """With every length at max_ctx the balanced split chooses the host's
