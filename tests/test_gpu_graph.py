@@ -1,11 +1,11 @@
 """Every entry point works under HIP graph capture: a step that calls them all
 (block attention in both modes with split contexts and with the balanced
-split, greedy and sampled
-consensus, the LM head's accept and denoising update, KV append into all
-layers, and a prompt prefill) is captured once and replayed three times,
-with unrelated eager work and synchronisations between the replays; every
-replay's outputs are bit-identical to an eager run of the same step (the
-kernels are deterministic and the step's writes are idempotent)."""
+split, greedy and sampled consensus, the LM head's accept, argmax over 96
+rows and denoising update, KV append into all layers, and a prompt prefill)
+is captured once and replayed three times, with unrelated eager work and
+synchronisations between the replays; every replay's outputs are
+bit-identical to an eager run of the same step (the kernels are
+deterministic and the step's writes are idempotent)."""
 
 import pytest
 import torch
@@ -33,6 +33,7 @@ def test_graph_replays_match_eager():
     hid, w, _ = I.make_lm_head_inputs(B * K, H, V, seed=3, device=d)
     head = ob.PackedLmHead(w)
     hid = hid.view(B, K, H)
+    hid96, _, _ = I.make_lm_head_inputs(96, H, V, seed=5, device=d)   # more than 64 rows: the wide tile kernel
     masked = torch.ones((B, K), dtype=torch.uint8, device=d)
     nun = torch.tensor([4, 9], dtype=torch.int32, device=d)
     kc, vc = inp.k_cache.clone(), inp.v_cache.clone()
@@ -52,6 +53,7 @@ def test_graph_replays_match_eager():
         outs += list(ob.sample_accept(ar, dr, sdrafts, ua, ur, 1.0))
         outs += list(ob.lm_head_greedy_accept(hid, head, drafts))
         outs += list(ob.lm_head_denoise_step(hid, head, masked, nun))
+        outs.append(ob.lm_head_argmax(hid96, head)[0])
         outs += list(ob.kv_append_layers(layers, inp.page_table, inp.ctx_lens, acc[0]))
         outs += list(ob.prefill(pre["q"], pre["k"], pre["v"], pkc, pvc, pre["page_table"], pre["ctx_lens"],
                                 pre["prompt_lens"], pre["max_prompt"], max_ctx_len=pre["max_ctx_len"]))
