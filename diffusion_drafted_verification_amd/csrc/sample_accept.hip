@@ -159,6 +159,32 @@ __device__ __forceinline__ float resid4(f32x4 xp, f32x4 xq, const f32x4& n, floa
   return s;
 }
 
+// x plus the value of the lane that a DPP control selects (0 where it
+// selects none): data movement on the VALU, no LDS round trip
+template <int CTRL, int ROW_MASK, bool BOUND_ZERO>
+__device__ __forceinline__ float dpp_add(float x) {
+  const int y = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROW_MASK, 0xf, BOUND_ZERO);
+  return x + __builtin_bit_cast(float, y);
+}
+
+// inclusive prefix sum over the wave in a fixed order: shifts by 1, 2, 4, 8
+// within each 16-lane row, then the row totals through the broadcasts of
+// lanes 15 and 31
+__device__ __forceinline__ float wave_scan(float x, int) {
+  x = dpp_add<0x111, 0xf, true>(x);   // row_shr:1
+  x = dpp_add<0x112, 0xf, true>(x);   // row_shr:2
+  x = dpp_add<0x114, 0xf, true>(x);   // row_shr:4
+  x = dpp_add<0x118, 0xf, true>(x);   // row_shr:8
+  x = dpp_add<0x142, 0xa, false>(x);  // row_bcast:15 -> rows 1, 3
+  x = dpp_add<0x143, 0xc, false>(x);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
+// the wave's total in every lane
+__device__ __forceinline__ float wave_sum(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wave_scan(x, 0)), kWave - 1));
+}
+
 __global__ void __launch_bounds__(kSampleThreads) sample_resid(SampleArgs a) {
   __shared__ f32x4 nrm[32];
   __shared__ int ok[32];
@@ -238,8 +264,7 @@ __global__ void __launch_bounds__(kSampleThreads) sample_resid(SampleArgs a) {
   } else {
     for (int v = begin + tid; v < end; v += kSampleThreads) s += resid(xp, xq, n, a.c, false, v);
   }
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) s += __shfl_xor(s, o, kWave);
+  s = wave_sum(s);
   if (lane == 0) red[wave] = s;
   __syncthreads();
   if (tid == 0) {
@@ -250,21 +275,6 @@ __global__ void __launch_bounds__(kSampleThreads) sample_resid(SampleArgs a) {
   }
 }
 
-// inclusive prefix sum over the wave (fixed order)
-__device__ __forceinline__ float wave_scan(float x, int lane) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const float y = __shfl_up(x, o, kWave);
-    if (lane >= o) x += y;
-  }
-  return x;
-}
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) x += __shfl_xor(x, o, kWave);
-  return x;
-}
 
 // mass of chunk k of the rejected row: the residual sum, or (when the
 // residual is zero everywhere) p's mass from the chunk pair
@@ -345,10 +355,27 @@ __global__ void __launch_bounds__(kSampleThreads) sample_pick(SampleArgs a) {
   // the thread's run of logits, all loads in flight, then its masses kept
   // in registers for the walk
   float xa[kRun], xd[kRun], rv[kRun];
+  if (hi - lo == kRun && ((reinterpret_cast<uintptr_t>(xp + lo) | reinterpret_cast<uintptr_t>(xq + lo)) & 15) == 0) {
+    // a whole, 16-byte aligned run (any vocabulary divisible by 4): 16-byte loads
+    const f32x4* pv = reinterpret_cast<const f32x4*>(xp + lo);
+    const f32x4* qv = reinterpret_cast<const f32x4*>(xq + lo);
+    f32x4 va[kRun / 4], vd[kRun / 4];
 #pragma unroll
-  for (int j = 0; j < kRun; ++j) {
-    xa[j] = lo + j < hi ? xp[lo + j] : -INFINITY;
-    xd[j] = lo + j < hi ? xq[lo + j] : -INFINITY;
+    for (int k = 0; k < kRun / 4; ++k) {
+      va[k] = pv[k];
+      vd[k] = qv[k];
+    }
+#pragma unroll
+    for (int j = 0; j < kRun; ++j) {
+      xa[j] = va[j / 4][j % 4];
+      xd[j] = vd[j / 4][j % 4];
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kRun; ++j) {
+      xa[j] = lo + j < hi ? xp[lo + j] : -INFINITY;
+      xd[j] = lo + j < hi ? xq[lo + j] : -INFINITY;
+    }
   }
   float s = 0.f;
 #pragma unroll
