@@ -43,20 +43,39 @@ __device__ __forceinline__ void keep_better(float& bv, int& bi, float v, int i) 
   }
 }
 
+// max of k and the key of the lane that a DPP control selects (key 0,
+// below every real key, where it selects none)
+template <int CTRL, int ROW_MASK, bool BOUND_ZERO>
+__device__ __forceinline__ unsigned long long dpp_max_u64(unsigned long long k) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)k, CTRL, ROW_MASK, 0xf, BOUND_ZERO);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(k >> 32), CTRL, ROW_MASK, 0xf, BOUND_ZERO);
+  const unsigned long long o = ((unsigned long long)hi << 32) | lo;
+  return o > k ? o : k;
+}
+
+// the wave's largest key, in every lane: a max-scan on the DPP paths (shifts
+// by 1, 2, 4, 8 within each 16-lane row, then the row maxima through the
+// broadcasts of lanes 15 and 31), read from the last lane
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long k) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const uint32_t lo = __shfl_xor((uint32_t)k, off, kWave);
-    const uint32_t hi = __shfl_xor((uint32_t)(k >> 32), off, kWave);
-    const unsigned long long o = ((unsigned long long)hi << 32) | lo;
-    k = o > k ? o : k;
-  }
-  return k;
+  k = dpp_max_u64<0x111, 0xf, true>(k);   // row_shr:1
+  k = dpp_max_u64<0x112, 0xf, true>(k);   // row_shr:2
+  k = dpp_max_u64<0x114, 0xf, true>(k);   // row_shr:4
+  k = dpp_max_u64<0x118, 0xf, true>(k);   // row_shr:8
+  k = dpp_max_u64<0x142, 0xa, false>(k);  // row_bcast:15 -> rows 1, 3
+  k = dpp_max_u64<0x143, 0xc, false>(k);  // row_bcast:31 -> rows 2, 3
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)k, kWave - 1);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(k >> 32), kWave - 1);
+  return ((unsigned long long)hi << 32) | lo;
+}
+
+// the key of a (value, index) candidate: a larger key is a larger value, then
+// a lower index (the empty candidate, -inf at index 2^31 - 1, stays above 0)
+__device__ __forceinline__ unsigned long long cand_key(float v, int i) {
+  return ((unsigned long long)order_bits(v) << 32) | (unsigned long long)(0xffffffffu - (uint32_t)i);
 }
 
 __global__ void __launch_bounds__(kArgmaxThreads) argmax_chunks(AcceptArgs a) {
-  __shared__ float wv[kArgmaxThreads / kWave];
-  __shared__ int wi[kArgmaxThreads / kWave];
+  __shared__ unsigned long long wkey[kArgmaxThreads / kWave];
 
   const int row = blockIdx.x / a.nchunks;  // b * K + i
   const int ck = blockIdx.x % a.nchunks;
@@ -85,23 +104,15 @@ __global__ void __launch_bounds__(kArgmaxThreads) argmax_chunks(AcceptArgs a) {
   }
   for (int idx = head_end + 4 * nvec + tid; idx < end; idx += kArgmaxThreads) keep_better(bv, bi, x[idx], idx);
 
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float ov = __shfl_xor(bv, off, kWave);
-    const int oi = __shfl_xor(bi, off, kWave);
-    keep_better(bv, bi, ov, oi);
-  }
+  const unsigned long long wk = wave_max_u64(cand_key(bv, bi));
   const int wave = tid / kWave, lane = tid % kWave;
-  if (lane == 0) {
-    wv[wave] = bv;
-    wi[wave] = bi;
-  }
+  if (lane == 0) wkey[wave] = wk;
   __syncthreads();
   if (tid == 0) {
+    unsigned long long k = wkey[0];
 #pragma unroll
-    for (int w = 1; w < kArgmaxThreads / kWave; ++w) keep_better(bv, bi, wv[w], wi[w]);
-    a.part[(size_t)row * a.nchunks + ck] =
-        ((unsigned long long)order_bits(bv) << 32) | (unsigned long long)(0xffffffffu - (uint32_t)bi);
+    for (int w = 1; w < kArgmaxThreads / kWave; ++w) k = wkey[w] > k ? wkey[w] : k;
+    a.part[(size_t)row * a.nchunks + ck] = k;
   }
 }
 
