@@ -69,6 +69,45 @@ __device__ __forceinline__ void ms_add4(float& m, float& s, f32x4 v, float c) {
   m = mm;
 }
 
+// merge the (m, s) pair of the lane that a DPP control selects into this
+// lane's; where it selects none (a row outside ROW_MASK) the pair merged is
+// (-inf, 0), which leaves this lane's unchanged.  Data movement on the VALU,
+// no LDS round trip.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void dpp_merge(float& m, float& s, float c) {
+  const float m2 = __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, -INFINITY), __builtin_bit_cast(int, m), CTRL,
+                                         ROW_MASK, 0xf, false));
+  const float s2 = __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, s), CTRL, ROW_MASK, 0xf, false));
+  ms_merge(m, s, m2, s2, c);
+}
+
+// both pairs reduced over each aligned group of 8 lanes, the result in every
+// lane of the group: partners at lane ^ 1, lane ^ 2, then the mirror image in
+// the group
+__device__ __forceinline__ void merge8(float& mp, float& sp, float& mq, float& sq, float c) {
+  dpp_merge<0xb1, 0xf>(mp, sp, c);   // quad_perm [1, 0, 3, 2]
+  dpp_merge<0xb1, 0xf>(mq, sq, c);
+  dpp_merge<0x4e, 0xf>(mp, sp, c);   // quad_perm [2, 3, 0, 1]
+  dpp_merge<0x4e, 0xf>(mq, sq, c);
+  dpp_merge<0x141, 0xf>(mp, sp, c);  // row_half_mirror
+  dpp_merge<0x141, 0xf>(mq, sq, c);
+}
+
+// both pairs reduced over the wave, the result in lane 63: groups of 8, the
+// 16-lane rows through their mirror image, then the row results through the
+// broadcasts of lanes 15 and 31
+__device__ __forceinline__ void merge_wave(float& mp, float& sp, float& mq, float& sq, float c) {
+  merge8(mp, sp, mq, sq, c);
+  dpp_merge<0x140, 0xf>(mp, sp, c);  // row_mirror
+  dpp_merge<0x140, 0xf>(mq, sq, c);
+  dpp_merge<0x142, 0xa>(mp, sp, c);  // row_bcast:15 -> rows 1, 3
+  dpp_merge<0x142, 0xa>(mq, sq, c);
+  dpp_merge<0x143, 0xc>(mp, sp, c);  // row_bcast:31 -> rows 2, 3
+  dpp_merge<0x143, 0xc>(mq, sq, c);
+}
+
 constexpr int kVecPerThread = kSampleChunk / 4 / kSampleThreads;
 
 // [begin, end) of one row as a scalar head up to 16-byte alignment (< 4
@@ -117,12 +156,8 @@ __global__ void __launch_bounds__(kSampleThreads) sample_stats(SampleArgs a) {
     ms_add4(mp, sp_, vp[j], a.c);
     ms_add4(mq, sq, vq[j], a.c);
   }
-#pragma unroll
-  for (int off = 1; off < kWave; off <<= 1) {
-    ms_merge(mp, sp_, __shfl_xor(mp, off, kWave), __shfl_xor(sp_, off, kWave), a.c);
-    ms_merge(mq, sq, __shfl_xor(mq, off, kWave), __shfl_xor(sq, off, kWave), a.c);
-  }
-  if (tid % kWave == 0) red[tid / kWave] = f32x4{mp, sp_, mq, sq};
+  merge_wave(mp, sp_, mq, sq, a.c);
+  if (tid % kWave == kWave - 1) red[tid / kWave] = f32x4{mp, sp_, mq, sq};
   __syncthreads();
   if (tid == 0) {
     mp = red[0][0], sp_ = red[0][1], mq = red[0][2], sq = red[0][3];
@@ -194,7 +229,7 @@ __global__ void __launch_bounds__(kSampleThreads) sample_resid(SampleArgs a) {
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
 
   // decision: kRowThreads threads per row merge its chunk pairs (chunks
-  // sub, sub + 8, ...), a butterfly over the 8 gives the normalisers
+  // sub, sub + 8, ...), a DPP merge over the 8 gives the normalisers
   {
     const int i = tid / kRowThreads, sub = tid % kRowThreads;
     const bool live = i < a.K;
@@ -217,11 +252,8 @@ __global__ void __launch_bounds__(kSampleThreads) sample_resid(SampleArgs a) {
         ms_merge(mp, sp, t[0], t[1], a.c);
         ms_merge(mq, sq, t[2], t[3], a.c);
       }
-#pragma unroll
-    for (int off = 1; off < kRowThreads; off <<= 1) {
-      ms_merge(mp, sp, __shfl_xor(mp, off, kWave), __shfl_xor(sp, off, kWave), a.c);
-      ms_merge(mq, sq, __shfl_xor(mq, off, kWave), __shfl_xor(sq, off, kWave), a.c);
-    }
+    static_assert(kRowThreads == 8, "the decision merges groups of 8 lanes");
+    merge8(mp, sp, mq, sq, a.c);
     if (live && sub == 0) {
       const f32x4 nr = recip_sums(f32x4{mp, sp, mq, sq});
       const float px = in ? prob(xa, nr[0], nr[1], a.c) : 0.f;
@@ -300,7 +332,7 @@ __global__ void __launch_bounds__(kSampleThreads) sample_pick(SampleArgs a) {
   if (r >= a.K) return;  // every draft accepted: next_token is already written
 
   if (wave == 0) {
-    // total residual mass (lane-strided, then butterfly)
+    // total residual mass (lane-strided, then a wave sum)
     float t = cs0;
     for (int k = lane + kWave; k < a.nchunks; k += kWave) t += a.rsum[(size_t)b * a.nchunks + k];
     t = wave_sum(t);
