@@ -173,6 +173,40 @@ def test_sample_zero_probability_and_out_of_vocabulary_drafts():
     assert gn[0] != drafts[0, 3] or ga[0] < 3
 
 
+def test_sample_masked_vocabulary():
+    """Heads whose logits are -inf over most of the vocabulary (as after a
+    top-k or grammar mask): whole 8192-logit chunks, whole waves of a chunk
+    and the upper lanes of a wave carry no mass, so their (max, sum) pairs
+    are (-inf, 0) where the chunk statistics and the row normalisers merge.
+    Drafts are samples of the masked draft head; sequence 2 has disjoint
+    supports (every draft has p = 0, the correction comes from p)."""
+    say("sample masked vocabulary")
+    B, K, V, T = 4, 8, 151936, 0.8
+    ar, dr, _, ua, ur = I.make_sample_inputs(B, K, V, T, seed=17, workload="")
+    v = torch.arange(V)
+    off = v % 8192
+    chunk = v // 8192
+    # p: the first 128 logits of each chunk (lanes 0-31 of wave 0), chunk 2
+    # whole, a band across a chunk boundary; the last chunk none
+    keep_p = (off < 128) | (chunk == 2) | ((v >= 106000) & (v < 106800))
+    keep_p &= chunk != V // 8192
+    # q: logits 64-319 of each chunk (across the first wave boundary), chunk 2
+    # whole, every 1009th; chunks 5-9 none
+    keep_q = ((off >= 64) & (off < 320)) | (chunk == 2) | (v % 1009 == 0)
+    keep_q &= (chunk < 5) | (chunk > 9)
+    ninf = torch.tensor(-float("inf"))
+    ar = torch.where(keep_p, ar, ninf)
+    dr = torch.where(keep_q, dr, ninf)
+    # sequence 2: p only in chunk 11, q only in chunk 2
+    ar[2] = torch.where(chunk == 11, ar[2] + 0.0, ninf)
+    dr[2] = torch.where(chunk == 2, dr[2] + 0.0, ninf)
+    g = torch.Generator().manual_seed(1717)
+    u = torch.rand((B, K, V), generator=g, dtype=torch.float64).clamp_(min=1e-300)
+    drafts = torch.argmax(dr.double() / T - torch.log(-torch.log(u)), dim=-1).to(torch.int32)
+    ga, gn, _ = check_sample(ar, dr, drafts, ua, ur, T, max_excused=0.25)
+    assert ga[2] == 0 and chunk[int(gn[2])] == 11
+
+
 def test_sample_low_temperature():
     """T = 0.02: p and q are close to one-hot; the rule then behaves like the
     greedy consensus and the decisions are far from their boundaries."""
