@@ -102,6 +102,18 @@ def test_qwen3_8b_ragged16_sampled(mode):
     check_attn(inp, mode, batches=pick)
 
 
+@pytest.mark.parametrize("B", [2, 4, 8, 16])
+def test_qwen3_8b_8k_batch_sweep_sampled(B):
+    """The batch sweep the benchmark times (Qwen3-8B heads, 8192 cached tokens
+    per sequence, automatic split: 512 positions per split at B2 up to 4096
+    at B16, 256 work-groups each), both modes; the oracle checks the first and last sequence on three
+    heads of different KV groups."""
+    say("qwen3_8b_8k batch sweep", B)
+    inp = I.make_attn_inputs("qwen3_8b_8k", seed=1, batch=B, ctx_lens=[8192] * B)
+    for mode in (DIFF, AR):
+        check_attn(inp, mode, batches=[0, B - 1], heads=[0, 13, 31])
+
+
 def test_qwen3_8b_32k_sampled():
     say("qwen3_8b_32k_b4 layer 0 sampled heads")
     inp = I.make_attn_inputs("qwen3_8b_32k_b4")
