@@ -56,12 +56,16 @@ def abs_bound(h, w, vslice=16384):
                                         for v0 in range(0, w.shape[0], vslice)], axis=-1), axis=-1)
 
 
-def check_random(rows, H, V, seed):
+def check_random(rows, H, V, seed, sample=None):
+    """GPU argmax of all rows; the oracle checks every row, or the rows in
+    `sample` (a row's token depends on that row alone)."""
     d = dev()
     h, w, _ = I.make_lm_head_inputs(rows, H, V, seed=seed)
     tok, mx = ob().lm_head_argmax(h.to(d), ob().PackedLmHead(w.to(d)), want_max=True)
     torch.cuda.synchronize()
     tok, mx = tok.cpu().numpy(), mx.cpu().numpy().astype(np.float64)
+    if sample is not None:
+        tok, mx, h = tok[sample], mx[sample], h[sample]
     lg = oracle_logits(h, w)
     ref = O.greedy_argmax(lg)
     eb = abs_bound(h, w)
@@ -88,6 +92,16 @@ def test_lm_head_random_vs_oracle(rows, H, V):
 def test_lm_head_qwen3_8b_random():
     say("lm_head qwen3-8b random")
     check_random(32, I.QWEN3_8B_HIDDEN, I.QWEN3_VOCAB, seed=1)
+
+
+@pytest.mark.parametrize("rows", [128, 512])
+def test_lm_head_qwen3_8b_random_wide_rows_sampled(rows):
+    """The benchmark's B4 and B16 row counts at the Qwen3-8B head (the wide
+    kernel, 64-row groups): the oracle checks rows on both sides of every
+    group boundary and the last row."""
+    say("lm_head qwen3-8b random wide", rows)
+    sample = sorted({0} | {m for k in range(64, rows, 64) for m in (k - 1, k)} | {rows - 1})
+    check_random(rows, I.QWEN3_8B_HIDDEN, I.QWEN3_VOCAB, seed=rows, sample=sample)
 
 
 @pytest.mark.parametrize("rows", [1, 32, 64, 96, 512])
