@@ -110,6 +110,17 @@ def test_prefill_qwen3_8b_2k_prompt_sampled():
     run_prefill(x, heads=[0, 9, 31], rows=[0, 1, 31, 32, 33, 500, 1023, 1024, 2047])
 
 
+@pytest.mark.parametrize("L,S", [(8192, 2048), (0, 8192)])
+def test_prefill_qwen3_8b_benchmark_shapes_sampled(L, S):
+    """The two larger prompts the benchmark times at the Qwen3-8B attention
+    shape (a 2048-token prompt after 8192 cached tokens; an 8192-token prompt
+    on an empty cache), in the launch configuration it times (automatic
+    split), compared on sampled heads and rows."""
+    say("prefill qwen3-8b benchmark shape", L, S)
+    x = I.make_prefill_inputs([L], [S], 32, 8, 128, seed=L + S)
+    run_prefill(x, heads=[0, 14, 31], rows=[0, 31, 32, S // 2 - 1, S // 2, S - 33, S - 1])
+
+
 def test_prefill_in_two_calls_equals_one():
     """Chunked prefill through the ABI: the prompt's second part after the
     first part's call (its rows now cached, new_ctx_lens as the context)
