@@ -49,13 +49,18 @@ def masks_and_counts(B, K, seed):
     return torch.from_numpy(masked), torch.from_numpy(n)
 
 
-def check_step(h, w, masked, n, head=None, max_excused=1):
+def check_step(h, w, masked, n, head=None, max_excused=1, seqs=None):
+    """GPU step over every sequence; the oracle checks every sequence, or
+    those in `seqs` (a sequence's tokens, confidences and unmasking depend
+    on its own rows alone)."""
     d = dev()
-    B, K, H = h.shape
     head = head or ob().PackedLmHead(w.to(d))
     tok, conf, nm = ob().lm_head_denoise_step(h.to(d), head, masked.to(d), n.to(d))
     torch.cuda.synchronize()
     tok, conf, nm = tok.cpu().numpy(), conf.cpu().numpy().astype(np.float64), nm.cpu().numpy().astype(bool)
+    if seqs is not None:
+        tok, conf, nm, h, masked, n = tok[seqs], conf[seqs], nm[seqs], h[seqs], masked[seqs], n[seqs]
+    B, K, H = h.shape
     lg = np.concatenate([O.lm_head_logits(h, w[v0:v0 + 16384]) for v0 in range(0, w.shape[0], 16384)], axis=-1)
     rtok, rconf = O.denoise_confidence(lg)
     rnm = O.denoise_select(rconf, masked.numpy().astype(bool), n.numpy())
@@ -100,6 +105,17 @@ def test_denoise_qwen3_8b_head():
     h, w, _ = I.make_lm_head_inputs(B * K, I.QWEN3_8B_HIDDEN, I.QWEN3_VOCAB, seed=7)
     masked, n = masks_and_counts(B, K, seed=7)
     check_step(h.view(B, K, -1), w, masked, n)
+
+
+def test_denoise_qwen3_8b_head_b16_sampled():
+    """The benchmark's B16 rows (512, the wide kernel's 64-row groups) at the
+    Qwen3-8B head; the oracle checks sequences at both ends and on both sides
+    of the 256-row point."""
+    say("denoise qwen3-8b B16 sampled")
+    B, K = 16, 32
+    h, w, _ = I.make_lm_head_inputs(B * K, I.QWEN3_8B_HIDDEN, I.QWEN3_VOCAB, seed=16)
+    masked, n = masks_and_counts(B, K, seed=16)
+    check_step(h.view(B, K, -1), w, masked, n, seqs=[0, 1, 7, 8, 15])
 
 
 def test_denoise_planted_sharpness_orders_the_unmasking():
