@@ -114,6 +114,16 @@ def test_qwen3_8b_8k_batch_sweep_sampled(B):
         check_attn(inp, mode, batches=[0, B - 1], heads=[0, 13, 31])
 
 
+def test_qwen3_8b_128k_context_sampled():
+    """One sequence with 131072 cached tokens (512 MiB of K/V per layer; the
+    automatic split gives 32 splits of 4096 positions), both modes, on three
+    heads; the block rows see the whole context plus the block."""
+    say("qwen3_8b 128k context sampled")
+    inp = I.make_attn_inputs("qwen3_8b_8k", seed=5, batch=1, ctx_lens=[131072])
+    for mode in (DIFF, AR):
+        check_attn(inp, mode, heads=[0, 17, 31])
+
+
 def test_qwen3_8b_32k_sampled():
     say("qwen3_8b_32k_b4 layer 0 sampled heads")
     inp = I.make_attn_inputs("qwen3_8b_32k_b4")
