@@ -9,6 +9,7 @@ block-dominant variants where a wrong key, page or mask gives an O(1) error.
 """
 
 import ctypes
+import dataclasses
 import math
 
 import numpy as np
@@ -530,6 +531,52 @@ def test_append_fp32():
     say("append fp32")
     inp = I.make_attn_inputs("tiny_fp32")
     check_append(inp, [12])
+
+
+@pytest.mark.parametrize("K,acc", [(7, [6, 0, 7]), (7, [2, 5, 3]), (1, [0, 1, 0]), (5, [4, 3, 0])])
+def test_append_block_sizes_off_the_row_group(K, acc):
+    """Block sizes below 32 that are not a multiple of 4 (K = 7, 5, 1),
+    with accept lengths from none to all: rows past K are neither read nor
+    written, and the slots and lengths match the definition."""
+    say("append block size", K, acc)
+    inp = I.make_attn_inputs("qwen3_8b_ragged16", batch=3)
+    inp = dataclasses.replace(inp, q=inp.q[:, :K].contiguous(), k_blk=inp.k_blk[:, :K].contiguous(),
+                              v_blk=inp.v_blk[:, :K].contiguous())
+    check_append(inp, acc)
+
+
+def test_append_invalid_page_ids_inside_a_row_group():
+    """Page ids of -1 and past the cache under some committed rows: those
+    rows are not written (slot -1) while their neighbours on valid pages are.
+    With 13 cached tokens, rows 0-2 sit on logical page 0 (id -1) and rows
+    3-18 on page 1; rows 19-24 sit on logical page 2 (an id past the
+    cache)."""
+    say("append invalid page ids")
+    d = dev()
+    inp = I.make_attn_inputs("qwen3_8b_8k", ctx_lens=[13])
+    acc = [24]                                     # n = 25 rows: positions 13 .. 37
+    pt = inp.page_table.clone()
+    pt[0, 0] = -1
+    pt[0, 2] = inp.k_cache.shape[0] + 5
+    skipped = [0, 1, 2] + list(range(19, 25))
+    kc0 = torch.full_like(inp.k_cache, -3.0)
+    vc0 = torch.full_like(inp.v_cache, 5.0)
+    kc, vc = kc0.to(d), vc0.to(d)
+    new_lens, slots = K_().kv_append(kc, vc, inp.k_blk.to(d), inp.v_blk.to(d), pt.to(d), inp.ctx_lens.to(d),
+                                     torch.tensor(acc, dtype=torch.int32, device=d), max_ctx_len=inp.max_ctx_len)
+    torch.cuda.synchronize()
+    # the definition with the valid table, then the skipped rows undone
+    rk, rv, rl, rs = O.kv_append(kc0, vc0, inp.k_blk, inp.v_blk, inp.page_table, inp.ctx_lens, acc)
+    k0, v0 = kc0.view(torch.int16).numpy(), vc0.view(torch.int16).numpy()
+    for r in skipped:
+        page, slot = divmod(int(rs[0, r]), 16)
+        rk[page, :, slot] = k0[page, :, slot]
+        rv[page, :, slot] = v0[page, :, slot]
+        rs[0, r] = -1
+    assert np.array_equal(kc.cpu().view(torch.int16).numpy(), rk)
+    assert np.array_equal(vc.cpu().view(torch.int16).numpy(), rv)
+    assert np.array_equal(new_lens.cpu().numpy(), rl) and np.array_equal(slots.cpu().numpy(), rs)
+    assert (slots.cpu().numpy()[0, [3, 18]] >= 0).all()
 
 
 def test_append_layers_matches_per_layer_oracle():
