@@ -27,7 +27,7 @@ Parallel Token Generation via Dual-View Diffusion" (gist.science, arXiv
 Everything is written as the definition, in fp64, with numpy primitives
 (fancy indexing, matmul, exp) as steps and no blocking or fusion.
 
-Readings of points the pages leave open (each one is listed in the design doc):
+Readings of points the pages leave open:
 
 * rows of the two views are aligned by position: row i of either view is the
   prediction for the token after block position i; drafts[i] is compared
