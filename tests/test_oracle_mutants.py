@@ -53,6 +53,21 @@ MUTANTS = {
                                   "s = scale * (keys[:L + i + 2] @ q[b, i, h])\n"
                                   "                w = np.exp(s - s.max())\n"
                                   "                out[b, i, h] = (w @ vals[:L + i + 2]) / w.sum()"),
+    "prompt_write_slot_shifted": ("            kc[page, :, pos % page_size, :] = kr[b, r]\n"
+                                  "            vc[page, :, pos % page_size, :] = vr[b, r]",
+                                  "            kc[page, :, (pos + 1) % page_size, :] = kr[b, r]\n"
+                                  "            vc[page, :, (pos + 1) % page_size, :] = vr[b, r]"),
+    "prefill_gqa_head_interleaved": ("g = h * Hkv // Hq\n            keys = np.concatenate",
+                                     "g = h % Hkv\n            keys = np.concatenate"),
+    "prefill_scale_dropped": ("scale = 1.0 / np.sqrt(D) if softmax_scale is None else float(softmax_scale)\n"
+                              "    out = np.full((B, S, Hq, D), np.nan)",
+                              "scale = 1.0 if softmax_scale is None else float(softmax_scale)\n"
+                              "    out = np.full((B, S, Hq, D), np.nan)"),
+    "accept_compare_inverted": ("        if int(d) != int(t):\n            break", "        if int(d) == int(t):\n            break"),
+    "sample_accept_len_one_late": ("            acc[b] = i\n", "            acc[b] = i + 1\n"),
+    "softmax_t_unnormalised": ("    return e / np.sum(e, axis=-1, keepdims=True)", "    return e"),
+    "denoise_unmasks_one_too_few": ("for i in order[:max(int(n[b]), 0)]:", "for i in order[:max(int(n[b]) - 1, 0)]:"),
+    "lm_head_hidden_reversed": ("return h @ w.T", "return h[..., ::-1] @ w.T"),
     "prompt_write_skips_row_0": ("        for r in range(int(n[b])):\n            pos = L + r",
                                  "        for r in range(1, int(n[b])):\n            pos = L + r"),
 }
