@@ -119,8 +119,10 @@ class Step:
 
 
 def capture(torch, fn):
-    """Capture fn() in a HIP graph on a side stream (after one eager run so
-    workspaces exist); returns a replay callable."""
+    """Capture fn() in a HIP graph on a side stream, after one eager run on
+    that same stream so that the binding's per-stream workspaces exist before
+    capture (and no zero fill of a new workspace lands in the graph); returns
+    a replay callable."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
@@ -128,7 +130,7 @@ def capture(torch, fn):
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
+    with torch.cuda.graph(g, stream=s):
         fn()
     torch.cuda.synchronize()
     return g.replay

@@ -1544,6 +1544,7 @@ orthrus_status orthrus::block_attn_run(const void* q, const void* k_cache, const
   if (!q || !k_cache || !v_cache || !k_blk || !v_blk || !page_table || !ctx_lens || !out)
     return ORTHRUS_ERR_NULL;
   if (mode != ORTHRUS_DIFF_BIDIR && mode != ORTHRUS_AR_CAUSAL) return ORTHRUS_ERR_SHAPE;
+  if (!aligned16(q, k_cache, v_cache, k_blk, v_blk, out) || !aligned4(page_table, ctx_lens)) return ORTHRUS_ERR_SHAPE;
   const orthrus_attn_desc& d = *desc;
   const size_t need = attn_workspace_bytes(d);
   if (need > 0 && (!workspace || workspace_bytes < need)) return ORTHRUS_ERR_WORKSPACE;
@@ -1605,3 +1606,4 @@ extern "C" orthrus_status orthrus_block_attn(const void* q, const void* k_cache,
   return block_attn_run(q, k_cache, v_cache, k_blk, v_blk, page_table, ctx_lens, mode, out, desc, workspace,
                         workspace_bytes, stream, true);
 }
+

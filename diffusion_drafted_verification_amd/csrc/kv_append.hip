@@ -33,13 +33,16 @@ __global__ void __launch_bounds__(256) kv_append_kernel(AppendArgs a) {
   const int layer = blockIdx.x / (a.B * a.K);
   const int br = blockIdx.x % (a.B * a.K);
   const int b = br / a.K, r = br % a.K;
-  int L = a.ctx_lens[b];
-  L = L < 0 ? 0 : (L > a.max_ctx ? a.max_ctx : L);
+  // a context length outside [0, max_ctx] breaks the call's contract: such a
+  // sequence is skipped (nothing written, new length and slots -1) rather
+  // than clamped, which would overwrite committed rows
+  const int L = a.ctx_lens[b];
+  const bool seq_ok = L >= 0 && L <= a.max_ctx;
   int acc = a.accept_len[b];
   acc = acc < 0 ? 0 : (acc > a.K ? a.K : acc);
   const int n = acc + 1 < a.K ? acc + 1 : a.K;
   const int pos = L + r;
-  bool write = r < n;
+  bool write = seq_ok && r < n;
   int page = -1;
   if (write) {
     const int lp = pos / kPage;
@@ -48,7 +51,7 @@ __global__ void __launch_bounds__(256) kv_append_kernel(AppendArgs a) {
   }
   if (threadIdx.x == 0 && layer == 0) {
     if (a.slots) a.slots[b * a.K + r] = write ? page * kPage + pos % kPage : -1;
-    if (r == 0 && a.new_ctx_lens) a.new_ctx_lens[b] = L + n;
+    if (r == 0 && a.new_ctx_lens) a.new_ctx_lens[b] = seq_ok ? L + n : -1;
   }
   if (!write) return;
   char* k_cache = a.k_cache_list ? reinterpret_cast<char*>(a.k_cache_list[layer]) : a.k_cache;
@@ -129,6 +132,9 @@ extern "C" orthrus_status orthrus_kv_append(void* k_cache, void* v_cache, const 
   orthrus_status st = validate_desc(desc);
   if (st != ORTHRUS_OK) return st;
   if (!k_cache || !v_cache || !k_blk || !v_blk || !page_table || !ctx_lens || !accept_len) return ORTHRUS_ERR_NULL;
+  if (!aligned16(k_cache, v_cache, k_blk, v_blk) ||
+      !aligned4(page_table, ctx_lens, accept_len, new_ctx_lens, slots))
+    return ORTHRUS_ERR_SHAPE;
   AppendArgs a = {};
   a.k_cache = (char*)k_cache;
   a.v_cache = (char*)v_cache;
@@ -148,6 +154,9 @@ extern "C" orthrus_status orthrus_kv_append_layers(const uint64_t* k_cache_ptrs,
   if (!k_cache_ptrs || !v_cache_ptrs || !k_blk_ptrs || !v_blk_ptrs || !page_table || !ctx_lens || !accept_len)
     return ORTHRUS_ERR_NULL;
   if (n_layers < 1 || n_layers > 4096) return ORTHRUS_ERR_SHAPE;
+  if (!aligned_to<8>(k_cache_ptrs, v_cache_ptrs, k_blk_ptrs, v_blk_ptrs) ||
+      !aligned4(page_table, ctx_lens, accept_len, new_ctx_lens, slots))
+    return ORTHRUS_ERR_SHAPE;
   AppendArgs a = {};
   a.k_cache_list = k_cache_ptrs;
   a.v_cache_list = v_cache_ptrs;

@@ -9,6 +9,23 @@
 
 namespace orthrus {
 
+// Every tensor the kernels move as 16-byte units (q, out, caches, block K/V)
+// must start on a 16-byte boundary, arrays of device addresses on an 8-byte
+// one and every int32 array on a 4-byte one.  NULL pointers pass (optional
+// outputs).
+template <size_t N, typename... P>
+inline bool aligned_to(P... p) {
+  return ((reinterpret_cast<uintptr_t>(p) % N == 0) && ...);
+}
+template <typename... P>
+inline bool aligned16(P... p) {
+  return aligned_to<16>(p...);
+}
+template <typename... P>
+inline bool aligned4(P... p) {
+  return aligned_to<4>(p...);
+}
+
 inline orthrus_status validate_desc(const orthrus_attn_desc* d) {
   if (!d) return ORTHRUS_ERR_NULL;
   if (d->batch < 1 || d->block_k < 1 || d->block_k > 32 || d->n_q_heads < 1 || d->n_kv_heads < 1 ||

@@ -135,6 +135,8 @@ extern "C" orthrus_status orthrus_prefill(const void* q, const void* k, const vo
                                           size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !k_cache || !v_cache || !page_table || !ctx_lens || !prompt_lens || !out)
     return ORTHRUS_ERR_NULL;
+  if (!aligned16(q, k, v, k_cache, v_cache, out) || !aligned4(page_table, ctx_lens, prompt_lens, new_ctx_lens))
+    return ORTHRUS_ERR_SHAPE;
   orthrus_attn_desc vd;
   int C, S;
   const orthrus_status vs = prefill_desc(desc, max_prompt, &vd, &C, &S);

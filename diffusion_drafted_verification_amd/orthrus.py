@@ -142,18 +142,34 @@ def make_desc(q, k_cache, page_table, max_ctx_len=None, softmax_scale=None, spli
                     float(softmax_scale) if softmax_scale else 0.0, int(split_tokens))
 
 
-_workspaces = {}
+_workspaces = {}   # (device, kind, stream) -> the cached workspace of that stream
+_retired = []      # workspaces replaced by larger ones: a graph captured earlier may still address them
 
 
-def workspace(device, nbytes, kind):
-    """A cached per-(device, kind) workspace of at least nbytes (the kernels
-    need no particular initial contents)."""
-    key = (str(device), kind)
+def workspace(device, nbytes, kind, stream=None):
+    """A workspace of at least nbytes for calls of one kind on one stream,
+    starting zeroed.
+
+    Calls that share a workspace must be ordered on one stream, so the cache
+    is per (device, kind, stream).  A workspace that has to grow is replaced
+    but never freed: a HIP graph captured earlier may still hold its address.
+    Sizes grow at least twofold, so few buffers are ever retired.  During
+    graph capture a missing or too small workspace is not cached: it comes
+    from the graph's own memory pool (and lives as long as the graph), since
+    an eager call after the graph is gone must not use that pool's memory."""
+    s = torch.cuda.current_stream(device) if stream is None else stream
+    key = (str(device), kind, s.cuda_stream)
     ws = _workspaces.get(key)
-    if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
-        _workspaces[key] = ws
-    return ws
+    if ws is not None and ws.numel() >= nbytes:
+        return ws
+    size = max(nbytes, 256, 2 * ws.numel() if ws is not None else 0)
+    if torch.cuda.is_current_stream_capturing():
+        return torch.zeros(size, dtype=torch.uint8, device=device)
+    new = torch.zeros(size, dtype=torch.uint8, device=device)
+    if ws is not None:
+        _retired.append(ws)
+    _workspaces[key] = new
+    return new
 
 
 def block_attn_workspace_bytes(desc):
@@ -183,7 +199,7 @@ def block_attn(q, k_cache, v_cache, k_blk, v_blk, page_table, ctx_lens, mode, ou
         raise OrthrusError("out must match q")
     need = lib().orthrus_block_attn_workspace_bytes(ctypes.byref(desc))
     if ws is None and need:
-        ws = workspace(dev, need, "attn")
+        ws = workspace(dev, need, "attn", stream)
     st = lib().orthrus_block_attn(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_blk), _ptr(v_blk),
                                   _ptr(page_table), _ptr(ctx_lens), int(mode), _ptr(out), ctypes.byref(desc),
                                   _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream))
@@ -205,7 +221,7 @@ def greedy_accept(ar_logits, draft_tokens, *, want_ar_tokens=True, ws=None, stre
     g = torch.empty((B, K), dtype=torch.int32, device=dev) if want_ar_tokens else None
     need = lib().orthrus_greedy_accept_workspace_bytes(B, K, V)
     if ws is None:
-        ws = workspace(dev, need, "accept")
+        ws = workspace(dev, need, "accept", stream)
     st = lib().orthrus_greedy_accept(_ptr(ar_logits), _ptr(draft_tokens), _ptr(acc), _ptr(nxt), _ptr(g),
                                      B, K, V, _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "orthrus_greedy_accept")
@@ -229,7 +245,7 @@ def sample_accept(ar_logits, draft_logits, draft_tokens, u_accept, u_resample, t
     nxt = torch.empty(B, dtype=torch.int32, device=dev)
     need = lib().orthrus_sample_accept_workspace_bytes(B, K, V)
     if ws is None:
-        ws = workspace(dev, need, "sample")
+        ws = workspace(dev, need, "sample", stream)
     st = lib().orthrus_sample_accept(_ptr(ar_logits), _ptr(draft_logits), _ptr(draft_tokens), _ptr(u_accept),
                                      _ptr(u_resample), float(temperature), _ptr(acc), _ptr(nxt), B, K, V,
                                      _ptr(ws), ws.numel(), _stream(stream))
@@ -274,7 +290,7 @@ def lm_head_argmax(hidden, head, *, want_max=False, ws=None, stream=None):
     mx = torch.empty(hidden.shape[:-1], dtype=torch.float32, device=dev) if want_max else None
     need = lib().orthrus_lm_head_workspace_bytes(rows, H, V)
     if ws is None:
-        ws = workspace(dev, need, "lm_head")
+        ws = workspace(dev, need, "lm_head", stream)
     st = lib().orthrus_lm_head_argmax(_ptr(hidden), _ptr(weight), _ptr(tok), _ptr(mx), rows, H, V, _ptr(ws),
                                       ws.numel(), _stream(stream))
     _check(st, "orthrus_lm_head_argmax")
@@ -297,7 +313,7 @@ def lm_head_greedy_accept(hidden, head, draft_tokens, *, want_ar_tokens=True, ws
     g = torch.empty((B, K), dtype=torch.int32, device=dev) if want_ar_tokens else None
     need = lib().orthrus_lm_head_workspace_bytes(B * K, H, V)
     if ws is None:
-        ws = workspace(dev, need, "lm_head")
+        ws = workspace(dev, need, "lm_head", stream)
     st = lib().orthrus_lm_head_greedy_accept(_ptr(hidden), _ptr(weight), _ptr(draft_tokens), _ptr(acc), _ptr(nxt),
                                              _ptr(g), B, K, H, V, _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "orthrus_lm_head_greedy_accept")
@@ -387,7 +403,7 @@ def lm_head_denoise_step(hidden, head, masked, n_unmask, *, new_masked=None, ws=
         new_masked = torch.empty_like(masked)
     need = lib().orthrus_lm_head_denoise_workspace_bytes(B * K, H, V)
     if ws is None:
-        ws = workspace(dev, need, "lm_head_denoise")
+        ws = workspace(dev, need, "lm_head_denoise", stream)
     st = lib().orthrus_lm_head_denoise_step(_ptr(hidden), _ptr(head.packed), _ptr(masked), _ptr(n_unmask),
                                             _ptr(tok), _ptr(conf), _ptr(new_masked), B, K, H, V, _ptr(ws),
                                             ws.numel(), _stream(stream))
@@ -415,7 +431,7 @@ def prefill(q, k, v, k_cache, v_cache, page_table, ctx_lens, prompt_lens, max_pr
     desc = make_desc(q[:, :32], k_cache, page_table, max_ctx_len, softmax_scale, split_tokens)
     need = lib().orthrus_prefill_workspace_bytes(ctypes.byref(desc), int(max_prompt))
     if ws is None:
-        ws = workspace(dev, need, "prefill")
+        ws = workspace(dev, need, "prefill", stream)
     st = lib().orthrus_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
                                _ptr(ctx_lens), _ptr(prompt_lens), int(max_prompt), _ptr(out), _ptr(new_ctx_lens),
                                ctypes.byref(desc), _ptr(ws), ws.numel(), _stream(stream))

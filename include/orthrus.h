@@ -22,6 +22,10 @@
  *     the kernels: an out-of-range context length or page id never faults; it
  *     makes the affected rows' results unspecified (cache rows are not
  *     written through an invalid page id).
+ *   - Alignment: q, out, k_cache, v_cache, k_blk, v_blk, k, v (prefill),
+ *     hidden and the LM-head weights must be 16-byte aligned, arrays of
+ *     device addresses 8-byte aligned and int32 arrays 4-byte aligned;
+ *     otherwise the call returns ORTHRUS_ERR_SHAPE and enqueues nothing.
  *   - For a fixed descriptor every output is bit-identical from run to run.
  *   - Calls are reentrant; calls that share a workspace must be ordered on
  *     one stream.
@@ -279,6 +283,10 @@ orthrus_status orthrus_lm_head_denoise_step(const void* hidden, const void* pack
  *   L_b + r = ctx_lens[b] + r of k_cache/v_cache.  Nothing else is written.
  *   new_ctx_lens[b] = L_b + n_b            (optional, may be NULL)
  *   slots[b, r] = page * P + slot written, -1 for r >= n_b (optional)
+ * A sequence with ctx_lens[b] outside [0, max_ctx_len] violates the
+ * descriptor: nothing of it is written, new_ctx_lens[b] = -1 and its slots
+ * are all -1 (the other sequences are unaffected).  A row whose page id is
+ * outside [0, num_pages) is not written and its slot is -1.
  * ctx_lens is read only: in a multi-layer step pass new_ctx_lens only on
  * the last layer so every layer appends at the same positions.  Neither
  * output may alias ctx_lens, accept_len or page_table. */

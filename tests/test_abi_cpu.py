@@ -262,3 +262,42 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 32, 4, 64)
     with pytest.raises(B.OrthrusError):
         B.block_attn(q, q, q, q, q, torch.zeros(1, 1, dtype=torch.int32), torch.zeros(1, dtype=torch.int32), 0)
+
+
+def test_misaligned_pointers_are_rejected():
+    """Tensors moved as 16-byte units must be 16-byte aligned, device-address
+    arrays 8-byte aligned and int32 arrays 4-byte aligned: a misaligned
+    pointer gives ERR_SHAPE (2) before anything is launched."""
+    lib = B.lib()
+    d = good_desc()
+    need = lib.orthrus_block_attn_workspace_bytes(ctypes.byref(d))
+    W = ctypes.c_void_p(4096 * 256)
+    A = FAKE
+    M8 = ctypes.c_void_p(4096 + 8)      # 8-byte but not 16-byte aligned
+    M2 = ctypes.c_void_p(4096 + 2)      # 2-byte aligned only
+    for slot in range(9):               # q, k_cache, v_cache, k_blk, v_blk, page_table, ctx_lens, (mode), out
+        if slot == 7:
+            continue
+        ptrs = [A] * 9
+        ptrs[slot] = M2 if slot in (5, 6) else M8
+        assert lib.orthrus_block_attn(*ptrs[:7], 0, ptrs[8], ctypes.byref(d), W, need, None) == 2, slot
+    # int32 arrays need only 4-byte alignment: the call gets past that check
+    # and fails on the (too small) workspace instead
+    assert lib.orthrus_block_attn(A, A, A, A, A, ctypes.c_void_p(4096 + 4), A, 0, A, ctypes.byref(d), W, need - 1,
+                                  None) == 4
+    for slot in range(4):
+        ptrs = [A] * 4
+        ptrs[slot] = M8
+        assert lib.orthrus_kv_append(*ptrs, A, A, A, None, None, ctypes.byref(d), None) == 2, slot
+    assert lib.orthrus_kv_append(A, A, A, A, M2, A, A, None, None, ctypes.byref(d), None) == 2
+    assert lib.orthrus_kv_append(A, A, A, A, A, A, A, None, M2, ctypes.byref(d), None) == 2
+    assert lib.orthrus_kv_append_layers(A, A, A, ctypes.c_void_p(4096 + 4), 36, A, A, A, None, None,
+                                        ctypes.byref(d), None) == 2
+    pd = good_desc(max_ctx_len=4096, max_pages_per_seq=514)
+    pw = lib.orthrus_prefill_workspace_bytes(ctypes.byref(pd), 4096)
+    P = ctypes.c_void_p(4096 * 256)
+    for slot in (0, 1, 2, 3, 4, 9):     # q, k, v, k_cache, v_cache, out
+        ptrs = [A] * 10
+        ptrs[slot] = M8
+        assert lib.orthrus_prefill(*ptrs[:8], 4096, ptrs[9], None, ctypes.byref(pd), P, pw, None) == 2, slot
+    assert lib.orthrus_prefill(A, A, A, A, A, A, A, M2, 4096, A, None, ctypes.byref(pd), P, pw, None) == 2

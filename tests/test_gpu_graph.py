@@ -86,3 +86,40 @@ def test_graph_replays_match_eager():
         for i, (c, e) in enumerate(zip(caches, eager_caches)):
             assert torch.equal(c, e), (rep, "cache", i)
         del junk
+
+
+def test_graph_replay_after_workspace_growth():
+    """A graph captured on a stream keeps working after a later eager call on
+    the same stream needs a larger workspace: the binding replaces the cached
+    workspace but never frees the one the graph holds, so memory allocated
+    afterwards cannot alias it.  The replay must match the eager result."""
+    print("[case] graph replay after workspace growth", flush=True)
+    d = dev()
+    from diffusion_drafted_verification_amd import orthrus as ob
+    small = I.make_attn_inputs("qwen3_8b_8k", batch=1, ctx_lens=[2000], device=d)
+    large = I.make_attn_inputs("qwen3_8b_8k", seed=3, batch=4, ctx_lens=[8192, 8000, 5000, 7000], device=d)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    call = lambda x, mx: ob.block_attn(x.q, x.k_cache, x.v_cache, x.k_blk, x.v_blk, x.page_table, x.ctx_lens,
+                                       ob.AR_CAUSAL, max_ctx_len=mx, split_tokens=64)
+    with torch.cuda.stream(s):
+        eager = call(small, 2000).clone()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        out = call(small, 2000)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        big = call(large, 8192)            # needs a larger workspace on the same stream
+    torch.cuda.synchronize()
+    fillers = [torch.full((1 << 22,), 0x55, dtype=torch.uint8, device=d) for _ in range(8)]
+    for rep in range(3):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), rep
+        with torch.cuda.stream(s):
+            again = call(large, 8192)
+        torch.cuda.synchronize()
+        assert torch.equal(again, big), rep
+    del fillers

@@ -333,6 +333,27 @@ def test_balanced_split_group_sizes_and_head_dims(G, D):
         check_attn(inp, mode, split=K_().SPLIT_BALANCED, max_ctx=inp.max_ctx_len)
 
 
+@pytest.mark.parametrize("mode", [DIFF, AR])
+def test_balanced_split_ragged16_bench_workload(mode):
+    """The ragged workload exactly as the benchmark times it: 16 sequences
+    with L_b ~ U[1024, 16384] (the benchmark's lengths), the balanced split
+    chosen on the device (splits of several thousand positions, up to three
+    per sequence).  The shortest, the longest and four more sequences are
+    checked against the oracle on heads of three KV groups, and a repeat of
+    the call gives identical bits."""
+    say("balanced split, ragged16 bench workload", mode)
+    inp = I.make_attn_inputs("qwen3_8b_ragged16")
+    lens = inp.ctx_lens.numpy()
+    assert list(lens) == list(I.draw_ctx_lens("qwen3_8b_ragged16", seed=0, batch=16))
+    pick = sorted({int(np.argmin(lens)), int(np.argmax(lens)), 0, 5, 9, 15})
+    bal = K_().SPLIT_BALANCED
+    out, _ = check_attn(inp, mode, split=bal, batches=pick, heads=[0, 13, 31])
+    g = inp.to(dev())
+    again = K_().block_attn(g.q, g.k_cache, g.v_cache, g.k_blk, g.v_blk, g.page_table, g.ctx_lens, mode,
+                            max_ctx_len=inp.max_ctx_len, split_tokens=bal)
+    assert torch.equal(out, again)
+
+
 @pytest.mark.parametrize("B,L", [(2, 8192), (3, 8192), (4, 3000), (16, 2048)])
 def test_balanced_split_equal_lengths_match_fixed(B, L):
     """With every length at max_ctx the balanced split chooses the host's
@@ -577,6 +598,43 @@ def test_append_invalid_page_ids_inside_a_row_group():
     assert np.array_equal(vc.cpu().view(torch.int16).numpy(), rv)
     assert np.array_equal(new_lens.cpu().numpy(), rl) and np.array_equal(slots.cpu().numpy(), rs)
     assert (slots.cpu().numpy()[0, [3, 18]] >= 0).all()
+
+
+def test_append_context_beyond_max_ctx_is_skipped():
+    """A loose max_ctx_len (above every length) gives the definition; a
+    max_ctx_len below some ctx_lens[b] breaks the descriptor for those
+    sequences: nothing of them is written (their committed rows stay intact),
+    their new length and slots are -1, and the other sequences still get
+    exactly the definition."""
+    say("append with loose and too small max_ctx_len")
+    d = dev()
+    inp = I.make_attn_inputs("qwen3_8b_ragged16", batch=4)
+    lens = inp.ctx_lens.numpy()
+    acc = [5, 0, 31, 12]
+    cap = inp.page_table.shape[1] * 16 - 32
+    for max_ctx in (cap, int(np.sort(lens)[1])):   # loose, then below the two longest
+        kc0 = torch.full_like(inp.k_cache, -3.0)
+        vc0 = torch.full_like(inp.v_cache, 5.0)
+        kc, vc = kc0.to(d), vc0.to(d)
+        nl, sl = K_().kv_append(kc, vc, inp.k_blk.to(d), inp.v_blk.to(d), inp.page_table.to(d),
+                                inp.ctx_lens.to(d), torch.tensor(acc, dtype=torch.int32, device=d),
+                                max_ctx_len=max_ctx)
+        torch.cuda.synchronize()
+        ok = lens <= max_ctx
+        acc_ok = [a if o else -1 for a, o in zip(acc, ok)]
+        # the definition on the sequences that fit; the others write nothing
+        keep = [b for b in range(4) if ok[b]]
+        rk, rv, rl, rs = O.kv_append(kc0, vc0, inp.k_blk[keep], inp.v_blk[keep], inp.page_table[keep],
+                                     inp.ctx_lens[keep], [acc[b] for b in keep])
+        assert np.array_equal(kc.cpu().view(torch.int16).numpy(), rk)
+        assert np.array_equal(vc.cpu().view(torch.int16).numpy(), rv)
+        exp_l = np.full(4, -1, dtype=np.int64)
+        exp_s = np.full((4, 32), -1, dtype=np.int64)
+        exp_l[keep] = rl
+        exp_s[keep] = rs
+        assert np.array_equal(nl.cpu().numpy(), exp_l), (max_ctx, nl.cpu().numpy(), exp_l, acc_ok)
+        assert np.array_equal(sl.cpu().numpy(), exp_s)
+        assert ok.all() == (max_ctx == cap)
 
 
 def test_append_layers_matches_per_layer_oracle():
