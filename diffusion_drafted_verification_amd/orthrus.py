@@ -148,23 +148,24 @@ _retired = []      # workspaces replaced by larger ones: a graph captured earlie
 
 def workspace(device, nbytes, kind, stream=None):
     """A workspace of at least nbytes for calls of one kind on one stream,
-    starting zeroed.
+    zero-filled when it is made.
 
     Calls that share a workspace must be ordered on one stream, so the cache
     is per (device, kind, stream).  A workspace that has to grow is replaced
     but never freed: a HIP graph captured earlier may still hold its address.
-    Sizes grow at least twofold, so few buffers are ever retired.  During
-    graph capture a missing or too small workspace is not cached: it comes
-    from the graph's own memory pool (and lives as long as the graph), since
-    an eager call after the graph is gone must not use that pool's memory."""
+    Sizes grow at least twofold, so few buffers are ever retired.  No
+    workspace is made during graph capture (the zero fill would become part
+    of the graph): run the call once on the capturing stream before capture,
+    or pass ws= explicitly."""
     s = torch.cuda.current_stream(device) if stream is None else stream
     key = (str(device), kind, s.cuda_stream)
     ws = _workspaces.get(key)
     if ws is not None and ws.numel() >= nbytes:
         return ws
-    size = max(nbytes, 256, 2 * ws.numel() if ws is not None else 0)
     if torch.cuda.is_current_stream_capturing():
-        return torch.zeros(size, dtype=torch.uint8, device=device)
+        raise OrthrusError(f"no {kind} workspace of {nbytes} bytes for the capturing stream: run the call once "
+                           "on that stream before capture, or pass ws=")
+    size = max(nbytes, 256, 2 * ws.numel() if ws is not None else 0)
     new = torch.zeros(size, dtype=torch.uint8, device=device)
     if ws is not None:
         _retired.append(ws)

@@ -301,3 +301,34 @@ def test_misaligned_pointers_are_rejected():
         ptrs[slot] = M8
         assert lib.orthrus_prefill(*ptrs[:8], 4096, ptrs[9], None, ctypes.byref(pd), P, pw, None) == 2, slot
     assert lib.orthrus_prefill(A, A, A, A, A, A, A, M2, 4096, A, None, ctypes.byref(pd), P, pw, None) == 2
+
+
+def test_binding_makes_no_workspace_during_capture(monkeypatch):
+    """The binding's cached workspaces are per (device, kind, stream), are
+    replaced (never freed) when they must grow, and are never made while a
+    stream is capturing a graph (the zero fill would become a graph node):
+    such a call raises and asks for a warm-up or an explicit ws=."""
+    import torch
+
+    class FakeStream:
+        cuda_stream = 0xabc
+
+    made = []
+    monkeypatch.setattr(torch, "zeros", lambda n, dtype=None, device=None: made.append(n) or torch.empty(n, dtype=dtype))
+    monkeypatch.setattr(torch.cuda, "is_current_stream_capturing", lambda: False)
+    B._workspaces.clear()
+    s = FakeStream()
+    w1 = B.workspace("cuda:0", 1000, "attn", s)
+    assert B.workspace("cuda:0", 900, "attn", s) is w1            # cached per stream
+    w2 = B.workspace("cuda:0", 1500, "attn", s)                   # grows at least twofold
+    assert w2.numel() == 2000 and made == [1000, 2000] and w1 in B._retired
+    monkeypatch.setattr(torch.cuda, "is_current_stream_capturing", lambda: True)
+    assert B.workspace("cuda:0", 1800, "attn", s) is w2           # big enough: fine while capturing
+    with pytest.raises(B.OrthrusError, match="capturing stream"):
+        B.workspace("cuda:0", 5000, "attn", s)
+    other = FakeStream()
+    other.cuda_stream = 0xdef
+    with pytest.raises(B.OrthrusError, match="capturing stream"):
+        B.workspace("cuda:0", 100, "attn", other)                 # another stream has none yet
+    B._workspaces.clear()
+    B._retired.clear()

@@ -71,7 +71,7 @@ def test_graph_replays_match_eager():
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
+    with torch.cuda.graph(g, stream=side):   # the warmed stream: its workspaces exist already
         outs = step()
     torch.cuda.synchronize()
     for rep in range(3):
@@ -123,3 +123,4 @@ def test_graph_replay_after_workspace_growth():
         torch.cuda.synchronize()
         assert torch.equal(again, big), rep
     del fillers
+

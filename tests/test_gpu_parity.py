@@ -372,6 +372,53 @@ def test_balanced_split_equal_lengths_match_fixed(B, L):
         assert torch.equal(run(ob.SPLIT_BALANCED), run(split))
 
 
+@pytest.mark.parametrize("B,lens,split", [
+    (48, [(n * 613) % 2048 for n in range(48)], 1024),      # up to 2 splits; 768 work-groups: several rounds
+    (40, [4096 - (n * 131) % 4096 for n in range(40)], 1024),   # up to 4 splits, 1280 work-groups
+])
+def test_split_launches_of_several_rounds(B, lens, split):
+    """Ragged batches whose split launch takes several rounds of work-groups
+    (some sequences unsplit, some with up to 4 splits, empty contexts among
+    them): sampled sequences and heads against the oracle, and a repeat on
+    the same workspace gives identical bits."""
+    say("split launch of several rounds", B, split)
+    d = dev()
+    ob = K_()
+    inp = I.make_attn_inputs("qwen3_8b_8k", seed=11, batch=B, ctx_lens=lens)
+    desc = ob.make_desc(inp.q, inp.k_cache, inp.page_table, max(lens), None, split)
+    ws = torch.full((ob.block_attn_workspace_bytes(desc),), 0x5a, dtype=torch.uint8, device=d)
+    pick = sorted({int(np.argmax(lens)), int(np.argmin(lens)), 1, B - 1})
+    g = inp.to(d)
+    for mode in (DIFF, AR):
+        run = lambda: ob.block_attn(g.q, g.k_cache, g.v_cache, g.k_blk, g.v_blk, g.page_table, g.ctx_lens, mode,
+                                    max_ctx_len=max(lens), split_tokens=split, ws=ws)
+        out = run()
+        torch.cuda.synchronize()
+        ref = O.block_attn(inp.q, inp.k_cache, inp.v_cache, inp.k_blk, inp.v_blk, inp.page_table, inp.ctx_lens,
+                           mode, batches=pick, heads=[0, 13, 31])
+        got = out.float().cpu().numpy().astype(np.float64)
+        err = np.abs(got - ref)[pick][:, :, [0, 13, 31]]
+        assert err.max() <= TOL * max_abs_v(inp), err.max()
+        assert torch.equal(run(), out)
+
+
+def test_repeated_calls_give_identical_bits():
+    """Fifty back-to-back calls of the benchmark shape (one sequence, 8192
+    cached tokens, 26 splits per KV head) on one workspace, alternating the
+    two views: every call of a view gives identical bits."""
+    say("50 repeated calls")
+    d = dev()
+    ob = K_()
+    x = I.make_attn_inputs("qwen3_8b_8k", device=d)
+    desc = ob.make_desc(x.q, x.k_cache, x.page_table, 8192, None, 0)
+    ws = torch.empty(ob.block_attn_workspace_bytes(desc), dtype=torch.uint8, device=d)
+    outs = [ob.block_attn(x.q, x.k_cache, x.v_cache, x.k_blk, x.v_blk, x.page_table, x.ctx_lens,
+                          DIFF if n % 2 else AR, max_ctx_len=8192, ws=ws) for n in range(50)]
+    torch.cuda.synchronize()
+    for n in range(2, 50):
+        assert torch.equal(outs[n], outs[n % 2]), n
+
+
 def test_ragged_with_loose_max_ctx():
     """max_ctx_len larger than every real context (grid sized by the bound,
     splits past a sequence's end exit early)."""
