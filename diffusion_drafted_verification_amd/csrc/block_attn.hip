@@ -1607,3 +1607,62 @@ extern "C" orthrus_status orthrus_block_attn(const void* q, const void* k_cache,
                         workspace_bytes, stream, true);
 }
 
+// ---------------------------------------------------------------------------
+// block attention without a caller workspace: the split partials live in a
+// fixed device array of the library (one copy per GPU, for the life of the
+// process), for callers that cannot allocate.
+// ---------------------------------------------------------------------------
+
+#include <mutex>
+
+static __device__ __align__(256) char scratch[ORTHRUS_STATIC_SCRATCH_BYTES];
+
+namespace orthrus {
+
+constexpr int kMaxDevices = 64;
+static void* g_scratch[kMaxDevices];  // device address of `scratch` on each GPU (host-side cache)
+static std::mutex g_scratch_mu;
+
+// Address of this library's scratch array on device `dev`, looked up once per
+// device with that device current (the host-side name `scratch` is only a
+// stand-in: each GPU holds its own copy at its own address).
+static void* scratch_on(int dev) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev]) return g_scratch[dev];
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return nullptr;
+  if (cur != dev && hipSetDevice(dev) != hipSuccess) return nullptr;
+  void* p = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (cur != dev) (void)hipSetDevice(cur);
+  if (e != hipSuccess || !p) return nullptr;
+  g_scratch[dev] = p;
+  return p;
+}
+
+}  // namespace orthrus
+
+extern "C" orthrus_status orthrus_block_attn_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                                     const void* k_blk, const void* v_blk,
+                                                     const int32_t* page_table, const int32_t* ctx_lens,
+                                                     orthrus_mode mode, void* out, const orthrus_attn_desc* desc,
+                                                     void* stream) {
+  orthrus_status st = validate_desc(desc);
+  if (st != ORTHRUS_OK) return st;
+  if (!q || !k_cache || !v_cache || !k_blk || !v_blk || !page_table || !ctx_lens || !out)
+    return ORTHRUS_ERR_NULL;
+  if (mode != ORTHRUS_DIFF_BIDIR && mode != ORTHRUS_AR_CAUSAL) return ORTHRUS_ERR_SHAPE;
+  if (!aligned16(q, k_cache, v_cache, k_blk, v_blk, out) || !aligned4(page_table, ctx_lens)) return ORTHRUS_ERR_SHAPE;
+  const size_t need = attn_workspace_bytes(*desc);
+  if (need > ORTHRUS_STATIC_SCRATCH_BYTES) return ORTHRUS_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0) {
+    int dev = -1;
+    const hipError_t e = stream ? hipStreamGetDevice((hipStream_t)stream, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) return ORTHRUS_ERR_LAUNCH;
+    ws = scratch_on(dev);
+    if (!ws) return ORTHRUS_ERR_LAUNCH;
+  }
+  return block_attn_run(q, k_cache, v_cache, k_blk, v_blk, page_table, ctx_lens, mode, out, desc, ws,
+                        need > 0 ? ORTHRUS_STATIC_SCRATCH_BYTES : 0, stream, true);
+}

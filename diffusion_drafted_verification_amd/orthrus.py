@@ -44,6 +44,7 @@ SIGNATURES = {
     "orthrus_block_attn_workspace_bytes": (_sz, [_DESC_P]),
     "orthrus_block_attn_split_tokens": (_i32, [_DESC_P]),
     "orthrus_block_attn": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _DESC_P, _vp, _sz, _vp]),
+    "orthrus_block_attn_noalloc": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _DESC_P, _vp]),
     "orthrus_greedy_accept_workspace_bytes": (_sz, [_i32, _i32, _i32]),
     "orthrus_greedy_accept": (_i32, [_vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _sz, _vp]),
     "orthrus_sample_accept_workspace_bytes": (_sz, [_i32, _i32, _i32]),
@@ -205,6 +206,25 @@ def block_attn(q, k_cache, v_cache, k_blk, v_blk, page_table, ctx_lens, mode, ou
                                   _ptr(page_table), _ptr(ctx_lens), int(mode), _ptr(out), ctypes.byref(desc),
                                   _ptr(ws), ws.numel() if ws is not None else 0, _stream(stream))
     _check(st, "orthrus_block_attn")
+    return out
+
+
+STATIC_SCRATCH_BYTES = 16 << 20   # ORTHRUS_STATIC_SCRATCH_BYTES
+
+
+def block_attn_noalloc(q, k_cache, v_cache, k_blk, v_blk, page_table, ctx_lens, mode, out, *, max_ctx_len=None,
+                       softmax_scale=None, split_tokens=0, stream=None):
+    """orthrus_block_attn_noalloc: block_attn into a caller-provided `out`,
+    with the split partials in the library's fixed per-GPU scratch array
+    (nothing is allocated)."""
+    _gpu(q, k_cache, v_cache, k_blk, v_blk, page_table, ctx_lens, out)
+    if out.shape != q.shape or out.dtype != q.dtype:
+        raise OrthrusError("out must match q")
+    desc = make_desc(q, k_cache, page_table, max_ctx_len, softmax_scale, split_tokens)
+    st = lib().orthrus_block_attn_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(k_blk), _ptr(v_blk),
+                                          _ptr(page_table), _ptr(ctx_lens), int(mode), _ptr(out),
+                                          ctypes.byref(desc), _stream(stream))
+    _check(st, "orthrus_block_attn_noalloc")
     return out
 
 

@@ -12,7 +12,8 @@
  * Conventions shared by every call
  *   - Every tensor pointer is a DEVICE pointer (hipMalloc / torch CUDA
  *     memory) owned by the caller.  The library never allocates, frees or
- *     retains caller memory and keeps no mutable global state.
+ *     retains caller memory; its only mutable global state is the fixed
+ *     scratch array of orthrus_block_attn_noalloc.
  *   - Work is only enqueued on `stream` (a hipStream_t; NULL = the default
  *     stream); no call synchronises.  Results are ready when the stream is.
  *   - Errors are synchronous and host-detectable only: a non-OK status means
@@ -153,6 +154,31 @@ orthrus_status orthrus_block_attn(const void* q, const void* k_cache, const void
                                   const int32_t* ctx_lens, orthrus_mode mode, void* out,
                                   const orthrus_attn_desc* desc, void* workspace,
                                   size_t workspace_bytes, void* stream);
+
+/* Largest workspace orthrus_block_attn_noalloc can serve (16 MiB: every
+ * decode shape up to 32 query heads x 32 rows x 32 splits per sequence and
+ * KV-head group, e.g. Qwen3-8B heads at batch 16 x 8192 or batch 4 x 32768
+ * cached tokens). */
+#define ORTHRUS_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* orthrus_block_attn for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, semantics and results as orthrus_block_attn,
+ * without the workspace: the split partials go to a fixed device array of
+ * ORTHRUS_STATIC_SCRATCH_BYTES that the library owns, one copy per GPU, held
+ * until the process ends.  The call allocates nothing (its first call on a
+ * GPU looks up that GPU's copy once).
+ *   ORTHRUS_ERR_WORKSPACE  when orthrus_block_attn_workspace_bytes(desc)
+ *                          exceeds ORTHRUS_STATIC_SCRATCH_BYTES;
+ *   ORTHRUS_ERR_LAUNCH     when the stream's device cannot be determined.
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents: calls that overlap in time on one GPU (on different streams or
+ * from different threads) race and give unspecified results.  Calls ordered
+ * on one stream are safe. */
+orthrus_status orthrus_block_attn_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                          const void* k_blk, const void* v_blk, const int32_t* page_table,
+                                          const int32_t* ctx_lens, orthrus_mode mode, void* out,
+                                          const orthrus_attn_desc* desc, void* stream);
 
 /* Bytes of the workspace orthrus_greedy_accept needs (one 8-byte key per
  * (row, 8192-logit chunk)).  The workspace needs no initialisation. */

@@ -24,7 +24,7 @@ def declared_entry_points():
 
 def test_exports_every_declared_symbol():
     names = declared_entry_points()
-    assert len(names) == 22
+    assert len(names) == 23
     assert set(names) == set(B.SIGNATURES)
     lib = B.lib()
     for n in names:
@@ -301,6 +301,23 @@ def test_misaligned_pointers_are_rejected():
         ptrs[slot] = M8
         assert lib.orthrus_prefill(*ptrs[:8], 4096, ptrs[9], None, ctypes.byref(pd), P, pw, None) == 2, slot
     assert lib.orthrus_prefill(A, A, A, A, A, A, A, M2, 4096, A, None, ctypes.byref(pd), P, pw, None) == 2
+
+
+def test_noalloc_validation():
+    """The entry point without a workspace validates like orthrus_block_attn
+    and refuses, before any HIP call, a descriptor whose partials exceed the
+    library's fixed scratch array."""
+    lib = B.lib()
+    d = good_desc()
+    call = lambda desc, q=FAKE, mode=0: lib.orthrus_block_attn_noalloc(q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, mode,
+                                                                       FAKE, ctypes.byref(desc), None)
+    assert call(d, q=None) == 1
+    assert call(d, mode=2) == 2
+    assert call(good_desc(head_dim=96)) == 3
+    assert call(d, q=ctypes.c_void_p(4096 + 8)) == 2
+    big = good_desc(batch=4, split_tokens=64)             # 4 x 128 splits: about 138 MB of partials
+    assert lib.orthrus_block_attn_workspace_bytes(ctypes.byref(big)) > 16 << 20
+    assert call(big) == 4
 
 
 def test_binding_makes_no_workspace_during_capture(monkeypatch):
