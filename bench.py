@@ -13,7 +13,9 @@ per step, several times the 256 MB Infinity Cache).  The step is captured once
 in a HIP graph and replayed; inputs are resident in HBM before timing starts.
 
 Output: one JSON line.  `value` = block-attention KV bytes read per step /
-step time (GB/s).  `roofline` = the block-attention call (main + combine
+step time (GB/s).  The step's accept replays one 19.4 MB logits buffer, so it
+reads it warm from the Infinity Cache (under 1 % of the step); the
+`greedy_accept` field times it alone both warm and cold.  `roofline` = the block-attention call (main + combine
 kernels) timed alone with HIP events on its stream, against the 8 TB/s HBM
 peak.  `cpu_baseline` = the fp64 oracle on a bounded sample of the same step
 on the host cores.  `sample_accept` = the sampled consensus at temperature 1
@@ -57,6 +59,7 @@ def parse():
     p.add_argument("--no-sample", action="store_true", help="skip the sampled-consensus timing")
     p.add_argument("--no-lm-head", action="store_true", help="skip the LM-head timing")
     p.add_argument("--no-prefill", action="store_true", help="skip the prompt-prefill timing")
+    p.add_argument("--no-config2", action="store_true", help="skip the Qwen3-1.7B attention-shape leg")
     p.add_argument("--no-long-context", action="store_true",
                    help="skip the 36-layer step at batch 4, 32768 cached tokens")
     p.add_argument("--copy-probe-mib", type=int, default=0,
@@ -326,6 +329,87 @@ def prefill_timing(torch, ob, I, use_graph):
             "shape": "B1 Hq32/Hkv8 D128 bf16, one layer", **out}
 
 
+def config2_timing(torch, ob, I, use_graph):
+    """The Qwen3-1.7B attention shape (Hq 16, Hkv 8, D 128: two query heads
+    per KV head), one sequence with 2048 cached tokens, K = 32: the block
+    attention call of both views timed alone, cycling over enough layers
+    (1 GiB of K/V) that every call reads its K/V cold.  Algorithmic bytes per
+    call: 2048 x 8 x 128 x 2 x 2 = 8 MiB."""
+    layers = max(2, math.ceil(1.0 * 2**30 / (2048 * 4096)))
+    s2 = Step(ob, I, torch, 1, 2048, layers, 0, seed=1, workload="qwen3_1p7b_2k")
+    spread = []
+    ms_diff = attn_only_ms(torch, s2, ob.DIFF_BIDIR, use_graph, iters=10, spread=spread)
+    ms_ar = attn_only_ms(torch, s2, ob.AR_CAUSAL, use_graph, iters=10, spread=spread)
+    ms = 0.5 * (ms_diff + ms_ar)
+    gbs = s2.kv_bytes_call / (ms * 1e-3) / 1e9
+    split = ob.lib().orthrus_block_attn_split_tokens(
+        ob.make_desc(s2.L[0]["q_diff"], s2.L[0]["k_cache"], s2.page_table, s2.max_ctx, None, 0))
+    flops = 2 * 2 * 1 * 32 * 16 * 128 * (2048 + 32)
+    out = {"workload": "qwen3_1p7b_2k: B1 Hq16/Hkv8 D128 ctx2048 K32 (block attention, both views)",
+           "us_per_call": round(ms * 1e3, 3), "us_diff": round(ms_diff * 1e3, 3), "us_ar": round(ms_ar * 1e3, 3),
+           "bytes_per_call": s2.kv_bytes_call, "kv_gbs": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+           "split_tokens": split, "mfma_tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+           "us_per_call_p10_p50_p90": [round(sorted(spread)[int(q * (len(spread) - 1))] * 1e3, 3)
+                                       for q in (0.1, 0.5, 0.9)]}
+    del s2
+    torch.cuda.empty_cache()
+    return out
+
+
+def accept_timing(torch, ob, I, use_graph, step):
+    """The step's greedy accept (32 x 151936 fp32 logits per sequence) timed
+    alone, warm (the same 19.4 MB each call, as the step replays it: the
+    logits stay in the 256 MB Infinity Cache) and cold (cycling over input
+    copies of at least 600 MB)."""
+    B, K, V = step.B, step.K, I.QWEN3_VOCAB
+    ws = torch.empty(ob.lib().orthrus_greedy_accept_workspace_bytes(B, K, V), dtype=torch.uint8, device="cuda:0")
+    n = max(2, math.ceil(600e6 / (B * K * V * 4)))
+    sets = [step.logits] + [step.logits.clone() for _ in range(n - 1)]
+    out = {}
+    for name, calls in (("warm", [step.logits] * n), ("cold", sets)):
+        fn = lambda calls=calls: [ob.greedy_accept(c, step.drafts, ws=ws) for c in calls]
+        fn()
+        rep = capture(torch, fn) if use_graph else fn
+        out[f"us_per_call_{name}"] = round(time_region(torch, rep, 10, 2) / n * 1e3, 2)
+    del sets
+    torch.cuda.empty_cache()
+    nbytes = B * K * V * 4
+    out.update({"kernel": "orthrus_greedy_accept (argmax_chunks + accept_rows)", "bytes_per_call": nbytes,
+                "gbs_cold": round(nbytes / (out["us_per_call_cold"] * 1e-6) / 1e9, 1),
+                "note": "the step replays one logits buffer, so its accept reads them warm"})
+    return out
+
+
+def _threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline_long(I, torch):
+    """The fp64 oracle, as is, on ONE layer of the long-context step (B4,
+    32768 cached tokens: DIFF and AR block attention, greedy accept over
+    4 x 32 x 151936 logits, append), run once; a step is 36 such layers."""
+    from oracle import orthrus_oracle as O
+    x = I.make_attn_inputs("qwen3_8b_32k_b4", layer=0)
+    logits, t = I.make_logits(4, 32, I.QWEN3_VOCAB, seed=0, workload="qwen3_8b_32k_b4", plant=True)
+    prefix = I.geometric_prefix(4, 32, seed=0, workload="qwen3_8b_32k_b4")
+    drafts = I.make_drafts(t, prefix, I.QWEN3_VOCAB, seed=0).numpy()
+    t0 = time.perf_counter()
+    O.block_attn(x.q, x.k_cache, x.v_cache, x.k_blk, x.v_blk, x.page_table, x.ctx_lens, O.DIFF_BIDIR)
+    O.block_attn(x.q, x.k_cache, x.v_cache, x.k_blk, x.v_blk, x.page_table, x.ctx_lens, O.AR_CAUSAL)
+    acc, _, _ = O.greedy_accept(logits.numpy(), drafts)
+    O.kv_append(x.k_cache, x.v_cache, x.k_blk, x.v_blk, x.page_table, x.ctx_lens, acc)
+    el = time.perf_counter() - t0
+    kv = 2 * I.kv_bytes([32768] * 4, 8, 128, 2)
+    return {"workload": "qwen3_8b_32k_b4 step", "s_per_layer_step": round(el, 2),
+            "s_per_step_x36": round(36 * el, 1), "kv_gbs": round(kv / el / 1e9, 4), "cores": int(_threads()),
+            "sample": "one layer of the B4 x 32768-token step (both views over 4 sequences, accept over "
+                      "4x32x151936, append), run once; x36 for the 36-layer step"}
+
+
 def cpu_baseline(step, I, seconds):
     """The fp64 oracle, as is, on one layer of the step (both views, accept,
     append) at the same shapes; repeated for about `seconds`."""
@@ -414,6 +498,8 @@ def main():
     ms_call = 0.5 * (ms_diff + ms_ar)
     achieved = step.kv_bytes_call / (ms_call * 1e-3) / 1e9
     pct = lambda q: round(sorted(spread)[min(len(spread) - 1, int(q * len(spread)))] * 1e3, 3)
+    log("greedy accept, warm and cold")
+    accept = accept_timing(torch, ob, I, use_graph, step)
     log("achievable read and copy rates")
     read_gbs, copy_gbs = achievable_gbs(torch, ob)
     flops = 2 * 2 * step.B * step.K * step.Hq * step.D * (args.ctx + step.K)
@@ -486,6 +572,13 @@ def main():
         del s5, rep5
         torch.cuda.empty_cache()
 
+    conf2 = None
+    if not args.no_config2:
+        log("config 2 (Qwen3-1.7B attention shape)")
+        step = None
+        torch.cuda.empty_cache()
+        conf2 = config2_timing(torch, ob, I, use_graph)
+
     sample = None
     if not args.no_sample:
         log("sampled consensus")
@@ -512,6 +605,9 @@ def main():
         log("cpu baseline")
         s1 = step if step is not None else Step(ob, I, torch, args.batch, args.ctx, 1, args.split_tokens)
         cpu = cpu_baseline(s1, I, args.cpu_seconds)
+        if not args.no_long_context:
+            log("cpu baseline: one layer of the long-context step")
+            cpu["long_context_step"] = cpu_baseline_long(I, torch)
 
     line = {"metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
@@ -523,6 +619,7 @@ def main():
                        "graph": use_graph, "parallelism": "none (1 GPU)"},
             "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
             "roofline": roof, "cpu_baseline": cpu, "sweep": sweep or None, "long_context_step": longctx,
+            "config2": conf2, "greedy_accept": accept,
             "sample_accept": sample, "lm_head": lmhead, "prefill": pre}
     print(json.dumps(line), flush=True)
 

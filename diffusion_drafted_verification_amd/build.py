@@ -2,6 +2,9 @@
 diffusion_drafted_verification_amd/liborthrus_gfx950.so.
 
     python -m diffusion_drafted_verification_amd.build
+    python -m diffusion_drafted_verification_amd.build --sanitize   (the same
+        library with AddressSanitizer + UBSan on its host code, under
+        _build/sanitize, for the CPU tests of the argument validation)
 
 Each .hip source is compiled separately for gfx950 (hipcc cross-compiles
 without a GPU) and linked into one shared library whose only interface is
@@ -41,6 +44,61 @@ def compile_flags():
             "-munsafe-fp-atomics"]
 
 
+SANITIZE_DIR = os.path.join(BUILD, "sanitize")
+SANITIZE_LIB = os.path.join(SANITIZE_DIR, LIB_NAME)
+
+
+def sanitize_flags():
+    """AddressSanitizer and UndefinedBehaviorSanitizer on the host code only
+    (the C-ABI validation and launch set-up); the gfx950 device code is built
+    as usual, without sanitizers."""
+    return [*compile_flags(), "-Xarch_host", "-fsanitize=address,undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+            "-Xarch_host", "-fno-sanitize-recover=undefined"]
+
+
+def asan_runtime():
+    """Path of the compiler's AddressSanitizer runtime (to preload into a
+    Python process that loads the sanitized library), or None."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    base = os.path.join(rocm, "llvm", "lib", "clang")
+    if not os.path.isdir(base):
+        return None
+    for v in sorted(os.listdir(base), reverse=True):
+        p = os.path.join(base, v, "lib", "linux", "libclang_rt.asan-x86_64.so")
+        if os.path.exists(p):
+            return p
+    return None
+
+
+def build_sanitized(verbose=True, force=False):
+    """Build the sanitized library (skipped when it is newer than every source
+    and header it is built from, unless force)."""
+    os.makedirs(SANITIZE_DIR, exist_ok=True)
+    deps = [os.path.join(CSRC, f) for f in os.listdir(CSRC)] + [os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE)]
+    deps.append(os.path.abspath(__file__))
+    if not force and os.path.exists(SANITIZE_LIB) and \
+            os.path.getmtime(SANITIZE_LIB) > max(os.path.getmtime(p) for p in deps):
+        return SANITIZE_LIB
+
+    def one(src):
+        out = os.path.join(SANITIZE_DIR, src.replace(".hip", ".o"))
+        r = subprocess.run([hipcc(), *sanitize_flags(), "-c", os.path.join(CSRC, src), "-o", out],
+                           capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"hipcc (sanitized build) failed on {src}:\n{r.stderr}")
+        return out
+
+    with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
+        objs = list(ex.map(one, SOURCES))
+    r = subprocess.run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address,undefined",
+                        "-o", SANITIZE_LIB, *objs], capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link (sanitized build) failed:\n{r.stderr}")
+    if verbose:
+        print(f"built {SANITIZE_LIB}")
+    return SANITIZE_LIB
+
+
 def _compile(src):
     out = os.path.join(BUILD, src.replace(".hip", ".o"))
     cmd = [hipcc(), *compile_flags(), "-c", os.path.join(CSRC, src), "-o", out]
@@ -74,4 +132,7 @@ def build(verbose=True):
 
 
 if __name__ == "__main__":
-    build()
+    if "--sanitize" in sys.argv[1:]:
+        build_sanitized(force=True)
+    else:
+        build()

@@ -1537,7 +1537,7 @@ extern "C" int32_t orthrus_block_attn_split_tokens(const orthrus_attn_desc* desc
 
 orthrus_status orthrus::block_attn_run(const void* q, const void* k_cache, const void* v_cache, const void* k_blk,
                                        const void* v_blk, const int32_t* page_table, const int32_t* ctx_lens,
-                                       orthrus_mode mode, void* out, const orthrus_attn_desc* desc, void* workspace,
+                                       int32_t mode, void* out, const orthrus_attn_desc* desc, void* workspace,
                                        size_t workspace_bytes, void* stream, bool kv_read_once) {
   orthrus_status st = validate_desc(desc);
   if (st != ORTHRUS_OK) return st;
@@ -1600,7 +1600,7 @@ orthrus_status orthrus::block_attn_run(const void* q, const void* k_cache, const
 extern "C" orthrus_status orthrus_block_attn(const void* q, const void* k_cache, const void* v_cache,
                                              const void* k_blk, const void* v_blk,
                                              const int32_t* page_table, const int32_t* ctx_lens,
-                                             orthrus_mode mode, void* out, const orthrus_attn_desc* desc,
+                                             int32_t mode, void* out, const orthrus_attn_desc* desc,
                                              void* workspace, size_t workspace_bytes, void* stream) {
   // a decode call reads every cached K/V byte once
   return block_attn_run(q, k_cache, v_cache, k_blk, v_blk, page_table, ctx_lens, mode, out, desc, workspace,
@@ -1645,7 +1645,7 @@ static void* scratch_on(int dev) {
 extern "C" orthrus_status orthrus_block_attn_noalloc(const void* q, const void* k_cache, const void* v_cache,
                                                      const void* k_blk, const void* v_blk,
                                                      const int32_t* page_table, const int32_t* ctx_lens,
-                                                     orthrus_mode mode, void* out, const orthrus_attn_desc* desc,
+                                                     int32_t mode, void* out, const orthrus_attn_desc* desc,
                                                      void* stream) {
   orthrus_status st = validate_desc(desc);
   if (st != ORTHRUS_OK) return st;

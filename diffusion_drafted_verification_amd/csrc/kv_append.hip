@@ -179,7 +179,7 @@ extern "C" orthrus_status orthrus_copy_probe(void* dst, const void* src, size_t 
 
 extern "C" int32_t orthrus_abi_version(void) { return ORTHRUS_ABI_VERSION; }
 
-extern "C" const char* orthrus_status_str(orthrus_status s) {
+extern "C" const char* orthrus_status_str(int32_t s) {
   switch (s) {
     case ORTHRUS_OK: return "ok";
     case ORTHRUS_ERR_NULL: return "a required pointer is NULL";

@@ -49,10 +49,11 @@ inline orthrus_status validate_desc(const orthrus_attn_desc* d) {
 // orthrus_block_attn with the cache policy of the context K/V stream chosen
 // by the caller: kv_read_once streams it with the nontemporal hint (a decode
 // call reads each byte once); callers that re-read the same K/V across
-// launches in quick succession (the chunks of a prefill) pass false.
+// launches in quick succession (the chunks of a prefill) pass false.  mode
+// is checked here (an orthrus_mode value, else ORTHRUS_ERR_SHAPE).
 orthrus_status block_attn_run(const void* q, const void* k_cache, const void* v_cache, const void* k_blk,
                               const void* v_blk, const int32_t* page_table, const int32_t* ctx_lens,
-                              orthrus_mode mode, void* out, const orthrus_attn_desc* desc, void* workspace,
+                              int32_t mode, void* out, const orthrus_attn_desc* desc, void* workspace,
                               size_t workspace_bytes, void* stream, bool kv_read_once);
 
 }  // namespace orthrus

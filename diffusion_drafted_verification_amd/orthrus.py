@@ -22,7 +22,9 @@ SPLIT_BALANCED = -1   # split_tokens: chosen on the device from ctx_lens (ragged
 PAGE_SIZE = 16
 
 LIB_NAME = "liborthrus_gfx950.so"
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
+# the in-tree library; ORTHRUS_LIBRARY may name another build of it (the
+# sanitized host-only build that the CPU validation tests run against)
+LIB_PATH = os.environ.get("ORTHRUS_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), LIB_NAME)
 
 STATUS = {0: "ok", 1: "ERR_NULL", 2: "ERR_SHAPE", 3: "ERR_UNSUPPORTED", 4: "ERR_WORKSPACE", 5: "ERR_LAUNCH"}
 

@@ -123,7 +123,10 @@ typedef struct {
 } orthrus_attn_desc;
 
 int32_t orthrus_abi_version(void);
-const char* orthrus_status_str(orthrus_status s);
+/* Text of a status code (any int; unknown codes give "unknown status").
+ * Codes and modes cross the ABI as int32_t: a caller may pass any value, and
+ * the library checks it before treating it as one of the enumerations. */
+const char* orthrus_status_str(int32_t status);
 
 /* Bytes of caller-provided scratch orthrus_block_attn needs for `desc`
  * (split-context partial results: bf16 for bf16 storage with Hq/Hkv <= 4,
@@ -140,6 +143,7 @@ int32_t orthrus_block_attn_split_tokens(const orthrus_attn_desc* desc);
 
 /* Block attention of one decode step (explainer §2.1-§2.3).
  *
+ * mode is an orthrus_mode value (anything else: ORTHRUS_ERR_SHAPE).
  * For every sequence b (L = ctx_lens[b]), query head h and block row i < K:
  *   keys/values = the L cached rows of KV head h*Hkv/Hq followed by the K
  *   block rows k_blk/v_blk[b, :, h*Hkv/Hq]; row i sees all L cached keys and
@@ -151,7 +155,7 @@ int32_t orthrus_block_attn_split_tokens(const orthrus_attn_desc* desc);
  * when orthrus_block_attn_workspace_bytes(desc) == 0. */
 orthrus_status orthrus_block_attn(const void* q, const void* k_cache, const void* v_cache,
                                   const void* k_blk, const void* v_blk, const int32_t* page_table,
-                                  const int32_t* ctx_lens, orthrus_mode mode, void* out,
+                                  const int32_t* ctx_lens, int32_t mode, void* out,
                                   const orthrus_attn_desc* desc, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
@@ -177,7 +181,7 @@ orthrus_status orthrus_block_attn(const void* q, const void* k_cache, const void
  * on one stream are safe. */
 orthrus_status orthrus_block_attn_noalloc(const void* q, const void* k_cache, const void* v_cache,
                                           const void* k_blk, const void* v_blk, const int32_t* page_table,
-                                          const int32_t* ctx_lens, orthrus_mode mode, void* out,
+                                          const int32_t* ctx_lens, int32_t mode, void* out,
                                           const orthrus_attn_desc* desc, void* stream);
 
 /* Bytes of the workspace orthrus_greedy_accept needs (one 8-byte key per
