@@ -1397,6 +1397,21 @@ int attn_split_tokens(const orthrus_attn_desc& d) {
   const long Tm = (Lm + kTile - 1) / kTile;
   const int Q = attn_round_slots(d);
   auto count = [&](int t) { return (long)d.batch * ceil_div(Tm, t); };
+  // One short sequence (each work-group has at most 8 stages): the call is
+  // bound by per-work-group latency, and the best measured fill is about
+  // 80 % of a round with at least 3 stages per work-group (B1: 192-position
+  // splits ran 6-9 % faster than 320 at 2048 and 4096 tokens with Qwen3-8B
+  // heads and at 2048 with Qwen3-1.7B heads; at 8192 tokens this picks 320,
+  // which beat 256 and 192).
+  if (d.batch == 1) {
+    const int Q80 = (Q * 13) / 16;
+    int t = 3;
+    while (t <= 8 && count(t) > Q80) ++t;
+    if (t <= 8) {
+      const long split = (long)t * kTile;
+      return (int)(split < l64 ? split : l64);
+    }
+  }
   int lo = kBalMinTiles, hi = kBalMaxTiles;
   if (count(hi) > Q) {
     lo = hi;

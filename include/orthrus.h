@@ -104,9 +104,13 @@ typedef enum {
  *                       in [64, 8192]; 0 = automatic (the shortest split,
  *                       at least 320, that keeps a batch of max_ctx_len
  *                       contexts within one round of ceil(256 / Hkv)
- *                       work-groups per KV head; the best choice when the
- *                       lengths are equal); ORTHRUS_SPLIT_BALANCED = chosen
- *                       on the device from ctx_lens (ragged batches, below) */
+ *                       work-groups per KV head; for one sequence whose
+ *                       context then needs at most 8 stages of 64 positions
+ *                       per work-group, the shortest split of at least 192
+ *                       that fills about 80 % of a round instead; the best
+ *                       measured choices when the lengths are equal);
+ *                       ORTHRUS_SPLIT_BALANCED = chosen on the device from
+ *                       ctx_lens (ragged batches, below) */
 typedef struct {
   int32_t batch;
   int32_t block_k;
