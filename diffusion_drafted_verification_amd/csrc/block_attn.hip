@@ -1372,6 +1372,289 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_stream(AttnArgs a) {
     a.ws_ml[part * kRows + i] = make_float2(row_m, row_l);
 }
 
+// Prompt prefill tile (AR_CAUSAL, bf16, G <= 4).  A prefill runs the
+// prompt's 32-row chunks as virtual sequences of this layout (chunk j of
+// sequence b: a causal block after L_b + 32 j cached tokens), C chunks per
+// sequence.  One work-group serves a PAIR of consecutive chunks (2j', 2j'+1)
+// of one sequence for KV head g and context split s.  Wave w owns query head
+// g G + w % G on the 32 rows of chunk 2j' + w / G and computes every position
+// of each 64-position stage (two 32-position score tiles), so each K/V byte
+// the work-group streams serves 64 G query rows instead of the 32 G of
+// attn_stream: the re-reads of a long prompt's prefix, which bound the
+// chunked prefill, halve.
+//
+// The stream covers the first chunk's context (L0 cached positions, read
+// through the page table) and then the pair's 64 prompt rows (read from the
+// prompt's own k/v, as block keys).  For the second chunk the first chunk's
+// rows are cached context; they are the same values.  Each chunk keeps its
+// own split partition, the one the combine derives from its context length:
+// in the first chunk's last split the second chunk's waves mask positions
+// past their own split end, and where only the second chunk has a split left
+// the first chunk's waves run with every position masked and write nothing.
+// Outputs and partials use the per-chunk rows of the virtual batch, so the
+// combine kernel is shared with attn_stream.
+template <int D, int G>
+__global__ void __launch_bounds__(2 * kWave * G) attn_prefill_pair(AttnArgs a, int C) {
+  typedef StreamLayout<D> Lay;
+  typedef DmaPlan<D, 2 * G> Plan;
+  constexpr int NW = 2 * G;
+  constexpr int KS = D / 16;
+  constexpr int MB = D / 32;
+  constexpr int QR = G * D * 2;                            // bytes of one row's G query heads
+  constexpr int QB = 2 * kRows * QR;                       // the pair's 64 query rows
+  constexpr int NQB = (QB + Lay::STAGE - 1) / Lay::STAGE;  // stage buffers they occupy
+  static_assert(NQB == 1 || NQB == 2, "the pair's query rows fit two stage buffers");
+  static_assert(QR <= 1024 && 1024 % QR == 0, "whole rows per DMA instruction");
+
+  __shared__ __attribute__((aligned(1024))) char st0[Lay::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[Lay::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st2[Lay::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st3[Lay::STAGE];
+  __shared__ __attribute__((aligned(16))) int pages[kMaxSplit / kPage];
+
+  // block id = s * (pairs * Hkv) + pair * Hkv + g: the work-groups of one KV
+  // head share an XCD; pairs in reverse order (the longest, latest chunks
+  // first)
+  const int PC = (C + 1) / 2;
+  const int NP = (a.B / C) * PC;
+  const int BH = NP * a.Hkv;
+  const int bg = blockIdx.x % BH;
+  const int g = bg % a.Hkv;
+  const int s = blockIdx.x / BH;
+  const int pb = NP - 1 - bg / a.Hkv;
+  const int jp = pb % PC;
+  const int vb0 = (pb / PC) * C + 2 * jp;  // the pair's first chunk
+  const bool has1 = 2 * jp + 1 < C;        // a second chunk exists
+  const int split = a.split;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int i = lane & 31, hi = lane >> 5;
+  const int hw = wave % G, rb = wave / G;
+  const int h = g * G + hw;
+
+  int L0 = a.ctx_lens[vb0];
+  L0 = L0 < 0 ? 0 : (L0 > a.max_ctx ? a.max_ctx : L0);
+  // each chunk's split count and the end of its range in split s
+  auto splits_of = [&](int Lc) { return Lc > 0 ? (Lc + split - 1) / split : 1; };
+  const int L1 = L0 + kRows;
+  const int S0 = splits_of(L0), S1 = splits_of(L1);
+  const int p_begin = s * split;
+  const int e0 = s < S0 ? (s == S0 - 1 ? L0 + kRows : p_begin + split) : p_begin;
+  const int e1 = has1 && s < S1 ? (s == S1 - 1 ? L1 + kRows : p_begin + split) : p_begin;
+  const int p_end = e0 > e1 ? e0 : e1;  // the stream: both chunks' ranges in split s
+  if (p_end <= p_begin) return;         // uniform over the work-group
+  const int ntiles = (p_end - p_begin + kTile - 1) / kTile;
+  // this wave's chunk: context Lw, its range ends at pew (p_begin: no split s)
+  const int Lw = rb == 0 ? L0 : L1;
+  const int pew = rb == 0 ? e0 : e1;
+  const int Sw = rb == 0 ? S0 : S1;
+  const int vbw = vb0 + rb;
+  const int page_base = p_begin >> 4;
+
+  // ---- prologue: the split's page ids and the pair's query rows reach LDS
+  // by DMA before the first stages, so the hand-placed vmcnt waits stay exact
+  {
+    const int npt = min(split / kPage, a.max_pages - page_base);
+    const int* prow = a.page_table + (size_t)vb0 * a.max_pages + page_base;
+    for (int k = wave; k * kWave < npt; k += NW) {
+      const int x = k * kWave + lane;
+      dma4(prow + (x < npt ? x : 0), reinterpret_cast<char*>(pages) + k * kWave * 4);
+    }
+  }
+  // query row r (0..63) of the pair: QR bytes at byte r QR of the query
+  // area (st3, or st2 then st3), its 16-byte chunks XOR-swizzled by (r & QSW);
+  // rows of a missing second chunk read row 0 (never used)
+  constexpr int QCH = QR / 16;
+  constexpr int QSW = (QCH < 16 ? QCH : 16) - 1;
+  constexpr int RQ = 1024 / QR;
+  char* const qarea0 = NQB == 2 ? st2 : st3;
+  auto qaddr = [&](int off) -> char* { return off < Lay::STAGE ? qarea0 + off : st3 + (off - Lay::STAGE); };
+  for (int k = wave; k < 2 * kRows / RQ; k += NW) {
+    const int row = k * RQ + lane / QCH, slot = lane % QCH;
+    const int src_row = row < kRows || has1 ? vb0 * kRows + row : vb0 * kRows;
+    const char* src = a.q + ((size_t)src_row * a.Hq + g * G) * D * 2 + ((slot ^ (row & QSW)) << 4);
+    dma16(src, qaddr(k * 1024));
+  }
+  // K/V stages 0 .. NPRO_ST - 1 (the ring's other buffers hold the queries)
+  constexpr int NPRO_ST = kRing - NQB;
+  char* const ring[kRing] = {st0, st1, st2, st3};
+  wait_vmcnt<0>();  // this wave's page-table and query DMA
+  __syncthreads();  // the split's page ids are in LDS
+#pragma unroll
+  for (int u = 0; u < NPRO_ST; ++u)
+    Plan::issue(ring[u], a, pages, page_base, vb0, g, L0, p_end, p_begin + u * kTile, wave, lane);
+  // stage 0 landed (the later prologue stages may still fly when all of
+  // them were issued)
+  if (ntiles >= NPRO_ST) wait_vmcnt<(NPRO_ST - 1) * Plan::NS>();
+  else wait_vmcnt<0>();
+  barrier_no_fence();
+  typedef bf16x8 V8;
+  V8 qf[KS];
+  {
+    const int r = kRows * rb + i;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int chunk = (hw * (D * 2 / 16) + 2 * ks + hi) ^ (r & QSW);
+      qf[ks] = __builtin_bit_cast(V8, *reinterpret_cast<const u32x4*>(qaddr(r * QR + chunk * 16)));
+    }
+  }
+
+  f32x16 o[MB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[m][r] = 0.f;
+  float m_c = -INFINITY;
+  float l = 0.f;
+  const float c = a.c;
+  const int kofs = i * Lay::ROWB + ((hi ^ (i & Lay::KSW)) << 4);
+  const int s16 = lane & 15, g2 = (lane >> 4) & 1;
+  const int vrow = s16 >> 2;
+  const int vchunk = (2 * g2 + ((s16 >> 1) & 1)) ^ Lay::vswz(vrow);
+  const int vofs = (8 * hi + vrow) * Lay::ROWB + (vchunk << 4) + 8 * (s16 & 1);
+
+  // One 32-position tile (positions 32 q .. 32 q + 31 of a stage) at a time,
+  // with online softmax per tile: the scores of the next tile (the stage's
+  // second tile, or the next stage's first) are computed before this tile's
+  // softmax, so their MFMAs can issue beside its exponentials, and only two
+  // score tiles are live (the register budget of two waves per SIMD).
+  auto qk = [&](const char* stage, int q, f32x16& sc) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const V8 av = __builtin_bit_cast(V8, ld16(stage + q * kRows * Lay::ROWB + (kofs ^ (ks << 5))));
+      sc = mfma_step(av, qf[ks], sc);
+    }
+  };
+  // mask (this wave's causal rows and range), row max, lazy rescale
+  const int vis_end = Lw < pew ? Lw : pew;  // below it every position is visible
+  auto sm_max = [&](f32x16& sc, int pbase) {
+    // sc[r]: position pbase + 16 (r / 8) + 8 hi + r % 8, row i
+    if (pbase + 32 > vis_end) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int pos = pbase + 16 * (r >> 3) + 8 * hi + (r & 7);
+        const bool vis = pos < pew && (pos < Lw || pos - Lw <= i);
+        if (!vis) sc[r] = -INFINITY;
+      }
+    }
+    float mx = sc[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+    mx = wave_max_xor32(mx);
+    const bool need = mx * c > m_c + kRescaleLog2;
+    if (__any(need)) {
+      const float new_mc = need ? mx * c : m_c;
+      const float f = (new_mc == m_c) ? 1.f : __builtin_amdgcn_exp2f(m_c - new_mc);
+#pragma unroll
+      for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[m][r] *= f;
+      l *= f;
+      m_c = new_mc;
+    }
+    return (m_c == -INFINITY) ? 0.f : m_c;
+  };
+  auto sm_exp = [&](f32x16& sc, float mref, V8& p0, V8& p1) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sc[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], c, -mref));
+      l += sc[r];
+    }
+    p0 = pack_p<bf16>(sc, 0);
+    p1 = pack_p<bf16>(sc, 1);
+  };
+  auto pv = [&](const char* stage, int q, const V8& p0, const V8& p1) {
+    const char* vt = stage + Lay::TILEB + q * kRows * Lay::ROWB;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const char* vb = vt + 16 * j * Lay::ROWB;
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        const int off = vofs ^ (m << 6);
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((ORTHRUS_LDS bf16x4*)(vb + off));
+        const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((ORTHRUS_LDS bf16x4*)(vb + 4 * Lay::ROWB + off));
+        V8 av;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          av[e] = lo[e];
+          av[4 + e] = hi4[e];
+        }
+        o[m] = mfma_step(av, j == 0 ? p0 : p1, o[m]);
+      }
+    }
+  };
+
+  // scores[q] holds the scores of tile q of the current stage
+  f32x16 scores[2];
+  qk(ring[0], 0, scores[0]);
+  for (int t0 = 0; t0 < ntiles; t0 += kRing) {
+#pragma unroll
+    for (int u = 0; u < kRing; ++u) {
+      const int t = t0 + u;
+      if (t >= ntiles) break;
+      // stage t+1 must have landed (the loads of stage t+2 may still fly;
+      // with two query buffers, stage 2 is issued only below, at t = 0)
+      if (NQB == 2 && t == 0) wait_vmcnt<0>();
+      else if (t + 2 < ntiles) wait_vmcnt<Plan::NS>();
+      else wait_vmcnt<0>();
+      barrier_no_fence();
+      if (NQB == 2 && t == 0)  // st2 held query rows until this barrier
+        Plan::issue(ring[2], a, pages, page_base, vb0, g, L0, p_end, p_begin + 2 * kTile, wave, lane);
+      Plan::issue(ring[(u + kRing - 1) % kRing], a, pages, page_base, vb0, g, L0, p_end,
+                  p_begin + (t + kRing - 1) * kTile, wave, lane);
+      const char* cur = ring[u];
+      const char* nxt = ring[(u + 1) % kRing];
+      const int pbase = p_begin + t * kTile;
+      // Past the last stage the next tile's QK reads a stale buffer whose
+      // scores are never used.
+      V8 p0, p1;
+      float mref = sm_max(scores[0], pbase);
+      qk(cur, 1, scores[1]);
+      sm_exp(scores[0], mref, p0, p1);
+      pv(cur, 0, p0, p1);
+      mref = sm_max(scores[1], pbase + kRows);
+      qk(nxt, 0, scores[0]);
+      sm_exp(scores[1], mref, p0, p1);
+      pv(cur, 1, p0, p1);
+    }
+  }
+  wait_vmcnt<0>();  // no DMA outlives the loop
+  if (pew <= p_begin) return;  // this chunk has no split s (or does not exist)
+
+  // ---- epilogue: every wave holds whole rows; the two lanes of a row
+  // (hi = 0, 1) add their halves of the row sum
+  const float row_l = l + __shfl_xor(l, 32, kWave);
+  const float inv = 1.f / row_l;
+  const size_t part = (size_t)(vbw * a.Hq + h) * a.s_max + s;
+  auto pack2 = [](float x, float y) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (bf16)x) | ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)y) << 16);
+  };
+  char* const row_out = Sw == 1 ? a.out + ((size_t)(vbw * a.K + i) * a.Hq + h) * D * 2
+                                : reinterpret_cast<char*>(a.ws_p) + (part * kRows + i) * D * 2;
+  // lane (i, hi) holds d = 32 m + 8 rg + 4 hi + e at o[m][4 rg + e]; one
+  // permlane32 swap per register pair gives each lane 8 consecutive
+  // elements d = 32 m + 16 hi + 8 j + (0..7) for one 16-byte store
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    uint32_t pk[4][2];
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      pk[rg][0] = pack2(o[m][4 * rg] * inv, o[m][4 * rg + 1] * inv);
+      pk[rg][1] = pack2(o[m][4 * rg + 2] * inv, o[m][4 * rg + 3] * inv);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const auto s0 = __builtin_amdgcn_permlane32_swap(pk[j][0], pk[j + 2][0], false, false);
+      const auto s1 = __builtin_amdgcn_permlane32_swap(pk[j][1], pk[j + 2][1], false, false);
+      const int d0 = 32 * m + 16 * hi + 8 * j;
+      *reinterpret_cast<u32x4*>(row_out + d0 * 2) = u32x4{s0[0], s1[0], s0[1], s1[1]};
+    }
+  }
+  if (Sw > 1 && hi == 0) a.ws_ml[part * kRows + i] = make_float2(m_c, row_l);
+}
+
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
@@ -1431,7 +1714,7 @@ static int attn_s_max(const orthrus_attn_desc& d, int split) {
 }
 
 // bf16 with up to 4 query heads per KV head runs the LDS-DMA streaming
-// kernel (in-kernel split merge); everything else the register-staged kernel
+// kernel plus attn_combine_bf16; everything else the register-staged kernel
 // plus attn_combine
 static bool attn_stream_path(const orthrus_attn_desc& d) {
   return d.dtype == ORTHRUS_BF16 && d.n_q_heads / d.n_kv_heads <= 4;
@@ -1526,6 +1809,27 @@ static hipError_t launch_attn(const AttnArgs& a, int mode, hipStream_t stream) {
   return launch_combine<T, D, stream_path>(a, stream);
 }
 
+// a prefill's virtual batch (C chunks per sequence) on the pair kernel,
+// then the combine of its split partials
+template <int D, int G>
+static hipError_t launch_prefill_pair(const AttnArgs& a, int C, hipStream_t stream) {
+  const int pairs = (a.B / C) * ((C + 1) / 2);
+  hipLaunchKernelGGL((attn_prefill_pair<D, G>), dim3(a.s_max * pairs * a.Hkv), dim3(2 * kWave * G), 0, stream, a,
+                     C);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.s_max <= 1) return e;
+  return launch_combine<bf16, D, true>(a, stream);
+}
+
+template <int D>
+static hipError_t dispatch_prefill_pair(const AttnArgs& a, int G, int C, hipStream_t s) {
+  switch (G) {
+    case 1: return launch_prefill_pair<D, 1>(a, C, s);
+    case 2: return launch_prefill_pair<D, 2>(a, C, s);
+    default: return launch_prefill_pair<D, 4>(a, C, s);
+  }
+}
+
 template <typename T, int D>
 static hipError_t dispatch_g(const AttnArgs& a, int G, int mode, hipStream_t s) {
   switch (G) {
@@ -1553,7 +1857,7 @@ extern "C" int32_t orthrus_block_attn_split_tokens(const orthrus_attn_desc* desc
 orthrus_status orthrus::block_attn_run(const void* q, const void* k_cache, const void* v_cache, const void* k_blk,
                                        const void* v_blk, const int32_t* page_table, const int32_t* ctx_lens,
                                        int32_t mode, void* out, const orthrus_attn_desc* desc, void* workspace,
-                                       size_t workspace_bytes, void* stream, bool kv_read_once) {
+                                       size_t workspace_bytes, void* stream, bool kv_read_once, int pair_chunks) {
   orthrus_status st = validate_desc(desc);
   if (st != ORTHRUS_OK) return st;
   if (!q || !k_cache || !v_cache || !k_blk || !v_blk || !page_table || !ctx_lens || !out)
@@ -1605,7 +1909,11 @@ orthrus_status orthrus::block_attn_run(const void* q, const void* k_cache, const
   const int G = d.n_q_heads / d.n_kv_heads;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
-  if (d.dtype == ORTHRUS_BF16)
+  if (pair_chunks > 0 && attn_stream_path(d) && mode == ORTHRUS_AR_CAUSAL && !plan.bal && d.block_k == kRows &&
+      d.batch % pair_chunks == 0)
+    e = d.head_dim == 128 ? dispatch_prefill_pair<128>(a, G, pair_chunks, s)
+                          : dispatch_prefill_pair<64>(a, G, pair_chunks, s);
+  else if (d.dtype == ORTHRUS_BF16)
     e = d.head_dim == 128 ? dispatch_g<bf16, 128>(a, G, mode, s) : dispatch_g<bf16, 64>(a, G, mode, s);
   else
     e = d.head_dim == 128 ? dispatch_g<float, 128>(a, G, mode, s) : dispatch_g<float, 64>(a, G, mode, s);

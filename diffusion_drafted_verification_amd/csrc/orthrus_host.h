@@ -51,9 +51,13 @@ inline orthrus_status validate_desc(const orthrus_attn_desc* d) {
 // call reads each byte once); callers that re-read the same K/V across
 // launches in quick succession (the chunks of a prefill) pass false.  mode
 // is checked here (an orthrus_mode value, else ORTHRUS_ERR_SHAPE).
+// pair_chunks > 0 marks a prefill's virtual batch (pair_chunks 32-row chunks
+// per sequence, chunk j after L_b + 32 j cached tokens, the prompt as the
+// block keys): on the streaming path its AR_CAUSAL call runs the pair
+// kernel, one work-group per two consecutive chunks.
 orthrus_status block_attn_run(const void* q, const void* k_cache, const void* v_cache, const void* k_blk,
                               const void* v_blk, const int32_t* page_table, const int32_t* ctx_lens,
                               int32_t mode, void* out, const orthrus_attn_desc* desc, void* workspace,
-                              size_t workspace_bytes, void* stream, bool kv_read_once);
+                              size_t workspace_bytes, void* stream, bool kv_read_once, int pair_chunks = 0);
 
 }  // namespace orthrus

@@ -104,6 +104,21 @@ static orthrus_status prefill_desc(const orthrus_attn_desc* d, int32_t max_promp
 
 static size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Chunks per attention work-group for the virtual batch vd of B sequences
+// with C chunks each: 2 (the pair kernel: bf16 with G <= 4) when that grid
+// still fills two rounds of 256 work-groups, else 1.  A pair does twice the
+// work of a chunk, so with fewer work-groups the longest pair sets the time.
+// Measured on the Qwen3-8B shape (one layer): an 8192-token prompt 750 ->
+// 689 us and a 2048-token prompt after 8192 cached tokens 461 -> 424 us with
+// pairs, but a 2048-token prompt on an empty cache (one round of pairs)
+// 76.5 -> 95 us.
+static int prefill_chunks_per_wg(const orthrus_attn_desc& vd, int B, int C) {
+  if (vd.dtype != ORTHRUS_BF16 || vd.n_q_heads / vd.n_kv_heads > 4) return 1;
+  const long splits = vd.max_ctx_len > 0 ? ((long)vd.max_ctx_len + vd.split_tokens - 1) / vd.split_tokens : 1;
+  const long grid = splits * B * ((C + 1) / 2) * vd.n_kv_heads;
+  return grid >= 2 * 256 ? 2 : 1;
+}
+
 struct PrefillWs {
   size_t off_ctx, off_attn, attn_bytes, total;
 };
@@ -126,6 +141,13 @@ extern "C" size_t orthrus_prefill_workspace_bytes(const orthrus_attn_desc* desc,
   int C, S;
   if (prefill_desc(desc, max_prompt, &vd, &C, &S) != ORTHRUS_OK) return 0;
   return prefill_ws(vd).total;
+}
+
+extern "C" int32_t orthrus_prefill_chunks_per_workgroup(const orthrus_attn_desc* desc, int32_t max_prompt) {
+  orthrus_attn_desc vd;
+  int C, S;
+  if (prefill_desc(desc, max_prompt, &vd, &C, &S) != ORTHRUS_OK) return 0;
+  return prefill_chunks_per_wg(vd, desc->batch, C);
 }
 
 extern "C" orthrus_status orthrus_prefill(const void* q, const void* k, const void* v, void* k_cache, void* v_cache,
@@ -173,5 +195,6 @@ extern "C" orthrus_status orthrus_prefill(const void* q, const void* k, const vo
   if (hipGetLastError() != hipSuccess) return ORTHRUS_ERR_LAUNCH;
   // the chunks re-read the prompt's K/V through the caches: ordinary loads
   return block_attn_run(q, k_cache, v_cache, k, v, a.vtable, a.vctx, ORTHRUS_AR_CAUSAL, out, &vd,
-                        w.attn_bytes ? ws + w.off_attn : nullptr, w.attn_bytes, stream, false);
+                        w.attn_bytes ? ws + w.off_attn : nullptr, w.attn_bytes, stream, false,
+                        prefill_chunks_per_wg(vd, desc->batch, C) == 2 ? C : 0);
 }

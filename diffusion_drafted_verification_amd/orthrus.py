@@ -62,6 +62,7 @@ SIGNATURES = {
     "orthrus_kv_append": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _DESC_P, _vp]),
     "orthrus_kv_append_layers": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _DESC_P, _vp]),
     "orthrus_prefill_workspace_bytes": (_sz, [_DESC_P, _i32]),
+    "orthrus_prefill_chunks_per_workgroup": (_i32, [_DESC_P, _i32]),
     "orthrus_prefill": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _DESC_P, _vp, _sz, _vp]),
     "orthrus_copy_probe": (_i32, [_vp, _vp, _sz, _vp]),
     "orthrus_read_probe": (_i32, [_vp, _sz, _vp, _sz, _vp]),
@@ -460,6 +461,20 @@ def prefill(q, k, v, k_cache, v_cache, page_table, ctx_lens, prompt_lens, max_pr
                                ctypes.byref(desc), _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "orthrus_prefill")
     return out, new_ctx_lens
+
+
+def prefill_chunks_per_workgroup(q, k_cache, page_table, max_prompt, *, max_ctx_len=None, split_tokens=0):
+    """orthrus_prefill_chunks_per_workgroup for the shape `prefill` would
+    get with these arguments: 2 when one attention work-group serves two
+    32-row chunks, else 1."""
+    S = q.shape[1]
+    if max_ctx_len is None:
+        max_ctx_len = page_table.shape[1] * PAGE_SIZE - S
+    desc = make_desc(q[:, :32], k_cache, page_table, max_ctx_len, None, split_tokens)
+    n = lib().orthrus_prefill_chunks_per_workgroup(ctypes.byref(desc), int(max_prompt))
+    if n == 0:
+        raise OrthrusError("orthrus_prefill_chunks_per_workgroup: invalid shape")
+    return n
 
 
 def copy_probe(dst, src, stream=None):

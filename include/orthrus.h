@@ -346,6 +346,14 @@ orthrus_status orthrus_kv_append_layers(const uint64_t* k_cache_ptrs, const uint
  * needs no initialisation; it must be 256-byte aligned. */
 size_t orthrus_prefill_workspace_bytes(const orthrus_attn_desc* desc, int32_t max_prompt);
 
+/* How many of the prompt's 32-row chunks one attention work-group of
+ * orthrus_prefill serves for this shape: 2 when the work-groups of chunk
+ * pairs still fill two rounds of the GPU (bf16 with at most 4 query heads per
+ * KV head; each work-group then streams its keys once for both chunks), else
+ * 1.  0 for an invalid shape.  Informational: the results do not depend on
+ * it beyond rounding order. */
+int32_t orthrus_prefill_chunks_per_workgroup(const orthrus_attn_desc* desc, int32_t max_prompt);
+
 /* Prompt prefill by the frozen AR head (explainer §2.1: the prompt's keys
  * and values fill the shared cache that both views read).  For sequence b
  * with L = ctx_lens[b] tokens already cached and n = prompt_lens[b] prompt

@@ -24,7 +24,7 @@ def declared_entry_points():
 
 def test_exports_every_declared_symbol():
     names = declared_entry_points()
-    assert len(names) == 23
+    assert len(names) == 24
     assert set(names) == set(B.SIGNATURES)
     lib = B.lib()
     for n in names:
@@ -80,6 +80,22 @@ def test_block_attn_rejects_null_mode_and_workspace():
     assert attn(d) == 4                                   # workspace missing
     assert attn(d, ws=FAKE, ws_bytes=need - 1) == 4       # too small
     assert attn(d, ws=ctypes.c_void_p(4100), ws_bytes=need) == 4   # misaligned
+
+
+def test_prefill_chunks_per_workgroup():
+    """The pair kernel (two 32-row chunks per work-group) runs where its grid
+    fills two rounds of 256 work-groups: the Qwen3-8B 8192-token prompt (128
+    pairs x 8 KV heads) and the 2048-token prompt after 8192 cached tokens (two
+    splits), not the 2048-token prompt alone (one round); never for fp32 or
+    G = 8 (no streaming kernel); 0 for an invalid shape."""
+    f = lambda d, mp: B.lib().orthrus_prefill_chunks_per_workgroup(ctypes.byref(d), mp)
+    pages = lambda n: dict(max_pages_per_seq=n, num_pages=n)
+    assert f(good_desc(max_ctx_len=0, **pages(512)), 8192) == 2
+    assert f(good_desc(max_ctx_len=0, **pages(128)), 2048) == 1
+    assert f(good_desc(max_ctx_len=8192, **pages(640)), 2048) == 2
+    assert f(good_desc(max_ctx_len=0, dtype=1, **pages(512)), 8192) == 1
+    assert f(good_desc(max_ctx_len=0, n_q_heads=64, **pages(512)), 8192) == 1
+    assert f(good_desc(max_ctx_len=0, **pages(512)), 0) == 0
 
 
 def test_split_and_workspace_arithmetic():

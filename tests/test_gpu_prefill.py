@@ -102,6 +102,35 @@ def test_prefill_split_lengths(split):
     run_prefill(x, split=split)
 
 
+def run_prefill_pairs(x, split):
+    """run_prefill on a shape that takes the pair kernel (two chunks per
+    attention work-group)."""
+    assert ob().prefill_chunks_per_workgroup(x["q"], x["k_cache"], x["page_table"], x["max_prompt"],
+                                             max_ctx_len=x["max_ctx_len"], split_tokens=split) == 2
+    return run_prefill(x, split=split)
+
+
+@pytest.mark.parametrize("split,G,D", [(64, 4, 128), (128, 4, 128), (64, 2, 128), (128, 1, 128), (64, 4, 64)])
+def test_prefill_split_boundary_at_chunk_pair(split, G, D):
+    """Contexts L_b + 64 j that are multiples of the split: chunk 2j's last
+    split ends at its block while chunk 2j + 1 (32 positions more context)
+    needs one more split, so a work-group serving both chunks computes one
+    chunk's split alone or masks the other's range.  Four sequences and 8 KV
+    heads make the grid large enough for the pair kernel."""
+    say("prefill pairs, split boundary", split, G, D)
+    x = I.make_prefill_inputs([0, split, 2 * split, 3 * split], [200, 200, 171, 200], 8 * G, 8, D,
+                              seed=split + G + D)
+    run_prefill_pairs(x, split)
+
+
+def test_prefill_pairs_ragged_batch_short_splits():
+    """Odd chunk counts in a batch (no chunk may pair with the next
+    sequence's first chunk) with many splits per chunk, on the pair kernel."""
+    say("prefill pairs, ragged short splits")
+    x = I.make_prefill_inputs([0, 700, 33], [100, 257, 1], 16, 8, 128, seed=13)
+    run_prefill_pairs(x, 64)
+
+
 def test_prefill_qwen3_8b_2k_prompt_sampled():
     """A 2048-token prompt at the Qwen3-8B attention shape after 4096 cached
     tokens, compared on sampled heads and rows (the oracle is slow)."""
@@ -118,6 +147,8 @@ def test_prefill_qwen3_8b_benchmark_shapes_sampled(L, S):
     split), compared on sampled heads and rows."""
     say("prefill qwen3-8b benchmark shape", L, S)
     x = I.make_prefill_inputs([L], [S], 32, 8, 128, seed=L + S)
+    assert ob().prefill_chunks_per_workgroup(x["q"], x["k_cache"], x["page_table"], x["max_prompt"],
+                                             max_ctx_len=x["max_ctx_len"]) == 2
     run_prefill(x, heads=[0, 14, 31], rows=[0, 31, 32, S // 2 - 1, S // 2, S - 33, S - 1])
 
 
