@@ -847,46 +847,6 @@ struct StreamLayout {
   __device__ static int vswz(int row) { return D == 128 ? (row & 3) << 2 : ((row >> 1) & 1) << 2; }
 };
 
-#define ORTHRUS_LDS __attribute__((address_space(3)))
-
-// One wave instruction of the LDS-DMA path: lane l copies 16 bytes from its
-// global address to LDS address (dst + 16 l).  Written as inline assembly so
-// that the compiler does not track these LDS writes: the kernel orders them
-// itself (s_waitcnt vmcnt + barrier before any wave reads a stage).  The
-// instruction has no register result; M0 holds the wave-uniform LDS base
-// (one wait state after writing M0 before the load reads it).
-__device__ __forceinline__ void dma16(const void* src, char* dst) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(
-      (uint32_t)reinterpret_cast<uintptr_t>((ORTHRUS_LDS char*)dst));
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(lds) : "memory");
-}
-
-// The same with the nontemporal hint: context K/V that a call reads exactly
-// once streams past the caches (measured on the Qwen3-8B shape: 9 % faster
-// at batch 1, a few % at batch 4 to 16; slower where the data is re-read, as
-// across the chunks of a prefill).
-__device__ __forceinline__ void dma16_nt(const void* src, char* dst) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(
-      (uint32_t)reinterpret_cast<uintptr_t>((ORTHRUS_LDS char*)dst));
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(src), "{m0}"(lds) : "memory");
-}
-
-// a K/V stage load: one instruction either way (the hand-placed vmcnt
-// counts do not change); `once` is uniform (a kernel argument)
-__device__ __forceinline__ void dma16_kv(const void* src, char* dst, int once) {
-  if (once)
-    dma16_nt(src, dst);
-  else
-    dma16(src, dst);
-}
-
-// The same with 4 bytes per lane (lane l writes dst + 4 l).
-__device__ __forceinline__ void dma4(const void* src, char* dst) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(
-      (uint32_t)reinterpret_cast<uintptr_t>((ORTHRUS_LDS char*)dst));
-  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, off" ::"v"(src), "{m0}"(lds) : "memory");
-}
-
 // a page id as used: ids outside [0, num_pages) read page 0 instead (results
 // for such positions are unspecified, but every access stays in bounds)
 __device__ __forceinline__ int valid_page(int p, int num_pages) {
@@ -978,32 +938,6 @@ struct DmaPlan {
       issue_tail(st, a, pages, page_base, b, g, L, p_end, p0, wave, lane);
   }
 };
-
-// wait until at most N of this wave's vector loads are outstanding.  Inline
-// assembly, like the DMA itself: the compiler does not count the DMA loads, so
-// the kernel places these waits by hand (only LDS-DMA loads are in flight
-// where they are used).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  else if constexpr (N == 1) asm volatile("s_waitcnt vmcnt(1)" ::: "memory");
-  else if constexpr (N == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-  else if constexpr (N == 3) asm volatile("s_waitcnt vmcnt(3)" ::: "memory");
-  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  else if constexpr (N == 6) asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else if constexpr (N == 12) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
-  else if constexpr (N == 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-  else if constexpr (N == 24) asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
-  else if constexpr (N == 32) asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
-  else if constexpr (N == 48) asm volatile("s_waitcnt vmcnt(48)" ::: "memory");
-  else static_assert(N < 0, "unsupported wait count");
-}
-
-__device__ __forceinline__ void barrier_no_fence() {
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 template <int D, int G, int MODE, bool BAL>
 __global__ void __launch_bounds__(2 * kWave * G) attn_stream(AttnArgs a) {

@@ -33,9 +33,11 @@
 // one tile (its row groups) are placed on one XCD so that, when the rows need
 // several groups, the later groups find the weight tile in that XCD's L2.
 //
-// lm_head_wide (more than 64 hidden rows): each wave streams two 32-row
-// tiles, so every hidden fragment read from LDS feeds two MFMAs; a
-// work-group covers 256 vocabulary rows and 64 hidden rows.
+// lm_head_dma (more than 64 hidden rows): both operands reach LDS by
+// LDS-DMA, the weight through a deep ring issued by two waves and the hidden
+// rows through a short ring issued by the other two, and every wave
+// multiplies its 32 weight rows by all of the work-group's 128, 256 or 512
+// hidden rows: each weight byte is read once per call (up to 512 rows).
 //
 // lm_head_finish: one work-group per group of rows reduces each row's tile
 // keys (32 threads per row, all loads issued before the reduction), writes the tokens
@@ -241,149 +243,177 @@ __global__ void __launch_bounds__(kLmThreads) lm_head_tiles(LmArgs a) {
   }
 }
 
-// Wide variant for more hidden rows: each wave streams TWO 32-row weight
-// tiles and multiplies both by every hidden fragment it reads from LDS, so a
-// 16-byte LDS read feeds two MFMAs (the LDS traffic per product halves) and
-// MT row tiles of 32 share each weight fragment.  A work-group covers
-// kLmWideN = 256 vocabulary rows (one key per row and 256-row tile: the
-// launch sets ntiles accordingly).  At MT = 2, KP = 64 the weight double
-// buffer, the hidden staging and the four accumulator tiles fit two waves
-// per SIMD (the launch bound asks for that occupancy).
-constexpr int kLmWideN = kLmWaves * 64;
-
-// 16-byte chunk c of hidden row r in the LDS phase buffer: an XOR swizzle
-// that keeps the 32 rows x 2 chunks of one MFMA operand read on distinct
-// bank groups for 16 consecutive rows
+// Many hidden rows (65 .. 512 per work-group): both operands reach LDS by
+// LDS-DMA in stages of 32 hidden elements, and every wave multiplies its
+// 32-row weight tile by all MT x 32 hidden rows (MT accumulator tiles, one
+// wave per SIMD), so each weight byte is read once per call and feeds up to
+// 512 rows.  The weight stream comes from HBM and needs many stages in
+// flight; the hidden rows come from L2 and need few.  Loads complete in
+// issue order per wave, so one wave that issued both would wait for the deep
+// weight prefetch whenever it needs the next hidden stage.  Hence the issue
+// is split by wave: waves 0 and 1 issue only the weight DMA (NWR stage
+// slots, NWR - 1 ahead), waves 2 and 3 only the hidden-row DMA (NHR slots,
+// NHR - 1 ahead); each waits on its own count, one barrier per stage
+// publishes both, and all four waves compute.
+//   weight stage j, slot b: 8 KiB, wave tile t, step s (16 elements) at
+//     (2 t + s) KiB, lane l's 16 bytes at + 16 l (the packed fragment order)
+//   hidden stage j, slot b: row r at 64 r, its 16-byte chunk c at
+//     ((c ^ ((r >> 2) & 3)) * 16): the 16 rows of a 16-lane read group land
+//     on 16 distinct bank groups
+// hidden row r's 16-byte chunk c in a stage of CH chunks per row: an XOR of
+// the chunk index that puts the 16 rows of a 16-lane read group on 16
+// distinct bank groups (CH = 4: 64-byte rows; CH = 8: 128-byte rows)
 template <int CH>
-__device__ __forceinline__ int lm_swz(int r, int c) {
-  if constexpr (CH >= 16) return r * CH + (c ^ (r & 15));
-  else return r * CH + (c ^ ((r >> 1) & (CH - 1)));
+__device__ __forceinline__ int lm_dma_hofs(int r, int c) {
+  if constexpr (CH == 4) return r * 64 + ((c ^ ((r >> 2) & 3)) << 4);
+  else return r * 128 + ((c ^ ((r >> 1) & 7)) << 4);
 }
 
-template <int MT, int KP, bool NT>
-__global__ void __launch_bounds__(kLmThreads, 2) lm_head_wide(LmArgs a) {
-  constexpr int CH = KP / 8;     // 16-byte chunks of one hidden row per phase
-  constexpr int NW = KP / 16;    // MFMA k-steps per phase
-  constexpr int ROWS = MT * 32;  // hidden rows per work-group
-  constexpr int NA = ROWS * CH / kLmThreads;
-  static_assert(CH == 8 || CH == 16, "phase shape");
-  static_assert((ROWS * CH) % kLmThreads == 0, "phase shape");
-  __shared__ u32x4 hs[2][ROWS * CH];
+// wait until the stages issued after the awaited one, at most K of them with
+// STEP loads each, are the only ones in flight (k = how many exist)
+template <int STEP, int K>
+__device__ __forceinline__ void lm_wait_stages(int k) {
+  if constexpr (K == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (k >= K) wait_vmcnt<K * STEP>();
+    else lm_wait_stages<STEP, K - 1>(k);
+  }
+}
+
+template <int MT, int KS, int NWR, int NHR, bool NT>
+__global__ void __launch_bounds__(kLmThreads, 1) lm_head_dma(LmArgs a) {
+  constexpr int ROWS = MT * 32;
+  constexpr int NS = KS / 16;                   // MFMA k-steps per stage
+  constexpr int CH = KS / 8;                    // 16-byte chunks of a hidden row per stage
+  constexpr int WSTAGE = kLmWaves * NS * 1024;  // weight bytes per stage
+  constexpr int HSTAGE = ROWS * KS * 2;         // hidden bytes per stage
+  constexpr int NWI = kLmWaves * NS / 2;        // weight DMA instructions per issuing wave and stage
+  static_assert(KS == 32 || KS == 64, "stage of 32 or 64 hidden elements");
+  constexpr int NHI = HSTAGE / 1024 / 2;       // hidden DMA instructions per issuing wave and stage
+  constexpr int DW = NWR - 1, DH = NHR - 1;    // stages in flight ahead of the one in use
+  static_assert(DW >= 1 && DH >= 1, "at least one stage ahead");
+  static_assert((DW - 1) * NWI <= 63 && (DH - 1) * NHI <= 63, "wait counts fit vmcnt");
+  __shared__ __attribute__((aligned(1024))) char wring[NWR][WSTAGE];
+  __shared__ __attribute__((aligned(1024))) char hring[NHR][HSTAGE];
   __shared__ float rv[kLmWaves][32];
   __shared__ int ri[kLmWaves][32];
   __shared__ float rs[kLmWaves][32];
 
+  // block -> (tile, row group): the row groups of one tile share an XCD
   const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
   const int tile = (local / a.mgroups) * 8 + xcd, mg = local % a.mgroups;
   if (tile >= a.ntiles) return;  // uniform: padding of the tile count to 8
 
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
   const int g = lane >> 5, c32 = lane & 31;
   const int m0 = mg * ROWS;
-  const int nbase = tile * kLmWideN + wave * 64;  // vocabulary row of this wave's first tile
+  const int nbase = tile * kLmTileN + wave * 32;
   const int steps = a.H / 16;
+  const int P = a.H / KS;
   const int last32 = (a.V - 1) / 32;
-  // 32-row tiles past the padded vocabulary read the last tile (in bounds);
-  // their rows are past V and are dropped below
-  const u32x4* wt0 = a.w + (size_t)min(nbase / 32, last32) * steps * kWave + lane;
-  const u32x4* wt1 = a.w + (size_t)min(nbase / 32 + 1, last32) * steps * kWave + lane;
-  const int P = a.H / KP;
 
-  auto load_w = [&](int p, u32x4(&wv)[2][NW]) {
-    const size_t o = (size_t)p * NW * kWave;
+  // weight issue (waves 0, 1): instruction q = NWI w + i covers tile q / NS,
+  // step q % NS of the stage; 32-row tiles past the padded vocabulary read
+  // the last tile (in bounds), their rows are dropped below
+  auto issue_w = [&](int j) {
+    if (j >= P) return;
+    char* dst = wring[j % NWR];
 #pragma unroll
-    for (int i = 0; i < NW; ++i) {
-      wv[0][i] = NT ? __builtin_nontemporal_load(wt0 + o + i * kWave) : wt0[o + i * kWave];
-      wv[1][i] = NT ? __builtin_nontemporal_load(wt1 + o + i * kWave) : wt1[o + i * kWave];
+    for (int i = 0; i < NWI; ++i) {
+      const int q = NWI * wave + i, t = q / NS, s = q % NS;
+      const int t32 = min(tile * (kLmTileN / 32) + t, last32);
+      const u32x4* src = a.w + ((size_t)t32 * steps + NS * j + s) * kWave + lane;
+      if (NT) dma16_nt(src, dst + q * 1024);
+      else dma16(src, dst + q * 1024);
     }
   };
-  auto load_h = [&](int p, u32x4(&hv)[NA]) {
+  // hidden issue (waves 2, 3): instruction q = (w - 2) + 2 k covers rows
+  // (64 / CH) q .. + 64 / CH - 1; lane l fills row (64 / CH) q + l / CH,
+  // slot l % CH with the chunk the swizzle puts there; rows past M repeat
+  // row M - 1 (dropped)
+  auto issue_h = [&](int j) {
+    if (j >= P) return;
+    char* dst = hring[j % NHR];
+    const int slot = lane % CH;
 #pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const int q = tid + kLmThreads * i, r = q / CH, c = q % CH;
-      const int m = min(m0 + r, a.M - 1);  // rows past M repeat the last row and are dropped
-      hv[i] = ld16(a.h + (size_t)m * a.H + (size_t)p * KP + 8 * c);
-    }
-  };
-  auto store_h = [&](int buf, const u32x4(&hv)[NA]) {
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const int q = tid + kLmThreads * i, r = q / CH, c = q % CH;
-      hs[buf][lm_swz<CH>(r, c)] = hv[i];
-    }
-  };
-  auto compute = [&](int buf, const u32x4(&wv)[2][NW], f32x16(&acc)[2][MT]) {
-#pragma unroll
-    for (int s = 0; s < NW; ++s) {
-      const bf16x8 a0 = __builtin_bit_cast(bf16x8, wv[0][s]);
-      const bf16x8 a1 = __builtin_bit_cast(bf16x8, wv[1][s]);
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const bf16x8 bv = __builtin_bit_cast(bf16x8, hs[buf][lm_swz<CH>(mt * 32 + c32, 2 * s + g)]);
-        acc[0][mt] = mfma_step(a0, bv, acc[0][mt]);
-        acc[1][mt] = mfma_step(a1, bv, acc[1][mt]);
-      }
+    for (int k = 0; k < NHI; ++k) {
+      const int q = (wave - 2) + 2 * k;
+      const int r = (kWave / CH) * q + lane / CH;
+      const int c = (lm_dma_hofs<CH>(r, slot) - r * CH * 16) >> 4;  // the swizzle is an involution
+      const int m = min(m0 + r, a.M - 1);
+      dma16(a.h + (size_t)m * a.H + (size_t)j * KS + 8 * c, dst + q * 1024);
     }
   };
 
-  f32x16 acc[2][MT];
+  f32x16 acc[MT];
 #pragma unroll
-  for (int v = 0; v < 2; ++v)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[v][mt][e] = 0.f;
+    for (int e = 0; e < 16; ++e) acc[mt][e] = 0.f;
 
-  u32x4 hv[NA], w0[2][NW], w1[2][NW];
-  load_h(0, hv);
-  load_w(0, w0);
-  store_h(0, hv);
-  __syncthreads();
-  for (int p = 0; p < P; p += 2) {
-    if (p + 1 < P) {
-      load_h(p + 1, hv);
-      load_w(p + 1, w1);
-    }
-    compute(0, w0, acc);
-    if (p + 1 < P) store_h(1, hv);
-    __syncthreads();
-    if (p + 1 >= P) break;
-    if (p + 2 < P) {
-      load_h(p + 2, hv);
-      load_w(p + 2, w0);
-    }
-    compute(1, w1, acc);
-    if (p + 2 < P) store_h(0, hv);
-    __syncthreads();
+  const bool wissue = wave < 2;
+  if (wissue) {
+    for (int u = 0; u < DW; ++u) issue_w(u);
+  } else {
+    for (int u = 0; u < DH; ++u) issue_h(u);
   }
+  for (int j = 0; j < P; ++j) {
+    // stage j has landed: the issuing waves wait on their own loads (only
+    // later stages may still fly), then one barrier publishes the stage and
+    // frees the slots of stage j - 1
+    if (wissue) lm_wait_stages<NWI, DW - 1>(min(DW - 1, P - 1 - j));
+    else lm_wait_stages<NHI, DH - 1>(min(DH - 1, P - 1 - j));
+    barrier_no_fence();
+    if (wissue) issue_w(j + DW);
+    else issue_h(j + DH);
+    // every operand of the stage is read from LDS before the first MFMA:
+    // with one wave per SIMD nothing else hides an LDS read's latency, and
+    // the reads return in issue order, so the MFMAs follow them down the queue
+    const char* ws = wring[j % NWR] + wave * NS * 1024 + lane * 16;
+    const char* hs = hring[j % NHR];
+    u32x4 af[NS], bf[NS][MT];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      af[s] = *reinterpret_cast<const u32x4*>(ws + s * 1024);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        bf[s][mt] = *reinterpret_cast<const u32x4*>(hs + lm_dma_hofs<CH>(mt * 32 + c32, 2 * s + g));
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        acc[mt] = mfma_step(__builtin_bit_cast(bf16x8, af[s]), __builtin_bit_cast(bf16x8, bf[s][mt]), acc[mt]);
+    __builtin_amdgcn_sched_group_barrier(0x100, NS * (1 + MT), 0);  // the LDS reads first
+    __builtin_amdgcn_sched_group_barrier(0x008, NS * MT, 0);        // then the MFMAs
+  }
+  wait_vmcnt<0>();  // nothing in flight past the loop (the last stages issue nothing)
 
-  // argmax of the 256-row tile per hidden row: lane (c32, g) holds, for the
-  // wave's tile v, vocabulary rows nbase + 32 v + 8 (e / 4) + 4 g + e % 4;
-  // rows grow with v then e, so a strict compare keeps the lowest index
+  // argmax of the tile per hidden row, as in lm_head_tiles: accumulator e of
+  // lane (c32, g) holds vocabulary row nbase + 8 (e / 4) + 4 g + e % 4 and
+  // hidden row m0 + 32 mt + c32
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     float bv = -INFINITY;
     int bi = 0x7fffffff;
 #pragma unroll
-    for (int v = 0; v < 2; ++v)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int nn = nbase + 32 * v + 8 * (e >> 2) + 4 * g + (e & 3);
-        if (nn < a.V && acc[v][mt][e] > bv) {
-          bv = acc[v][mt][e];
-          bi = nn;
-        }
+    for (int e = 0; e < 16; ++e) {
+      const int nn = nbase + 8 * (e >> 2) + 4 * g + (e & 3);
+      if (nn < a.V && acc[mt][e] > bv) {
+        bv = acc[mt][e];
+        bi = nn;
       }
+    }
     lm_keep(bv, bi, __shfl_xor(bv, 32, kWave), __shfl_xor(bi, 32, kWave));
     float se = 0.f;
     if (a.ms) {
 #pragma unroll
-      for (int v = 0; v < 2; ++v)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int nn = nbase + 32 * v + 8 * (e >> 2) + 4 * g + (e & 3);
-          se += nn < a.V ? __builtin_amdgcn_exp2f((acc[v][mt][e] - bv) * kLog2e) : 0.f;
-        }
+      for (int e = 0; e < 16; ++e) {
+        const int nn = nbase + 8 * (e >> 2) + 4 * g + (e & 3);
+        se += nn < a.V ? __builtin_amdgcn_exp2f((acc[mt][e] - bv) * kLog2e) : 0.f;
+      }
       se += __shfl_xor(se, 32, kWave);
     }
     if (g == 0) {
@@ -413,11 +443,11 @@ __global__ void __launch_bounds__(kLmThreads, 2) lm_head_wide(LmArgs a) {
   }
 }
 
-template <int MT, int KP, bool NT>
-static orthrus_status lm_launch_wide(LmArgs& a, hipStream_t s) {
-  a.ntiles = (a.V + kLmWideN - 1) / kLmWideN;
+template <int MT, int KS, int NWR, int NHR, bool NT>
+static orthrus_status lm_launch_dma(const LmArgs& a, hipStream_t s) {
   const long tiles8 = ((long)a.ntiles + 7) / 8 * 8;
-  hipLaunchKernelGGL((lm_head_wide<MT, KP, NT>), dim3((unsigned)(tiles8 * a.mgroups)), dim3(kLmThreads), 0, s, a);
+  hipLaunchKernelGGL((lm_head_dma<MT, KS, NWR, NHR, NT>), dim3((unsigned)(tiles8 * a.mgroups)), dim3(kLmThreads), 0, s,
+                     a);
   return hipGetLastError() == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_LAUNCH;
 }
 
@@ -577,20 +607,31 @@ static orthrus_status lm_run(LmArgs a, hipStream_t s, int finish_groups) {
   // 32 rows: one group, deep phases.  64 rows: one 64-row group with shallow
   // phases (two waves per SIMD fit).  One row group reads every weight byte
   // once: nontemporal loads (measured about 15 % faster at 32 and 64 rows).
-  // More rows: 64-row groups of the wide kernel (two weight tiles per wave,
-  // 64-element phases; measured 5 % faster at 128 rows and 10 % at 512 than
-  // 64-row groups of the narrow one).  The groups of one weight tile run on
-  // one XCD, so after the first group the tile mostly comes from L2: ordinary
-  // loads.
+  // More rows: one group of 128, 256 or 512 rows in the DMA kernel (64- or
+  // 32-element stages by what fits LDS).  Measured at the Qwen3-8B head
+  // against 64-row groups of a kernel with two weight tiles per wave: 128
+  // rows 305 -> 286 us, 512 rows 794 -> 772 us; two 256-row groups at 512
+  // rows measured 807 us.  Above 512 rows the 512-row groups of one weight
+  // tile run on one XCD, so after the first group the tile mostly comes from
+  // L2: ordinary loads.
   if (a.M <= 32) {
     a.mgroups = 1;
     st = lm_launch_tiles<1, 256, true>(a, s);
   } else if (a.M <= 64) {
     a.mgroups = 1;
     st = lm_launch_tiles<2, 128, true>(a, s);
+  } else if (a.M <= 128) {
+    a.mgroups = 1;
+    st = lm_launch_dma<4, 64, 6, 3, true>(a, s);
+  } else if (a.M <= 256) {
+    a.mgroups = 1;
+    st = lm_launch_dma<8, 64, 5, 2, true>(a, s);
+  } else if (a.M <= 512) {
+    a.mgroups = 1;
+    st = lm_launch_dma<16, 32, 7, 3, true>(a, s);
   } else {
-    a.mgroups = (a.M + 63) / 64;
-    st = lm_launch_wide<2, 64, false>(a, s);
+    a.mgroups = (a.M + 511) / 512;
+    st = lm_launch_dma<16, 32, 7, 3, false>(a, s);
   }
   if (st != ORTHRUS_OK) return st;
   hipLaunchKernelGGL(lm_head_finish, dim3((unsigned)finish_groups), dim3(kLmFinThreads), 0, s, a);

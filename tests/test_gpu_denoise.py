@@ -108,9 +108,9 @@ def test_denoise_qwen3_8b_head():
 
 
 def test_denoise_qwen3_8b_head_b16_sampled():
-    """The benchmark's B16 rows (512, the wide kernel's 64-row groups) at the
-    Qwen3-8B head; the oracle checks sequences at both ends and on both sides
-    of the 256-row point."""
+    """The benchmark's B16 rows (512, one work-group's rows in the many-row
+    kernel) at the Qwen3-8B head; the oracle checks sequences at both ends
+    and on both sides of the 256-row point."""
     say("denoise qwen3-8b B16 sampled")
     B, K = 16, 32
     h, w, _ = I.make_lm_head_inputs(B * K, I.QWEN3_8B_HIDDEN, I.QWEN3_VOCAB, seed=16)

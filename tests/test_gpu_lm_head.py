@@ -80,11 +80,13 @@ def check_random(rows, H, V, seed, sample=None):
 
 
 @pytest.mark.parametrize("rows,H,V", [(1, 256, 1000), (7, 512, 5003), (32, 1024, 20000), (33, 256, 777),
-                                      (64, 2048, 10007), (100, 512, 3001), (130, 256, 4099), (257, 512, 2000)])
+                                      (64, 2048, 10007), (100, 512, 3001), (130, 256, 4099), (257, 512, 2000),
+                                      (600, 256, 1500)])
 def test_lm_head_random_vs_oracle(rows, H, V):
-    """Row counts 1..257 cover one 32-row group and one to five 64-row
-    groups with ragged tails; vocabularies from 777 to 20000 cover ragged
-    128-row tiles."""
+    """Row counts 1..600 cover every kernel and row grouping: one 32-row
+    group, one 64-row group, one group of 128, 256 and 512 rows of the
+    many-row kernel (ragged tails), and two 512-row groups; vocabularies
+    from 777 to 20000 cover ragged 128-row tiles."""
     say("lm_head random", rows, H, V)
     check_random(rows, H, V, seed=rows + V)
 
@@ -96,15 +98,17 @@ def test_lm_head_qwen3_8b_random():
 
 @pytest.mark.parametrize("rows", [128, 512])
 def test_lm_head_qwen3_8b_random_wide_rows_sampled(rows):
-    """The benchmark's B4 and B16 row counts at the Qwen3-8B head (the wide
-    kernel, 64-row groups): the oracle checks rows on both sides of every
-    group boundary and the last row."""
+    """The benchmark's B4 and B16 row counts at the Qwen3-8B head (the
+    many-row kernel: all rows in one work-group, 32-row accumulator tiles):
+    the oracle checks rows on both sides of accumulator-tile boundaries and
+    the last row."""
     say("lm_head qwen3-8b random wide", rows)
-    sample = sorted({0} | {m for k in range(64, rows, 64) for m in (k - 1, k)} | {rows - 1})
+    step = 32 if rows <= 128 else 64
+    sample = sorted({0} | {m for k in range(step, rows, step) for m in (k - 1, k)} | {rows - 1})
     check_random(rows, I.QWEN3_8B_HIDDEN, I.QWEN3_VOCAB, seed=rows, sample=sample)
 
 
-@pytest.mark.parametrize("rows", [1, 32, 64, 96, 512])
+@pytest.mark.parametrize("rows", [1, 32, 64, 96, 512, 1100])
 def test_lm_head_planted_qwen3_8b(rows):
     """Planted targets at the Qwen3-8B head, bit-exact; the maximum is H."""
     say("lm_head planted", rows)
@@ -137,16 +141,16 @@ def test_lm_head_planted_ties_resolve_to_lowest_index():
 
 
 def test_lm_head_planted_ties_many_rows():
-    """The same ties with more than 64 hidden rows (the wide kernel: two
-    32-row weight tiles per wave, 256-row key tiles): copies in the other tile
-    of the same wave, in the other lane half, in another wave of the same
-    256-row tile, and in another tile, before or after the winner.  Every row
-    must give the lower index of the pair, exactly."""
+    """The same ties with more than 64 hidden rows (the many-row kernel:
+    128-row key tiles, every wave's 32-row weight slice multiplied by all
+    rows): copies in the same 32-row slice, in the other lane half, in another
+    wave of the same 128-row tile, and in another tile, before or after the
+    winner.  Every row must give the lower index of the pair, exactly."""
     say("lm_head ties, many rows")
     d = dev()
     H, V, rows = 1024, 10000, 96
     _, w, _ = I.make_lm_head_inputs(1, H, V, seed=6, planted=True, device=d)
-    # 5030 is row 38 of its wave's 64-row slice (second tile); 5000 is row 8 (first tile)
+    # 5000 and 5030 sit in different waves' 32-row slices of one 128-row tile
     cases = [(5030, 5000), (5000, 5030), (5000, 4997), (5000, 4990), (5000, 5100), (5000, 4863), (9999, 9998),
              (300, 44)]
     for winner, copy in cases:
