@@ -65,8 +65,10 @@ struct AttnArgs {
   int kv_once;      // the call reads each context K/V byte once: nontemporal stream
   // balanced split (streaming path): the split length is chosen per call from
   // ctx_lens so that one round of Q work-groups per KV head covers the batch;
-  // the partial of unit (b, s) sits in slot P_b + s of its KV head's U slots
-  int bal, Q, U;
+  // the partial of unit (b, s) sits in slot P_b + s of its KV head's U slots;
+  // Q2 > Q allows a second round of units (Q2 per KV head) when one round
+  // leaves the batch poorly balanced
+  int bal, Q, U, Q2;
   int2* ws_rec;     // balanced split: (splits, first slot) per sequence, for attn_combine
   int s_hint;       // split count that sizes the combine's lane groups (a
                     // batch with every length at max_ctx has this many)
@@ -74,6 +76,8 @@ struct AttnArgs {
 
 constexpr int kBalMinTiles = 320 / kTile;        // shortest automatic or balanced split: 320 positions
 constexpr int kBalMaxTiles = kMaxSplit / kTile;  // longest: kMaxSplit
+constexpr float kBalRoundEff = 0.85f;            // balanced split: below this average / longest unit
+                                                 // in one round, use two
 
 // Inclusive prefix sum over the 64 lanes of a wave on the DPP paths (no LDS
 // round trip): shifts by 1, 2, 4, 8 within each 16-lane row, then the row
@@ -134,6 +138,23 @@ __device__ BalSplit balanced_split(const AttnArgs& a, int lane, int t_guess) {
       const int mid = (lo + hi) >> 1;
       if (count(mid) <= a.Q) hi = mid;
       else lo = mid + 1;
+    }
+  }
+  // One round (at most Q units per KV head) is poorly balanced when its
+  // average unit is below kBalRoundEff of the longest, t: then up to Q2
+  // shorter units (two rounds), numbered longest first within each sequence
+  // and dispatched as work-groups free up, shorten the critical path (an
+  // equal-length batch stays at one round: its average is t)
+  if (a.Q2 > a.Q && lo > kBalMinTiles) {
+    const int tiles = wave_total(act ? (T > 0 ? T : 1) : 0);
+    if ((float)tiles < kBalRoundEff * (float)a.Q * (float)lo) {
+      int lo2 = kBalMinTiles, hi2 = lo;
+      while (lo2 < hi2) {
+        const int mid = (lo2 + hi2) >> 1;
+        if (count(mid) <= a.Q2) hi2 = mid;
+        else lo2 = mid + 1;
+      }
+      lo = lo2;
     }
   }
   BalSplit r;
@@ -1658,20 +1679,22 @@ static bool attn_stream_path(const orthrus_attn_desc& d) {
 // balanced split requested, several sequences (at most 64, fewer than 256
 // (b, KV head) pairs) and the streaming kernel, the split length is chosen on the device
 // from ctx_lens (balanced_split): the smallest multiple of 64 positions in
-// [256, kMaxSplit] that makes at most Q = ceil(256 / Hkv) units per KV head,
+// [320, kMaxSplit] that makes at most Q = ceil(256 / Hkv) units per KV head,
 // so one round of about 256 work-groups covers a ragged batch as evenly as
-// the 64-position tiles allow.  The host knows only max_ctx_len: its split
+// the 64-position tiles allow; where that round's average unit is below
+// kBalRoundEff of its longest, the smallest split with at most Q2 = 2 Q units
+// (two rounds) instead.  The host knows only max_ctx_len: its split
 // is the one a batch of that length everywhere gets, the partial slots are
 // sized for the worst case, and the grid has U slots per KV head (units past
 // the batch's last one exit at once).  Otherwise the split is fixed by the
 // host (attn_split_tokens).
 struct SplitPlan {
   bool bal;
-  int split, s_max, s_hint, Q, U;
+  int split, s_max, s_hint, Q, U, Q2;
 };
 
 static SplitPlan attn_plan(const orthrus_attn_desc& d) {
-  SplitPlan p{false, attn_split_tokens(d), 0, 0, 0, 0};
+  SplitPlan p{false, attn_split_tokens(d), 0, 0, 0, 0, 0};
   p.s_max = attn_s_max(d, p.split);
   p.s_hint = p.s_max;
   if (d.split_tokens != ORTHRUS_SPLIT_BALANCED || !attn_stream_path(d) || d.batch < 2 || d.batch > 64 ||
@@ -1683,8 +1706,9 @@ static SplitPlan attn_plan(const orthrus_attn_desc& d) {
   // equal max_ctx_len: the device's search starts from it
   p.bal = true;
   p.Q = attn_round_slots(d);
+  p.Q2 = 2 * p.Q;
   const long most_units = (long)d.batch * ceil_div(Tm, kBalMaxTiles);
-  p.U = (int)(most_units > p.Q ? most_units : p.Q);
+  p.U = (int)(most_units > p.Q2 ? most_units : p.Q2);
   const int most = ceil_div(Tm, kBalMinTiles);
   p.s_max = most < p.U - d.batch + 1 ? most : p.U - d.batch + 1;
   p.s_hint = ceil_div(Tm, p.split / kTile);
@@ -1824,6 +1848,7 @@ orthrus_status orthrus::block_attn_run(const void* q, const void* k_cache, const
   a.s_max = plan.s_max;
   a.bal = plan.bal ? 1 : 0;
   a.Q = plan.Q;
+  a.Q2 = plan.Q2;
   a.U = plan.U;
   a.s_hint = plan.s_hint;
   a.ws_o = nullptr;

@@ -73,10 +73,14 @@ typedef enum { ORTHRUS_BF16 = 0, ORTHRUS_F32 = 1 } orthrus_dtype;
  * With bf16 storage, Hq / Hkv <= 4, 2 <= batch <= 64, batch * Hkv < 256 and
  * max_ctx_len < 2^24, the kernels read every ctx_lens[b] and take the
  * smallest split (a multiple of 64 in [320, 8192]) that gives at most
- * ceil(256 / Hkv) work-groups per KV head, so that one round of about 256
- * work-groups covers the batch as evenly as 64-position tiles allow; the
- * launch and the workspace are sized for the worst case that max_ctx_len
- * allows.  Outside those bounds it means 0 (automatic). */
+ * Q = ceil(256 / Hkv) work-groups per KV head, so that one round of about 256
+ * work-groups covers the batch as evenly as 64-position tiles allow.  When
+ * that round would be poorly balanced (the average work-group below 85 % of
+ * the longest), they take the smallest split with at most 2 Q work-groups
+ * per KV head instead (two rounds of shorter work-groups); a batch of equal
+ * lengths always stays at one round.  The launch and the workspace are sized
+ * for the worst case that max_ctx_len allows.  Outside those bounds it means
+ * 0 (automatic). */
 #define ORTHRUS_SPLIT_BALANCED (-1)
 
 typedef enum {

@@ -119,18 +119,20 @@ def test_split_and_workspace_arithmetic():
 
 
 @pytest.mark.parametrize("batch,hq,hkv,max_ctx,split,units", [
-    (2, 32, 8, 8192, 512, 32),      # 2 x 16 splits fill one 32-slot round per KV head
-    (4, 32, 8, 8192, 1024, 32),
-    (16, 32, 8, 8192, 4096, 32),
-    (3, 32, 8, 8192, 832, 32),      # 3 x 10 splits fit one 32-slot round (a 768 split would need 33)
-    (16, 32, 8, 16379, 8192, 32),   # the ragged batch's bound: its lengths pick the split on the device
-    (16, 32, 8, 200000, 8192, 400),  # 25 splits of 8192 each: more than one round
-    (64, 8, 2, 8192, 4096, 128)])
+    (2, 32, 8, 8192, 512, 64),      # 2 x 16 splits fill one 32-slot round per KV head; slots for two rounds
+    (4, 32, 8, 8192, 1024, 64),
+    (16, 32, 8, 8192, 4096, 64),
+    (3, 32, 8, 8192, 832, 64),      # 3 x 10 splits fit one 32-slot round (a 768 split would need 33)
+    (16, 32, 8, 16379, 8192, 64),   # the ragged batch's bound: its lengths pick the split on the device
+    (16, 32, 8, 200000, 8192, 400),  # 25 splits of 8192 each: more than two rounds
+    (64, 8, 2, 8192, 4096, 256)])
 def test_balanced_split_plan(batch, hq, hkv, max_ctx, split, units):
     """Balanced split requested, several sequences, bf16 with Hq/Hkv <= 4:
     the split that a batch with every length at max_ctx gets (the smallest
     multiple of 64 in [320, 8192] giving at most ceil(256 / Hkv) work-groups
-    per KV head), and partial slots for `units` work-groups per KV head."""
+    per KV head), and partial slots for `units` work-groups per KV head: two
+    rounds of ceil(256 / Hkv) (a poorly balanced batch may take the second),
+    or every split of every sequence at the longest split if that is more."""
     lib = B.lib()
     pages = -(-(max_ctx + 32) // 16)
     d = good_desc(batch=batch, n_q_heads=hq, n_kv_heads=hkv, max_ctx_len=max_ctx, max_pages_per_seq=pages,

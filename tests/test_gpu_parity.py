@@ -337,8 +337,8 @@ def test_balanced_split_group_sizes_and_head_dims(G, D):
 def test_balanced_split_ragged16_bench_workload(mode):
     """The ragged workload exactly as the benchmark times it: 16 sequences
     with L_b ~ U[1024, 16384] (the benchmark's lengths), the balanced split
-    chosen on the device (splits of several thousand positions, up to three
-    per sequence).  The shortest, the longest and four more sequences are
+    chosen on the device: one round would be 75 % balanced, so the kernels
+    take two rounds of 37-tile units (up to seven per sequence).  The shortest, the longest and four more sequences are
     checked against the oracle on heads of three KV groups, and a repeat of
     the call gives identical bits."""
     say("balanced split, ragged16 bench workload", mode)
