@@ -212,7 +212,7 @@ def block_attn(q, k_cache, v_cache, k_blk, v_blk, page_table, ctx_lens, mode, ou
     return out
 
 
-STATIC_SCRATCH_BYTES = 16 << 20   # ORTHRUS_STATIC_SCRATCH_BYTES
+STATIC_SCRATCH_BYTES = 32 << 20   # ORTHRUS_STATIC_SCRATCH_BYTES
 
 
 def block_attn_noalloc(q, k_cache, v_cache, k_blk, v_blk, page_table, ctx_lens, mode, out, *, max_ctx_len=None,

@@ -167,11 +167,12 @@ orthrus_status orthrus_block_attn(const void* q, const void* k_cache, const void
                                   const orthrus_attn_desc* desc, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
-/* Largest workspace orthrus_block_attn_noalloc can serve (16 MiB: every
- * decode shape up to 32 query heads x 32 rows x 32 splits per sequence and
- * KV-head group, e.g. Qwen3-8B heads at batch 16 x 8192 or batch 4 x 32768
- * cached tokens). */
-#define ORTHRUS_STATIC_SCRATCH_BYTES ((size_t)16 << 20)
+/* Largest workspace orthrus_block_attn_noalloc can serve (32 MiB: every
+ * decode shape up to 32 query heads x 32 rows x 64 partial slots per
+ * sequence and KV-head group, e.g. Qwen3-8B heads at batch 16 x 8192 or
+ * batch 4 x 32768 cached tokens, or the balanced split of 16 ragged
+ * sequences of up to 16384 tokens, whose two rounds take 64 slots). */
+#define ORTHRUS_STATIC_SCRATCH_BYTES ((size_t)32 << 20)
 
 /* orthrus_block_attn for callers that cannot allocate device memory: code
  * under HIP graph capture, tight serving loops, harnesses that forbid

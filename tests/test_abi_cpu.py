@@ -334,7 +334,7 @@ def test_noalloc_validation():
     assert call(good_desc(head_dim=96)) == 3
     assert call(d, q=ctypes.c_void_p(4096 + 8)) == 2
     big = good_desc(batch=4, split_tokens=64)             # 4 x 128 splits: about 138 MB of partials
-    assert lib.orthrus_block_attn_workspace_bytes(ctypes.byref(big)) > 16 << 20
+    assert lib.orthrus_block_attn_workspace_bytes(ctypes.byref(big)) > 32 << 20
     assert call(big) == 4
 
 

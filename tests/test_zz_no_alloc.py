@@ -22,10 +22,12 @@ def dev():
 def test_noalloc_matches_workspace_entry_point():
     d = dev()
     from diffusion_drafted_verification_amd import orthrus as ob
-    cases = [("qwen3_8b_8k B1 ctx 8192 (26 splits)", dict(ctx_lens=[8192]), 0, 8192),
-             ("qwen3_8b_8k B3 ragged, split 256", dict(batch=3, ctx_lens=[3001, 17, 1200]), 256, 3001)]
-    for name, kw, split, mx in cases:
-        x = I.make_attn_inputs("qwen3_8b_8k", device=d, **kw)
+    cases = [("qwen3_8b_8k B1 ctx 8192 (26 splits)", "qwen3_8b_8k", dict(ctx_lens=[8192]), 0, 8192),
+             ("qwen3_8b_8k B3 ragged, split 256", "qwen3_8b_8k", dict(batch=3, ctx_lens=[3001, 17, 1200]), 256, 3001),
+             ("qwen3_8b_ragged16, balanced split (two rounds)", "qwen3_8b_ragged16", {}, ob.SPLIT_BALANCED, None)]
+    for name, workload, kw, split, mx in cases:
+        x = I.make_attn_inputs(workload, device=d, **kw)
+        mx = x.max_ctx_len if mx is None else mx
         desc = ob.make_desc(x.q, x.k_cache, x.page_table, mx, None, split)
         need = ob.block_attn_workspace_bytes(desc)
         assert 0 < need <= ob.STATIC_SCRATCH_BYTES, need
