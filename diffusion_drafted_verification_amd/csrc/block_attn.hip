@@ -1098,14 +1098,16 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_stream(AttnArgs a) {
   // One stage = QK (scores of this wave's 32 positions), softmax, PV.  The
   // scores of stage t+1 are computed during iteration t (software
   // pipelining), so their MFMAs can overlap this stage's softmax VALU work.
+  // A tile's MFMA operands are all read from LDS before its first MFMA (one
+  // read issued before each MFMA made every MFMA wait for its own read).
   auto qk = [&](const char* stage, f32x16& sc) {
+    V8 kf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kf[ks] = __builtin_bit_cast(V8, ld16(stage + (kofs ^ (ks << 5))));
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc[r] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const V8 av = __builtin_bit_cast(V8, ld16(stage + (kofs ^ (ks << 5))));
-      sc = mfma_step(av, qf[ks], sc);
-    }
+    for (int ks = 0; ks < KS; ++ks) sc = mfma_step(kf[ks], qf[ks], sc);
   };
   // softmax, first half: mask the tail, row max, lazy rescale of the
   // running state; returns the reference max for the exponentials
@@ -1151,6 +1153,7 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_stream(AttnArgs a) {
   };
   auto pv = [&](const char* stage, const V8& p0, const V8& p1) {
     const char* vt = stage + Lay::TILEB + 32 * sub * Lay::ROWB;
+    V8 vf[2][MB];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const char* vb = vt + 16 * j * Lay::ROWB;
@@ -1159,15 +1162,17 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_stream(AttnArgs a) {
         const int off = vofs ^ (m << 6);
         const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((ORTHRUS_LDS bf16x4*)(vb + off));
         const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((ORTHRUS_LDS bf16x4*)(vb + 4 * Lay::ROWB + off));
-        V8 av;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          av[e] = lo[e];
-          av[4 + e] = hi4[e];
+          vf[j][m][e] = lo[e];
+          vf[j][m][4 + e] = hi4[e];
         }
-        o[m] = mfma_step(av, j == 0 ? p0 : p1, o[m]);
       }
     }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int m = 0; m < MB; ++m) o[m] = mfma_step(vf[j][m], j == 0 ? p0 : p1, o[m]);
   };
 
   char* const ring[kRing] = {st0, st1, st2, st3};
@@ -1473,14 +1478,18 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_prefill_pair(AttnArgs a, i
   // second tile, or the next stage's first) are computed before this tile's
   // softmax, so their MFMAs can issue beside its exponentials, and only two
   // score tiles are live (the register budget of two waves per SIMD).
+  // The operands of a tile's MFMAs are all read from LDS before the first of
+  // them: issued one before each MFMA, every MFMA waited for its own read
+  // (measured 5 % slower on the 8192-token prompt).
   auto qk = [&](const char* stage, int q, f32x16& sc) {
+    V8 kf[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kf[ks] = __builtin_bit_cast(V8, ld16(stage + q * kRows * Lay::ROWB + (kofs ^ (ks << 5))));
 #pragma unroll
     for (int r = 0; r < 16; ++r) sc[r] = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const V8 av = __builtin_bit_cast(V8, ld16(stage + q * kRows * Lay::ROWB + (kofs ^ (ks << 5))));
-      sc = mfma_step(av, qf[ks], sc);
-    }
+    for (int ks = 0; ks < KS; ++ks) sc = mfma_step(kf[ks], qf[ks], sc);
   };
   // mask (this wave's causal rows and range), row max, lazy rescale
   const int vis_end = Lw < pew ? Lw : pew;  // below it every position is visible
@@ -1522,6 +1531,7 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_prefill_pair(AttnArgs a, i
   };
   auto pv = [&](const char* stage, int q, const V8& p0, const V8& p1) {
     const char* vt = stage + Lay::TILEB + q * kRows * Lay::ROWB;
+    V8 vf[2][MB];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const char* vb = vt + 16 * j * Lay::ROWB;
@@ -1530,15 +1540,17 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_prefill_pair(AttnArgs a, i
         const int off = vofs ^ (m << 6);
         const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((ORTHRUS_LDS bf16x4*)(vb + off));
         const bf16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((ORTHRUS_LDS bf16x4*)(vb + 4 * Lay::ROWB + off));
-        V8 av;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          av[e] = lo[e];
-          av[4 + e] = hi4[e];
+          vf[j][m][e] = lo[e];
+          vf[j][m][4 + e] = hi4[e];
         }
-        o[m] = mfma_step(av, j == 0 ? p0 : p1, o[m]);
       }
     }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int m = 0; m < MB; ++m) o[m] = mfma_step(vf[j][m], j == 0 ? p0 : p1, o[m]);
   };
 
   // scores[q] holds the scores of tile q of the current stage
