@@ -34,9 +34,9 @@
 // several groups, the later groups find the weight tile in that XCD's L2.
 //
 // lm_head_dma (more than 64 hidden rows): both operands reach LDS by
-// LDS-DMA, the weight through a deep ring issued by two waves and the hidden
-// rows through a short ring issued by the other two, and every wave
-// multiplies its 32 weight rows by all of the work-group's 128, 256 or 512
+// LDS-DMA, the weight through a deep ring issued by half of the eight waves
+// and the hidden rows through a short ring issued by the other half, and the
+// work-group multiplies its 128 weight rows by all of its 128, 256 or 512
 // hidden rows: each weight byte is read once per call (up to 512 rows).
 //
 // lm_head_finish: one work-group per group of rows reduces each row's tile
@@ -244,22 +244,24 @@ __global__ void __launch_bounds__(kLmThreads) lm_head_tiles(LmArgs a) {
 }
 
 // Many hidden rows (65 .. 512 per work-group): both operands reach LDS by
-// LDS-DMA in stages of 32 hidden elements, and every wave multiplies its
-// 32-row weight tile by all MT x 32 hidden rows (MT accumulator tiles, one
-// wave per SIMD), so each weight byte is read once per call and feeds up to
-// 512 rows.  The weight stream comes from HBM and needs many stages in
+// LDS-DMA in stages of 32 or 64 hidden elements, and the work-group
+// multiplies its 128-row weight tile by all MT x 32 hidden rows: wave w
+// takes the 32 weight rows of slice w % 4 and MT / RH of the accumulator
+// tiles (row part w / 4; RH = 2: eight waves, two per SIMD, which hides LDS
+// latency and the per-stage barrier better than one wave per SIMD), so each
+// weight byte is read once per call and feeds up to 512 rows.  The weight stream comes from HBM and needs many stages in
 // flight; the hidden rows come from L2 and need few.  Loads complete in
 // issue order per wave, so one wave that issued both would wait for the deep
 // weight prefetch whenever it needs the next hidden stage.  Hence the issue
-// is split by wave: waves 0 and 1 issue only the weight DMA (NWR stage
-// slots, NWR - 1 ahead), waves 2 and 3 only the hidden-row DMA (NHR slots,
-// NHR - 1 ahead); each waits on its own count, one barrier per stage
-// publishes both, and all four waves compute.
-//   weight stage j, slot b: 8 KiB, wave tile t, step s (16 elements) at
-//     (2 t + s) KiB, lane l's 16 bytes at + 16 l (the packed fragment order)
-//   hidden stage j, slot b: row r at 64 r, its 16-byte chunk c at
-//     ((c ^ ((r >> 2) & 3)) * 16): the 16 rows of a 16-lane read group land
-//     on 16 distinct bank groups
+// is split by wave: the first half of the waves issue only the weight DMA
+// (NWR stage slots, NWR - 1 ahead), the second half only the hidden-row DMA
+// (NHR slots, NHR - 1 ahead); each waits on its own count, one barrier per
+// stage publishes both, and all waves compute.
+//   weight stage j: weight slice t, step s (16 elements) at (NS t + s) KiB,
+//     lane l's 16 bytes at + 16 l (the packed fragment order)
+//   hidden stage j: row r at r * 2 KS bytes, its 16-byte chunks XOR-swizzled
+//     (lm_dma_hofs) so that the 16 rows of a 16-lane read group land on 16
+//     distinct bank groups
 // hidden row r's 16-byte chunk c in a stage of CH chunks per row: an XOR of
 // the chunk index that puts the 16 rows of a 16-lane read group on 16
 // distinct bank groups (CH = 4: 64-byte rows; CH = 8: 128-byte rows)
@@ -281,24 +283,28 @@ __device__ __forceinline__ void lm_wait_stages(int k) {
   }
 }
 
-template <int MT, int KS, int NWR, int NHR, bool NT>
-__global__ void __launch_bounds__(kLmThreads, 1) lm_head_dma(LmArgs a) {
+template <int MT, int KS, int NWR, int NHR, int RH, bool NT>
+__global__ void __launch_bounds__(kLmThreads * RH, 1) lm_head_dma(LmArgs a) {
+  constexpr int NWV = kLmWaves * RH;            // waves: 4 vocabulary slices x RH row parts
+  constexpr int MTW = MT / RH;                  // accumulator tiles per wave
   constexpr int ROWS = MT * 32;
   constexpr int NS = KS / 16;                   // MFMA k-steps per stage
   constexpr int CH = KS / 8;                    // 16-byte chunks of a hidden row per stage
   constexpr int WSTAGE = kLmWaves * NS * 1024;  // weight bytes per stage
   constexpr int HSTAGE = ROWS * KS * 2;         // hidden bytes per stage
-  constexpr int NWI = kLmWaves * NS / 2;        // weight DMA instructions per issuing wave and stage
+  constexpr int NIW = NWV / 2;                  // waves issuing each operand
+  constexpr int NWI = kLmWaves * NS / NIW;      // weight DMA instructions per issuing wave and stage
+  constexpr int NHI = HSTAGE / 1024 / NIW;      // hidden DMA instructions per issuing wave and stage
   static_assert(KS == 32 || KS == 64, "stage of 32 or 64 hidden elements");
-  constexpr int NHI = HSTAGE / 1024 / 2;       // hidden DMA instructions per issuing wave and stage
+  static_assert(MT % RH == 0 && NWI * NIW == kLmWaves * NS && NHI * NIW * 1024 == HSTAGE, "issue shape");
   constexpr int DW = NWR - 1, DH = NHR - 1;    // stages in flight ahead of the one in use
   static_assert(DW >= 1 && DH >= 1, "at least one stage ahead");
   static_assert((DW - 1) * NWI <= 63 && (DH - 1) * NHI <= 63, "wait counts fit vmcnt");
   __shared__ __attribute__((aligned(1024))) char wring[NWR][WSTAGE];
   __shared__ __attribute__((aligned(1024))) char hring[NHR][HSTAGE];
-  __shared__ float rv[kLmWaves][32];
-  __shared__ int ri[kLmWaves][32];
-  __shared__ float rs[kLmWaves][32];
+  __shared__ float rv[RH][kLmWaves][32];
+  __shared__ int ri[RH][kLmWaves][32];
+  __shared__ float rs[RH][kLmWaves][32];
 
   // block -> (tile, row group): the row groups of one tile share an XCD
   const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
@@ -307,16 +313,17 @@ __global__ void __launch_bounds__(kLmThreads, 1) lm_head_dma(LmArgs a) {
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
+  const int vs = wave % kLmWaves, rh = wave / kLmWaves;  // vocabulary slice, row part
   const int g = lane >> 5, c32 = lane & 31;
   const int m0 = mg * ROWS;
-  const int nbase = tile * kLmTileN + wave * 32;
+  const int nbase = tile * kLmTileN + vs * 32;
   const int steps = a.H / 16;
   const int P = a.H / KS;
   const int last32 = (a.V - 1) / 32;
 
-  // weight issue (waves 0, 1): instruction q = NWI w + i covers tile q / NS,
-  // step q % NS of the stage; 32-row tiles past the padded vocabulary read
-  // the last tile (in bounds), their rows are dropped below
+  // weight issue (waves 0 .. NIW - 1): instruction q = NWI w + i covers
+  // tile q / NS, step q % NS of the stage; 32-row tiles past the padded
+  // vocabulary read the last tile (in bounds), their rows are dropped below
   auto issue_w = [&](int j) {
     if (j >= P) return;
     char* dst = wring[j % NWR];
@@ -329,17 +336,17 @@ __global__ void __launch_bounds__(kLmThreads, 1) lm_head_dma(LmArgs a) {
       else dma16(src, dst + q * 1024);
     }
   };
-  // hidden issue (waves 2, 3): instruction q = (w - 2) + 2 k covers rows
-  // (64 / CH) q .. + 64 / CH - 1; lane l fills row (64 / CH) q + l / CH,
-  // slot l % CH with the chunk the swizzle puts there; rows past M repeat
-  // row M - 1 (dropped)
+  // hidden issue (waves NIW .. NWV - 1): instruction q = (w - NIW) + NIW k
+  // covers rows (64 / CH) q .. + 64 / CH - 1; lane l fills row
+  // (64 / CH) q + l / CH, slot l % CH with the chunk the swizzle puts there;
+  // rows past M repeat row M - 1 (dropped)
   auto issue_h = [&](int j) {
     if (j >= P) return;
     char* dst = hring[j % NHR];
     const int slot = lane % CH;
 #pragma unroll
     for (int k = 0; k < NHI; ++k) {
-      const int q = (wave - 2) + 2 * k;
+      const int q = (wave - NIW) + NIW * k;
       const int r = (kWave / CH) * q + lane / CH;
       const int c = (lm_dma_hofs<CH>(r, slot) - r * CH * 16) >> 4;  // the swizzle is an involution
       const int m = min(m0 + r, a.M - 1);
@@ -347,13 +354,13 @@ __global__ void __launch_bounds__(kLmThreads, 1) lm_head_dma(LmArgs a) {
     }
   };
 
-  f32x16 acc[MT];
+  f32x16 acc[MTW];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int k = 0; k < MTW; ++k)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[mt][e] = 0.f;
+    for (int e = 0; e < 16; ++e) acc[k][e] = 0.f;
 
-  const bool wissue = wave < 2;
+  const bool wissue = wave < NIW;
   if (wissue) {
     for (int u = 0; u < DW; ++u) issue_w(u);
   } else {
@@ -369,40 +376,40 @@ __global__ void __launch_bounds__(kLmThreads, 1) lm_head_dma(LmArgs a) {
     if (wissue) issue_w(j + DW);
     else issue_h(j + DH);
     // every operand of the stage is read from LDS before the first MFMA:
-    // with one wave per SIMD nothing else hides an LDS read's latency, and
     // the reads return in issue order, so the MFMAs follow them down the queue
-    const char* ws = wring[j % NWR] + wave * NS * 1024 + lane * 16;
+    const char* ws = wring[j % NWR] + vs * NS * 1024 + lane * 16;
     const char* hs = hring[j % NHR];
-    u32x4 af[NS], bf[NS][MT];
+    u32x4 af[NS], bf[NS][MTW];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       af[s] = *reinterpret_cast<const u32x4*>(ws + s * 1024);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        bf[s][mt] = *reinterpret_cast<const u32x4*>(hs + lm_dma_hofs<CH>(mt * 32 + c32, 2 * s + g));
+      for (int k = 0; k < MTW; ++k)
+        bf[s][k] = *reinterpret_cast<const u32x4*>(hs + lm_dma_hofs<CH>((rh * MTW + k) * 32 + c32, 2 * s + g));
     }
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        acc[mt] = mfma_step(__builtin_bit_cast(bf16x8, af[s]), __builtin_bit_cast(bf16x8, bf[s][mt]), acc[mt]);
-    __builtin_amdgcn_sched_group_barrier(0x100, NS * (1 + MT), 0);  // the LDS reads first
-    __builtin_amdgcn_sched_group_barrier(0x008, NS * MT, 0);        // then the MFMAs
+      for (int k = 0; k < MTW; ++k)
+        acc[k] = mfma_step(__builtin_bit_cast(bf16x8, af[s]), __builtin_bit_cast(bf16x8, bf[s][k]), acc[k]);
+    __builtin_amdgcn_sched_group_barrier(0x100, NS * (1 + MTW), 0);  // the LDS reads first
+    __builtin_amdgcn_sched_group_barrier(0x008, NS * MTW, 0);        // then the MFMAs
   }
   wait_vmcnt<0>();  // nothing in flight past the loop (the last stages issue nothing)
 
   // argmax of the tile per hidden row, as in lm_head_tiles: accumulator e of
   // lane (c32, g) holds vocabulary row nbase + 8 (e / 4) + 4 g + e % 4 and
-  // hidden row m0 + 32 mt + c32
+  // hidden row m0 + 32 (rh MTW + k) + c32; the four vocabulary slices of a
+  // row part merge in LDS
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
+  for (int k = 0; k < MTW; ++k) {
     float bv = -INFINITY;
     int bi = 0x7fffffff;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int nn = nbase + 8 * (e >> 2) + 4 * g + (e & 3);
-      if (nn < a.V && acc[mt][e] > bv) {
-        bv = acc[mt][e];
+      if (nn < a.V && acc[k][e] > bv) {
+        bv = acc[k][e];
         bi = nn;
       }
     }
@@ -412,21 +419,21 @@ __global__ void __launch_bounds__(kLmThreads, 1) lm_head_dma(LmArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int nn = nbase + 8 * (e >> 2) + 4 * g + (e & 3);
-        se += nn < a.V ? __builtin_amdgcn_exp2f((acc[mt][e] - bv) * kLog2e) : 0.f;
+        se += nn < a.V ? __builtin_amdgcn_exp2f((acc[k][e] - bv) * kLog2e) : 0.f;
       }
       se += __shfl_xor(se, 32, kWave);
     }
     if (g == 0) {
-      rv[wave][c32] = bv;
-      ri[wave][c32] = bi;
-      rs[wave][c32] = se;
+      rv[rh][vs][c32] = bv;
+      ri[rh][vs][c32] = bi;
+      rs[rh][vs][c32] = se;
     }
     __syncthreads();
-    if (wave == 0 && g == 0) {
+    if (vs == 0 && g == 0) {
       const float wmax0 = bv;
 #pragma unroll
-      for (int w = 1; w < kLmWaves; ++w) lm_keep(bv, bi, rv[w][c32], ri[w][c32]);
-      const int m = m0 + mt * 32 + c32;
+      for (int w = 1; w < kLmWaves; ++w) lm_keep(bv, bi, rv[rh][w][c32], ri[rh][w][c32]);
+      const int m = m0 + (rh * MTW + k) * 32 + c32;
       if (m < a.M) {
         a.part[(size_t)m * a.ntiles + tile] =
             ((unsigned long long)lm_order_bits(bv) << 32) | (unsigned long long)(0xffffffffu - (uint32_t)bi);
@@ -434,7 +441,9 @@ __global__ void __launch_bounds__(kLmThreads, 1) lm_head_dma(LmArgs a) {
           float tot = se * __builtin_amdgcn_exp2f((wmax0 - bv) * kLog2e);
 #pragma unroll
           for (int w = 1; w < kLmWaves; ++w)
-            tot += rv[w][c32] == -INFINITY ? 0.f : rs[w][c32] * __builtin_amdgcn_exp2f((rv[w][c32] - bv) * kLog2e);
+            tot += rv[rh][w][c32] == -INFINITY
+                       ? 0.f
+                       : rs[rh][w][c32] * __builtin_amdgcn_exp2f((rv[rh][w][c32] - bv) * kLog2e);
           a.ms[(size_t)m * a.ntiles + tile] = lm_f32x2{bv, tot};
         }
       }
@@ -443,11 +452,11 @@ __global__ void __launch_bounds__(kLmThreads, 1) lm_head_dma(LmArgs a) {
   }
 }
 
-template <int MT, int KS, int NWR, int NHR, bool NT>
+template <int MT, int KS, int NWR, int NHR, int RH, bool NT>
 static orthrus_status lm_launch_dma(const LmArgs& a, hipStream_t s) {
   const long tiles8 = ((long)a.ntiles + 7) / 8 * 8;
-  hipLaunchKernelGGL((lm_head_dma<MT, KS, NWR, NHR, NT>), dim3((unsigned)(tiles8 * a.mgroups)), dim3(kLmThreads), 0, s,
-                     a);
+  hipLaunchKernelGGL((lm_head_dma<MT, KS, NWR, NHR, RH, NT>), dim3((unsigned)(tiles8 * a.mgroups)),
+                     dim3(kLmThreads * RH), 0, s, a);
   return hipGetLastError() == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_LAUNCH;
 }
 
@@ -608,10 +617,11 @@ static orthrus_status lm_run(LmArgs a, hipStream_t s, int finish_groups) {
   // phases (two waves per SIMD fit).  One row group reads every weight byte
   // once: nontemporal loads (measured about 15 % faster at 32 and 64 rows).
   // More rows: one group of 128, 256 or 512 rows in the DMA kernel (64- or
-  // 32-element stages by what fits LDS).  Measured at the Qwen3-8B head
-  // against 64-row groups of a kernel with two weight tiles per wave: 128
-  // rows 305 -> 286 us, 512 rows 794 -> 772 us; two 256-row groups at 512
-  // rows measured 807 us.  Above 512 rows the 512-row groups of one weight
+  // 32-element stages by what fits LDS), eight waves (two per SIMD, each with
+  // half of the accumulator tiles).  Measured at the Qwen3-8B head against
+  // 64-row groups of a kernel with two weight tiles per wave: 128 rows 305 ->
+  // 286 us with four waves, 275 us with eight; 512 rows 794 -> 772 us with
+  // four, 736 us with eight; two 256-row groups at 512 rows measured 807 us.  Above 512 rows the 512-row groups of one weight
   // tile run on one XCD, so after the first group the tile mostly comes from
   // L2: ordinary loads.
   if (a.M <= 32) {
@@ -622,16 +632,16 @@ static orthrus_status lm_run(LmArgs a, hipStream_t s, int finish_groups) {
     st = lm_launch_tiles<2, 128, true>(a, s);
   } else if (a.M <= 128) {
     a.mgroups = 1;
-    st = lm_launch_dma<4, 64, 6, 3, true>(a, s);
+    st = lm_launch_dma<4, 64, 6, 3, 2, true>(a, s);
   } else if (a.M <= 256) {
     a.mgroups = 1;
-    st = lm_launch_dma<8, 64, 5, 2, true>(a, s);
+    st = lm_launch_dma<8, 64, 5, 2, 2, true>(a, s);
   } else if (a.M <= 512) {
     a.mgroups = 1;
-    st = lm_launch_dma<16, 32, 7, 3, true>(a, s);
+    st = lm_launch_dma<16, 32, 7, 3, 2, true>(a, s);
   } else {
     a.mgroups = (a.M + 511) / 512;
-    st = lm_launch_dma<16, 32, 7, 3, false>(a, s);
+    st = lm_launch_dma<16, 32, 7, 3, 2, false>(a, s);
   }
   if (st != ORTHRUS_OK) return st;
   hipLaunchKernelGGL(lm_head_finish, dim3((unsigned)finish_groups), dim3(kLmFinThreads), 0, s, a);
