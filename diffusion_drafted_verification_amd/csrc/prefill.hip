@@ -113,7 +113,8 @@ static size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 // pairs, but a 2048-token prompt on an empty cache (one round of pairs)
 // 76.5 -> 95 us.
 static int prefill_chunks_per_wg(const orthrus_attn_desc& vd, int B, int C) {
-  if (vd.dtype != ORTHRUS_BF16 || vd.n_q_heads / vd.n_kv_heads > 4) return 1;
+  // the pair kernel serves fixed splits of the streaming path only
+  if (vd.dtype != ORTHRUS_BF16 || vd.n_q_heads / vd.n_kv_heads > 4 || vd.split_tokens <= 0) return 1;
   const long splits = vd.max_ctx_len > 0 ? ((long)vd.max_ctx_len + vd.split_tokens - 1) / vd.split_tokens : 1;
   const long grid = splits * B * ((C + 1) / 2) * vd.n_kv_heads;
   return grid >= 2 * 256 ? 2 : 1;

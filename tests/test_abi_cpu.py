@@ -96,6 +96,7 @@ def test_prefill_chunks_per_workgroup():
     assert f(good_desc(max_ctx_len=0, dtype=1, **pages(512)), 8192) == 1
     assert f(good_desc(max_ctx_len=0, n_q_heads=64, **pages(512)), 8192) == 1
     assert f(good_desc(max_ctx_len=0, **pages(512)), 0) == 0
+    assert f(good_desc(max_ctx_len=0, split_tokens=B.SPLIT_BALANCED, **pages(512)), 8192) == 1
 
 
 def test_split_and_workspace_arithmetic():
