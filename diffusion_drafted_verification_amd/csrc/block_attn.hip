@@ -32,8 +32,12 @@
 //     that XCD's L2;
 //   * the split length is fixed by the host from max_ctx_len, or, for a
 //     ragged batch that asks for it, chosen on the device from ctx_lens so
-//     that one round of about 256 work-groups covers the batch evenly (a
-//     separate instantiation of the streaming kernel and its combine).
+//     that one round of about 256 work-groups covers the batch evenly, or
+//     two rounds of shorter ones where one round would be poorly balanced (a
+//     separate instantiation of the streaming kernel and its combine);
+//   * a prompt prefill runs its 32-row chunks as virtual sequences of this
+//     layout; attn_prefill_pair serves two consecutive chunks per work-group
+//     so that each streamed key feeds twice the query rows.
 #include <type_traits>
 
 #include "orthrus_device.h"
