@@ -13,15 +13,17 @@
 // prefill is one call of the block-attention kernels over B x C "virtual"
 // sequences (C = chunks per sequence), each reading its sequence's page
 // table row:
-//   prefill_setup     virtual page-table rows and context lengths, and the
-//                     sequences' new lengths L_b + prompt_len_b;
-//   prefill_kv_write  prompt rows r < prompt_len_b of k and v to logical
-//                     positions L_b + r (one work-group per row, 16-byte
-//                     copies);
+//   prefill_prepare   one launch: the virtual page-table rows and context
+//                     lengths and the sequences' new lengths L_b +
+//                     prompt_len_b (prefill_setup), and the prompt rows
+//                     r < prompt_len_b of k and v at logical positions
+//                     L_b + r (prefill_kv_write: one work-group per row,
+//                     16-byte copies);
 //   orthrus_block_attn(AR_CAUSAL) on the virtual batch, with the prompt's
 //                     own k/v as the block keys/values.
 // Each chunk's group of G query heads shares one (G x 32)-row MFMA tile per
-// KV head, so every key read serves 32 G query rows.
+// KV head, so every key read serves 32 G query rows (64 G where the pair
+// kernel serves two chunks per work-group).
 #include "orthrus_device.h"
 #include "orthrus_host.h"
 
@@ -45,9 +47,9 @@ struct PrefillArgs {
 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
-// one work-group per virtual sequence (b, j)
-__global__ void __launch_bounds__(256) prefill_setup(PrefillArgs a) {
-  const int bc = blockIdx.x, b = bc / a.C, j = bc % a.C;
+// virtual sequence bc = (b, j): its page-table row and context length
+__device__ void prefill_setup(const PrefillArgs& a, int bc) {
+  const int b = bc / a.C, j = bc % a.C;
   const int L = clampi(a.ctx_lens[b], 0, a.max_ctx);
   const int n = clampi(a.prompt_lens[b], 0, a.S);
   for (int p = threadIdx.x; p < a.max_pages; p += blockDim.x)
@@ -59,9 +61,9 @@ __global__ void __launch_bounds__(256) prefill_setup(PrefillArgs a) {
   }
 }
 
-// one work-group per prompt row (b, r)
-__global__ void __launch_bounds__(256) prefill_kv_write(PrefillArgs a) {
-  const int b = blockIdx.x / a.S, r = blockIdx.x % a.S;
+// prompt row (b, r) into the cache
+__device__ void prefill_kv_write(const PrefillArgs& a, int row) {
+  const int b = row / a.S, r = row % a.S;
   const int n = clampi(a.prompt_lens[b], 0, a.S);
   if (r >= n) return;
   const int pos = clampi(a.ctx_lens[b], 0, a.max_ctx) + r;
@@ -79,6 +81,16 @@ __global__ void __launch_bounds__(256) prefill_kv_write(PrefillArgs a) {
     else
       st16(a.v_cache + dst, ld16(a.v + src_row + uu * 16));
   }
+}
+
+// One launch for both preparations (they write disjoint outputs and the
+// attention launch after it orders them): work-groups 0 .. B C - 1 set up the
+// virtual sequences, the next B S write one prompt row each.  Two launches
+// cost a launch and a kernel boundary more on every prefill call.
+__global__ void __launch_bounds__(256) prefill_prepare(PrefillArgs a) {
+  const long nv = (long)a.B * a.C;
+  if ((long)blockIdx.x < nv) prefill_setup(a, (int)blockIdx.x);
+  else prefill_kv_write(a, (int)((long)blockIdx.x - nv));
 }
 
 // the block-attention descriptor of the virtual batch, validated
@@ -190,9 +202,7 @@ extern "C" orthrus_status orthrus_prefill(const void* q, const void* k, const vo
   a.row_bytes = vd.n_kv_heads * a.head_bytes;
   a.Hkv = vd.n_kv_heads;
   hipStream_t s = (hipStream_t)stream;
-  hipLaunchKernelGGL(prefill_setup, dim3((unsigned)(a.B * C)), dim3(256), 0, s, a);
-  if (hipGetLastError() != hipSuccess) return ORTHRUS_ERR_LAUNCH;
-  hipLaunchKernelGGL(prefill_kv_write, dim3((unsigned)((long)a.B * S)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(prefill_prepare, dim3((unsigned)((long)a.B * C + (long)a.B * S)), dim3(256), 0, s, a);
   if (hipGetLastError() != hipSuccess) return ORTHRUS_ERR_LAUNCH;
   // the chunks re-read the prompt's K/V through the caches: ordinary loads
   return block_attn_run(q, k_cache, v_cache, k, v, a.vtable, a.vctx, ORTHRUS_AR_CAUSAL, out, &vd,
