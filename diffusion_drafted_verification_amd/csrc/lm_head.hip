@@ -37,7 +37,8 @@
 // LDS-DMA, the weight through a deep ring issued by half of the eight waves
 // and the hidden rows through a short ring issued by the other half, and the
 // work-group multiplies its 128 weight rows by all of its 128, 256 or 512
-// hidden rows: each weight byte is read once per call (up to 512 rows).
+// hidden rows (each wave a block of weight slices by accumulator tiles): each
+// weight byte is read once per call (up to 512 rows).
 //
 // lm_head_finish: one work-group per group of rows reduces each row's tile
 // keys (32 threads per row, all loads issued before the reduction), writes the tokens
@@ -245,11 +246,16 @@ __global__ void __launch_bounds__(kLmThreads) lm_head_tiles(LmArgs a) {
 
 // Many hidden rows (65 .. 512 per work-group): both operands reach LDS by
 // LDS-DMA in stages of 32 or 64 hidden elements, and the work-group
-// multiplies its 128-row weight tile by all MT x 32 hidden rows: wave w
-// takes the 32 weight rows of slice w % 4 and MT / RH of the accumulator
-// tiles (row part w / 4; RH = 2: eight waves, two per SIMD, which hides LDS
-// latency and the per-stage barrier better than one wave per SIMD), so each
-// weight byte is read once per call and feeds up to 512 rows.  The weight stream comes from HBM and needs many stages in
+// multiplies its 128-row weight tile by all MT x 32 hidden rows, so each
+// weight byte is read once per call and feeds up to 512 rows.  Eight waves,
+// two per SIMD (which hides LDS latency and the per-stage barrier better than
+// one wave per SIMD): wave w computes a block of VW 32-row weight slices
+// (vocabulary part w % (4 / VW)) by RW 32-row accumulator tiles (row part
+// w / (4 / VW)).  Per k-step a wave reads VW + RW operand fragments from LDS
+// for VW RW products: blocks of 2 x 2 (256 rows) and 4 x 2 (512 rows) read a
+// third less of LDS per product than 1 x 4 and 1 x 8, and with VW = 4 the
+// wave owns whole tile rows, so no vocabulary parts merge in LDS.  The
+// weight stream comes from HBM and needs many stages in
 // flight; the hidden rows come from L2 and need few.  Loads complete in
 // issue order per wave, so one wave that issued both would wait for the deep
 // weight prefetch whenever it needs the next hidden stage.  Hence the issue
@@ -283,10 +289,11 @@ __device__ __forceinline__ void lm_wait_stages(int k) {
   }
 }
 
-template <int MT, int KS, int NWR, int NHR, int RH, bool NT>
-__global__ void __launch_bounds__(kLmThreads * RH, 1) lm_head_dma(LmArgs a) {
-  constexpr int NWV = kLmWaves * RH;            // waves: 4 vocabulary slices x RH row parts
-  constexpr int MTW = MT / RH;                  // accumulator tiles per wave
+template <int MT, int KS, int NWR, int NHR, int VW, int RW, bool NT>
+__global__ void __launch_bounds__(kWave * (kLmWaves / VW) * (MT / RW), 1) lm_head_dma(LmArgs a) {
+  constexpr int NVP = kLmWaves / VW;            // vocabulary parts (VW 32-row weight slices each)
+  constexpr int NRP = MT / RW;                  // row parts (RW accumulator tiles of 32 rows each)
+  constexpr int NWV = NVP * NRP;                // waves
   constexpr int ROWS = MT * 32;
   constexpr int NS = KS / 16;                   // MFMA k-steps per stage
   constexpr int CH = KS / 8;                    // 16-byte chunks of a hidden row per stage
@@ -296,15 +303,16 @@ __global__ void __launch_bounds__(kLmThreads * RH, 1) lm_head_dma(LmArgs a) {
   constexpr int NWI = kLmWaves * NS / NIW;      // weight DMA instructions per issuing wave and stage
   constexpr int NHI = HSTAGE / 1024 / NIW;      // hidden DMA instructions per issuing wave and stage
   static_assert(KS == 32 || KS == 64, "stage of 32 or 64 hidden elements");
-  static_assert(MT % RH == 0 && NWI * NIW == kLmWaves * NS && NHI * NIW * 1024 == HSTAGE, "issue shape");
+  static_assert(kLmWaves % VW == 0 && MT % RW == 0, "wave tiling");
+  static_assert(NWI * NIW == kLmWaves * NS && NHI * NIW * 1024 == HSTAGE, "issue shape");
   constexpr int DW = NWR - 1, DH = NHR - 1;    // stages in flight ahead of the one in use
   static_assert(DW >= 1 && DH >= 1, "at least one stage ahead");
   static_assert((DW - 1) * NWI <= 63 && (DH - 1) * NHI <= 63, "wait counts fit vmcnt");
   __shared__ __attribute__((aligned(1024))) char wring[NWR][WSTAGE];
   __shared__ __attribute__((aligned(1024))) char hring[NHR][HSTAGE];
-  __shared__ float rv[RH][kLmWaves][32];
-  __shared__ int ri[RH][kLmWaves][32];
-  __shared__ float rs[RH][kLmWaves][32];
+  __shared__ float rv[NRP][NVP][32];
+  __shared__ int ri[NRP][NVP][32];
+  __shared__ float rs[NRP][NVP][32];
 
   // block -> (tile, row group): the row groups of one tile share an XCD
   const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
@@ -313,17 +321,16 @@ __global__ void __launch_bounds__(kLmThreads * RH, 1) lm_head_dma(LmArgs a) {
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
-  const int vs = wave % kLmWaves, rh = wave / kLmWaves;  // vocabulary slice, row part
+  const int vp = wave % NVP, rp = wave / NVP;  // vocabulary part, row part
   const int g = lane >> 5, c32 = lane & 31;
   const int m0 = mg * ROWS;
-  const int nbase = tile * kLmTileN + vs * 32;
   const int steps = a.H / 16;
   const int P = a.H / KS;
   const int last32 = (a.V - 1) / 32;
 
   // weight issue (waves 0 .. NIW - 1): instruction q = NWI w + i covers
-  // tile q / NS, step q % NS of the stage; 32-row tiles past the padded
-  // vocabulary read the last tile (in bounds), their rows are dropped below
+  // slice q / NS, step q % NS of the stage; 32-row slices past the padded
+  // vocabulary read the last slice (in bounds), their rows are dropped below
   auto issue_w = [&](int j) {
     if (j >= P) return;
     char* dst = wring[j % NWR];
@@ -354,11 +361,13 @@ __global__ void __launch_bounds__(kLmThreads * RH, 1) lm_head_dma(LmArgs a) {
     }
   };
 
-  f32x16 acc[MTW];
+  f32x16 acc[VW][RW];
 #pragma unroll
-  for (int k = 0; k < MTW; ++k)
+  for (int v = 0; v < VW; ++v)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[k][e] = 0.f;
+    for (int k = 0; k < RW; ++k)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[v][k][e] = 0.f;
 
   const bool wissue = wave < NIW;
   if (wissue) {
@@ -377,86 +386,100 @@ __global__ void __launch_bounds__(kLmThreads * RH, 1) lm_head_dma(LmArgs a) {
     else issue_h(j + DH);
     // every operand of the stage is read from LDS before the first MFMA:
     // the reads return in issue order, so the MFMAs follow them down the queue
-    const char* ws = wring[j % NWR] + vs * NS * 1024 + lane * 16;
+    const char* ws = wring[j % NWR] + vp * VW * NS * 1024 + lane * 16;
     const char* hs = hring[j % NHR];
-    u32x4 af[NS], bf[NS][MTW];
+    u32x4 af[NS][VW], bf[NS][RW];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      af[s] = *reinterpret_cast<const u32x4*>(ws + s * 1024);
 #pragma unroll
-      for (int k = 0; k < MTW; ++k)
-        bf[s][k] = *reinterpret_cast<const u32x4*>(hs + lm_dma_hofs<CH>((rh * MTW + k) * 32 + c32, 2 * s + g));
+      for (int v = 0; v < VW; ++v) af[s][v] = *reinterpret_cast<const u32x4*>(ws + (v * NS + s) * 1024);
+#pragma unroll
+      for (int k = 0; k < RW; ++k)
+        bf[s][k] = *reinterpret_cast<const u32x4*>(hs + lm_dma_hofs<CH>((rp * RW + k) * 32 + c32, 2 * s + g));
     }
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
-      for (int k = 0; k < MTW; ++k)
-        acc[k] = mfma_step(__builtin_bit_cast(bf16x8, af[s]), __builtin_bit_cast(bf16x8, bf[s][k]), acc[k]);
-    __builtin_amdgcn_sched_group_barrier(0x100, NS * (1 + MTW), 0);  // the LDS reads first
-    __builtin_amdgcn_sched_group_barrier(0x008, NS * MTW, 0);        // then the MFMAs
+      for (int v = 0; v < VW; ++v)
+#pragma unroll
+        for (int k = 0; k < RW; ++k)
+          acc[v][k] = mfma_step(__builtin_bit_cast(bf16x8, af[s][v]), __builtin_bit_cast(bf16x8, bf[s][k]),
+                                acc[v][k]);
+    __builtin_amdgcn_sched_group_barrier(0x100, NS * (VW + RW), 0);  // the LDS reads first
+    __builtin_amdgcn_sched_group_barrier(0x008, NS * VW * RW, 0);    // then the MFMAs
   }
   wait_vmcnt<0>();  // nothing in flight past the loop (the last stages issue nothing)
 
   // argmax of the tile per hidden row, as in lm_head_tiles: accumulator e of
-  // lane (c32, g) holds vocabulary row nbase + 8 (e / 4) + 4 g + e % 4 and
-  // hidden row m0 + 32 (rh MTW + k) + c32; the four vocabulary slices of a
-  // row part merge in LDS
+  // acc[v][k] in lane (c32, g) holds vocabulary row nbase_v + 8 (e / 4) +
+  // 4 g + e % 4 (nbase_v = first row of the wave's slice v) and hidden row
+  // m0 + 32 (rp RW + k) + c32; slices are visited in vocabulary order, so a
+  // strict compare keeps the lowest index; the NVP vocabulary parts of a row
+  // part merge in LDS
+  const int nbase = tile * kLmTileN + vp * VW * 32;
 #pragma unroll
-  for (int k = 0; k < MTW; ++k) {
+  for (int k = 0; k < RW; ++k) {
     float bv = -INFINITY;
     int bi = 0x7fffffff;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int nn = nbase + 8 * (e >> 2) + 4 * g + (e & 3);
-      if (nn < a.V && acc[k][e] > bv) {
-        bv = acc[k][e];
-        bi = nn;
+    for (int v = 0; v < VW; ++v)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int nn = nbase + 32 * v + 8 * (e >> 2) + 4 * g + (e & 3);
+        if (nn < a.V && acc[v][k][e] > bv) {
+          bv = acc[v][k][e];
+          bi = nn;
+        }
       }
-    }
     lm_keep(bv, bi, __shfl_xor(bv, 32, kWave), __shfl_xor(bi, 32, kWave));
     float se = 0.f;
     if (a.ms) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int nn = nbase + 8 * (e >> 2) + 4 * g + (e & 3);
-        se += nn < a.V ? __builtin_amdgcn_exp2f((acc[k][e] - bv) * kLog2e) : 0.f;
-      }
+      for (int v = 0; v < VW; ++v)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int nn = nbase + 32 * v + 8 * (e >> 2) + 4 * g + (e & 3);
+          se += nn < a.V ? __builtin_amdgcn_exp2f((acc[v][k][e] - bv) * kLog2e) : 0.f;
+        }
       se += __shfl_xor(se, 32, kWave);
     }
-    if (g == 0) {
-      rv[rh][vs][c32] = bv;
-      ri[rh][vs][c32] = bi;
-      rs[rh][vs][c32] = se;
+    if constexpr (NVP > 1) {
+      if (g == 0) {
+        rv[rp][vp][c32] = bv;
+        ri[rp][vp][c32] = bi;
+        rs[rp][vp][c32] = se;
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    if (vs == 0 && g == 0) {
+    if (vp == 0 && g == 0) {
       const float wmax0 = bv;
 #pragma unroll
-      for (int w = 1; w < kLmWaves; ++w) lm_keep(bv, bi, rv[rh][w][c32], ri[rh][w][c32]);
-      const int m = m0 + (rh * MTW + k) * 32 + c32;
+      for (int w = 1; w < NVP; ++w) lm_keep(bv, bi, rv[rp][w][c32], ri[rp][w][c32]);
+      const int m = m0 + (rp * RW + k) * 32 + c32;
       if (m < a.M) {
         a.part[(size_t)m * a.ntiles + tile] =
             ((unsigned long long)lm_order_bits(bv) << 32) | (unsigned long long)(0xffffffffu - (uint32_t)bi);
         if (a.ms) {
+          // parts whose rows are all past V hold (-inf, 0) and add nothing
           float tot = se * __builtin_amdgcn_exp2f((wmax0 - bv) * kLog2e);
 #pragma unroll
-          for (int w = 1; w < kLmWaves; ++w)
-            tot += rv[rh][w][c32] == -INFINITY
+          for (int w = 1; w < NVP; ++w)
+            tot += rv[rp][w][c32] == -INFINITY
                        ? 0.f
-                       : rs[rh][w][c32] * __builtin_amdgcn_exp2f((rv[rh][w][c32] - bv) * kLog2e);
+                       : rs[rp][w][c32] * __builtin_amdgcn_exp2f((rv[rp][w][c32] - bv) * kLog2e);
           a.ms[(size_t)m * a.ntiles + tile] = lm_f32x2{bv, tot};
         }
       }
     }
-    __syncthreads();
+    if constexpr (NVP > 1) __syncthreads();
   }
 }
 
-template <int MT, int KS, int NWR, int NHR, int RH, bool NT>
+template <int MT, int KS, int NWR, int NHR, int VW, int RW, bool NT>
 static orthrus_status lm_launch_dma(const LmArgs& a, hipStream_t s) {
   const long tiles8 = ((long)a.ntiles + 7) / 8 * 8;
-  hipLaunchKernelGGL((lm_head_dma<MT, KS, NWR, NHR, RH, NT>), dim3((unsigned)(tiles8 * a.mgroups)),
-                     dim3(kLmThreads * RH), 0, s, a);
+  hipLaunchKernelGGL((lm_head_dma<MT, KS, NWR, NHR, VW, RW, NT>), dim3((unsigned)(tiles8 * a.mgroups)),
+                     dim3(kWave * (kLmWaves / VW) * (MT / RW)), 0, s, a);
   return hipGetLastError() == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_LAUNCH;
 }
 
@@ -617,13 +640,17 @@ static orthrus_status lm_run(LmArgs a, hipStream_t s, int finish_groups) {
   // phases (two waves per SIMD fit).  One row group reads every weight byte
   // once: nontemporal loads (measured about 15 % faster at 32 and 64 rows).
   // More rows: one group of 128, 256 or 512 rows in the DMA kernel (64- or
-  // 32-element stages by what fits LDS), eight waves (two per SIMD, each with
-  // half of the accumulator tiles).  Measured at the Qwen3-8B head against
-  // 64-row groups of a kernel with two weight tiles per wave: 128 rows 305 ->
-  // 286 us with four waves, 275 us with eight; 512 rows 794 -> 772 us with
-  // four, 736 us with eight; two 256-row groups at 512 rows measured 807 us.  Above 512 rows the 512-row groups of one weight
-  // tile run on one XCD, so after the first group the tile mostly comes from
-  // L2: ordinary loads.
+  // 32-element stages by what fits LDS), eight waves (two per SIMD) with wave
+  // blocks of 1 x 2, 2 x 2 and 4 x 2 (weight slices x accumulator tiles).
+  // Measured at the Qwen3-8B head against 64-row groups of a kernel with two
+  // weight tiles per wave: 128 rows 305 -> 286 us with four waves, 275 us
+  // with eight; 512 rows 794 -> 772 us with four, 736 us with eight; two
+  // 256-row groups at 512 rows measured 807 us.  Against eight waves of
+  // 1 x MT / 2 blocks (alternating runs on one box): 256 rows 417-419 ->
+  // 398-400 us, 512 rows 742-745 -> 700-709 us (2 x 4 blocks: 711-720 us),
+  // 128 rows unchanged with 2 x 1.  Above 512 rows the 512-row groups of one
+  // weight tile run on one XCD, so after the first group the tile mostly
+  // comes from L2: ordinary loads.
   if (a.M <= 32) {
     a.mgroups = 1;
     st = lm_launch_tiles<1, 256, true>(a, s);
@@ -632,16 +659,16 @@ static orthrus_status lm_run(LmArgs a, hipStream_t s, int finish_groups) {
     st = lm_launch_tiles<2, 128, true>(a, s);
   } else if (a.M <= 128) {
     a.mgroups = 1;
-    st = lm_launch_dma<4, 64, 6, 3, 2, true>(a, s);
+    st = lm_launch_dma<4, 64, 6, 3, 1, 2, true>(a, s);
   } else if (a.M <= 256) {
     a.mgroups = 1;
-    st = lm_launch_dma<8, 64, 5, 2, 2, true>(a, s);
+    st = lm_launch_dma<8, 64, 5, 2, 2, 2, true>(a, s);
   } else if (a.M <= 512) {
     a.mgroups = 1;
-    st = lm_launch_dma<16, 32, 7, 3, 2, true>(a, s);
+    st = lm_launch_dma<16, 32, 7, 3, 4, 2, true>(a, s);
   } else {
     a.mgroups = (a.M + 511) / 512;
-    st = lm_launch_dma<16, 32, 7, 3, 2, false>(a, s);
+    st = lm_launch_dma<16, 32, 7, 3, 4, 2, false>(a, s);
   }
   if (st != ORTHRUS_OK) return st;
   hipLaunchKernelGGL(lm_head_finish, dim3((unsigned)finish_groups), dim3(kLmFinThreads), 0, s, a);
