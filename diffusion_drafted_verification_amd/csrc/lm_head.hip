@@ -34,11 +34,10 @@
 // several groups, the later groups find the weight tile in that XCD's L2.
 //
 // lm_head_dma (more than 64 hidden rows): both operands reach LDS by
-// LDS-DMA, the weight through a deep ring issued by half of the eight waves
-// and the hidden rows through a short ring issued by the other half, and the
-// work-group multiplies its 128 weight rows by all of its 128, 256 or 512
-// hidden rows (each wave a block of weight slices by accumulator tiles): each
-// weight byte is read once per call (up to 512 rows).
+// LDS-DMA, the weight issued by half of the eight waves and the hidden rows by
+// the other half, and the work-group multiplies a tile of 128 weight rows by
+// 128 hidden rows, or 256 by 256 (each wave a block of weight slices by
+// accumulator tiles).  The two 256-row groups of 512 rows run on one XCD.
 //
 // lm_head_finish: one work-group per group of rows reduces each row's tile
 // keys (32 threads per row, all loads issued before the reduction), writes the tokens
@@ -244,19 +243,20 @@ __global__ void __launch_bounds__(kLmThreads) lm_head_tiles(LmArgs a) {
   }
 }
 
-// Many hidden rows (65 .. 512 per work-group): both operands reach LDS by
-// LDS-DMA in stages of 32 or 64 hidden elements, and the work-group
-// multiplies its 128-row weight tile by all MT x 32 hidden rows, so each
-// weight byte is read once per call and feeds up to 512 rows.  Eight waves,
-// two per SIMD (which hides LDS latency and the per-stage barrier better than
-// one wave per SIMD): wave w computes a block of VW 32-row weight slices
-// (vocabulary part w % (4 / VW)) by RW 32-row accumulator tiles (row part
-// w / (4 / VW)).  Per k-step a wave reads VW + RW operand fragments from LDS
-// for VW RW products: blocks of 2 x 2 (256 rows) and 4 x 2 (512 rows) read a
-// third less of LDS per product than 1 x 4 and 1 x 8, and with VW = 4 the
-// wave owns whole tile rows, so no vocabulary parts merge in LDS.  The
-// weight stream comes from HBM and needs many stages in
-// flight; the hidden rows come from L2 and need few.  Loads complete in
+// Many hidden rows (more than 64): both operands reach LDS by LDS-DMA in
+// stages of 32 or 64 hidden elements, and the work-group multiplies a tile of
+// NSL 32-row weight slices by MT 32-row accumulator tiles.  Eight waves, two
+// per SIMD (which hides LDS latency and the per-stage barrier better than one
+// wave per SIMD): wave w computes a block of VW weight slices (vocabulary part
+// w % (NSL / VW)) by RW accumulator tiles (row part w / (NSL / VW)).  Per
+// k-step a wave reads VW + RW operand fragments from LDS for VW RW products.
+// Moving the operands into LDS is what bounds this kernel: with its MFMAs
+// taken out it ran nearly as long (670 against 720 us at 512 rows), and each
+// CU moved about 40 GB/s whatever the mix of HBM and L2 bytes.  So the tile
+// is chosen for bytes per product: 256 x 256 (65,536 accumulators, 128
+// registers per lane) moves (256 + 256) rows per k for the products that
+// 128 x 512 serves with (128 + 512).  The weight stream comes from HBM and
+// the hidden rows from L2.  Loads complete in
 // issue order per wave, so one wave that issued both would wait for the deep
 // weight prefetch whenever it needs the next hidden stage.  Hence the issue
 // is split by wave: the first half of the waves issue only the weight DMA
@@ -289,30 +289,33 @@ __device__ __forceinline__ void lm_wait_stages(int k) {
   }
 }
 
-template <int MT, int KS, int NWR, int NHR, int VW, int RW, bool NT>
-__global__ void __launch_bounds__(kWave * (kLmWaves / VW) * (MT / RW), 1) lm_head_dma(LmArgs a) {
-  constexpr int NVP = kLmWaves / VW;            // vocabulary parts (VW 32-row weight slices each)
+template <int NSL, int MT, int KS, int NWR, int NHR, int VW, int RW, bool NT>
+__global__ void __launch_bounds__(kWave * (NSL / VW) * (MT / RW), 1) lm_head_dma(LmArgs a) {
+  constexpr int NVP = NSL / VW;                 // vocabulary parts (VW 32-row weight slices each)
   constexpr int NRP = MT / RW;                  // row parts (RW accumulator tiles of 32 rows each)
   constexpr int NWV = NVP * NRP;                // waves
   constexpr int ROWS = MT * 32;
   constexpr int NS = KS / 16;                   // MFMA k-steps per stage
   constexpr int CH = KS / 8;                    // 16-byte chunks of a hidden row per stage
-  constexpr int WSTAGE = kLmWaves * NS * 1024;  // weight bytes per stage
+  constexpr int WSTAGE = NSL * NS * 1024;       // weight bytes per stage
   constexpr int HSTAGE = ROWS * KS * 2;         // hidden bytes per stage
   constexpr int NIW = NWV / 2;                  // waves issuing each operand
-  constexpr int NWI = kLmWaves * NS / NIW;      // weight DMA instructions per issuing wave and stage
+  constexpr int NWI = NSL * NS / NIW;           // weight DMA instructions per issuing wave and stage
   constexpr int NHI = HSTAGE / 1024 / NIW;      // hidden DMA instructions per issuing wave and stage
   static_assert(KS == 32 || KS == 64, "stage of 32 or 64 hidden elements");
-  static_assert(kLmWaves % VW == 0 && MT % RW == 0, "wave tiling");
-  static_assert(NWI * NIW == kLmWaves * NS && NHI * NIW * 1024 == HSTAGE, "issue shape");
+  static_assert(NSL % VW == 0 && MT % RW == 0, "wave tiling");
+  static_assert(NWI * NIW == NSL * NS && NHI * NIW * 1024 == HSTAGE, "issue shape");
   constexpr int DW = NWR - 1, DH = NHR - 1;    // stages in flight ahead of the one in use
   static_assert(DW >= 1 && DH >= 1, "at least one stage ahead");
   static_assert((DW - 1) * NWI <= 63 && (DH - 1) * NHI <= 63, "wait counts fit vmcnt");
   __shared__ __attribute__((aligned(1024))) char wring[NWR][WSTAGE];
   __shared__ __attribute__((aligned(1024))) char hring[NHR][HSTAGE];
-  __shared__ float rv[NRP][NVP][32];
-  __shared__ int ri[NRP][NVP][32];
-  __shared__ float rs[NRP][NVP][32];
+  // the epilogue's merge of the vocabulary parts reuses the weight ring
+  // (dead once every wave is past the loop), so the rings may take all of LDS
+  static_assert(3 * NRP * NVP * 32 * 4 <= NWR * WSTAGE, "merge arrays fit the weight ring");
+  float(*rv)[NVP][32] = reinterpret_cast<float(*)[NVP][32]>(&wring[0][0]);
+  int(*ri)[NVP][32] = reinterpret_cast<int(*)[NVP][32]>(&wring[0][0] + NRP * NVP * 32 * 4);
+  float(*rs)[NVP][32] = reinterpret_cast<float(*)[NVP][32]>(&wring[0][0] + 2 * NRP * NVP * 32 * 4);
 
   // block -> (tile, row group): the row groups of one tile share an XCD
   const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
@@ -337,7 +340,7 @@ __global__ void __launch_bounds__(kWave * (kLmWaves / VW) * (MT / RW), 1) lm_hea
 #pragma unroll
     for (int i = 0; i < NWI; ++i) {
       const int q = NWI * wave + i, t = q / NS, s = q % NS;
-      const int t32 = min(tile * (kLmTileN / 32) + t, last32);
+      const int t32 = min(tile * NSL + t, last32);
       const u32x4* src = a.w + ((size_t)t32 * steps + NS * j + s) * kWave + lane;
       if (NT) dma16_nt(src, dst + q * 1024);
       else dma16(src, dst + q * 1024);
@@ -409,6 +412,7 @@ __global__ void __launch_bounds__(kWave * (kLmWaves / VW) * (MT / RW), 1) lm_hea
     __builtin_amdgcn_sched_group_barrier(0x008, NS * VW * RW, 0);    // then the MFMAs
   }
   wait_vmcnt<0>();  // nothing in flight past the loop (the last stages issue nothing)
+  if constexpr (NVP > 1) __syncthreads();  // every wave's last ring reads are done
 
   // argmax of the tile per hidden row, as in lm_head_tiles: accumulator e of
   // acc[v][k] in lane (c32, g) holds vocabulary row nbase_v + 8 (e / 4) +
@@ -416,7 +420,7 @@ __global__ void __launch_bounds__(kWave * (kLmWaves / VW) * (MT / RW), 1) lm_hea
   // m0 + 32 (rp RW + k) + c32; slices are visited in vocabulary order, so a
   // strict compare keeps the lowest index; the NVP vocabulary parts of a row
   // part merge in LDS
-  const int nbase = tile * kLmTileN + vp * VW * 32;
+  const int nbase = tile * NSL * 32 + vp * VW * 32;
 #pragma unroll
   for (int k = 0; k < RW; ++k) {
     float bv = -INFINITY;
@@ -475,11 +479,12 @@ __global__ void __launch_bounds__(kWave * (kLmWaves / VW) * (MT / RW), 1) lm_hea
   }
 }
 
-template <int MT, int KS, int NWR, int NHR, int VW, int RW, bool NT>
-static orthrus_status lm_launch_dma(const LmArgs& a, hipStream_t s) {
+template <int NSL, int MT, int KS, int NWR, int NHR, int VW, int RW, bool NT>
+static orthrus_status lm_launch_dma(LmArgs& a, hipStream_t s) {
+  a.ntiles = (a.V + 32 * NSL - 1) / (32 * NSL);
   const long tiles8 = ((long)a.ntiles + 7) / 8 * 8;
-  hipLaunchKernelGGL((lm_head_dma<MT, KS, NWR, NHR, VW, RW, NT>), dim3((unsigned)(tiles8 * a.mgroups)),
-                     dim3(kWave * (kLmWaves / VW) * (MT / RW)), 0, s, a);
+  hipLaunchKernelGGL((lm_head_dma<NSL, MT, KS, NWR, NHR, VW, RW, NT>), dim3((unsigned)(tiles8 * a.mgroups)),
+                     dim3(kWave * (NSL / VW) * (MT / RW)), 0, s, a);
   return hipGetLastError() == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_LAUNCH;
 }
 
@@ -639,18 +644,20 @@ static orthrus_status lm_run(LmArgs a, hipStream_t s, int finish_groups) {
   // 32 rows: one group, deep phases.  64 rows: one 64-row group with shallow
   // phases (two waves per SIMD fit).  One row group reads every weight byte
   // once: nontemporal loads (measured about 15 % faster at 32 and 64 rows).
-  // More rows: one group of 128, 256 or 512 rows in the DMA kernel (64- or
-  // 32-element stages by what fits LDS), eight waves (two per SIMD) with wave
-  // blocks of 1 x 2, 2 x 2 and 4 x 2 (weight slices x accumulator tiles).
-  // Measured at the Qwen3-8B head against 64-row groups of a kernel with two
-  // weight tiles per wave: 128 rows 305 -> 286 us with four waves, 275 us
-  // with eight; 512 rows 794 -> 772 us with four, 736 us with eight; two
-  // 256-row groups at 512 rows measured 807 us.  Against eight waves of
-  // 1 x MT / 2 blocks (alternating runs on one box): 256 rows 417-419 ->
-  // 398-400 us, 512 rows 742-745 -> 700-709 us (2 x 4 blocks: 711-720 us),
-  // 128 rows unchanged with 2 x 1.  Above 512 rows the 512-row groups of one
-  // weight tile run on one XCD, so after the first group the tile mostly
-  // comes from L2: ordinary loads.
+  // More rows: the DMA kernel, eight waves (two per SIMD).  128 rows: 128 x
+  // 128 tiles in 64-element stages.  256 rows: 256 x 256 tiles.  512 rows:
+  // the two 256-row groups of each 256-row weight tile on one XCD; the
+  // nontemporal hint measured slightly faster there than ordinary loads
+  // (638-643 against 647-650 us), though each group reads the tile.  Measured
+  // at the Qwen3-8B head (alternating runs on one box, us per call): 128 x 512
+  // tiles with 4 x 2 wave blocks took 697-711 us at 512 rows, 256 x 256 tiles
+  // 628-634; at 256 rows 128 x 256 tiles with 2 x 2 blocks took 400-416 us,
+  // 256 x 256 tiles 386-390.  128 x 128 tiles at 128 rows measured the same
+  // as 256 x 128 (594 work-groups, three rounds).  Earlier: eight waves
+  // beat four (275 against 286 us at 128 rows), and squarer wave blocks beat
+  // 1 x MT / 2 ones by about 5 %.  Above 512 rows, 256-row groups of one
+  // weight tile run on one XCD with ordinary loads, so after the first group
+  // the tile mostly comes from L2.
   if (a.M <= 32) {
     a.mgroups = 1;
     st = lm_launch_tiles<1, 256, true>(a, s);
@@ -659,16 +666,16 @@ static orthrus_status lm_run(LmArgs a, hipStream_t s, int finish_groups) {
     st = lm_launch_tiles<2, 128, true>(a, s);
   } else if (a.M <= 128) {
     a.mgroups = 1;
-    st = lm_launch_dma<4, 64, 6, 3, 1, 2, true>(a, s);
+    st = lm_launch_dma<4, 4, 64, 6, 3, 1, 2, true>(a, s);
   } else if (a.M <= 256) {
     a.mgroups = 1;
-    st = lm_launch_dma<8, 64, 5, 2, 2, 2, true>(a, s);
+    st = lm_launch_dma<8, 8, 32, 6, 4, 2, 4, true>(a, s);
   } else if (a.M <= 512) {
-    a.mgroups = 1;
-    st = lm_launch_dma<16, 32, 7, 3, 4, 2, true>(a, s);
+    a.mgroups = 2;
+    st = lm_launch_dma<8, 8, 32, 4, 6, 4, 2, true>(a, s);
   } else {
-    a.mgroups = (a.M + 511) / 512;
-    st = lm_launch_dma<16, 32, 7, 3, 4, 2, false>(a, s);
+    a.mgroups = (a.M + 255) / 256;
+    st = lm_launch_dma<8, 8, 32, 4, 6, 4, 2, false>(a, s);
   }
   if (st != ORTHRUS_OK) return st;
   hipLaunchKernelGGL(lm_head_finish, dim3((unsigned)finish_groups), dim3(kLmFinThreads), 0, s, a);

@@ -91,8 +91,13 @@ def check_step(h, w, masked, n, head=None, max_excused=1, seqs=None):
     return tok, conf, nm
 
 
-@pytest.mark.parametrize("B,K,H,V", [(1, 32, 256, 1000), (4, 32, 1024, 20011), (3, 7, 512, 5000), (2, 1, 256, 300)])
+@pytest.mark.parametrize("B,K,H,V", [(1, 32, 256, 1000), (4, 32, 1024, 20011), (3, 7, 512, 5000), (2, 1, 256, 300),
+                                     (7, 32, 512, 5000), (10, 32, 256, 3001)])
 def test_denoise_random_vs_oracle(B, K, H, V):
+    """Up to 32 rows (the tile kernel), 128 rows (the many-row kernel's
+    128 x 128 tiles), 224 rows (256 x 256 tiles, four vocabulary parts merge
+    their softmax statistics in LDS) and 320 rows (two 256-row groups, two
+    parts), ragged vocabularies."""
     say("denoise random", B, K, H, V)
     h, w, _ = I.make_lm_head_inputs(B * K, H, V, seed=B * K + V)
     masked, n = masks_and_counts(B, K, seed=V)
@@ -108,9 +113,9 @@ def test_denoise_qwen3_8b_head():
 
 
 def test_denoise_qwen3_8b_head_b16_sampled():
-    """The benchmark's B16 rows (512, one work-group's rows in the many-row
+    """The benchmark's B16 rows (512: two 256-row groups of the many-row
     kernel) at the Qwen3-8B head; the oracle checks sequences at both ends
-    and on both sides of the 256-row point."""
+    and on both sides of the groups' boundary at row 256."""
     say("denoise qwen3-8b B16 sampled")
     B, K = 16, 32
     h, w, _ = I.make_lm_head_inputs(B * K, I.QWEN3_8B_HIDDEN, I.QWEN3_VOCAB, seed=16)

@@ -84,9 +84,11 @@ def check_random(rows, H, V, seed, sample=None):
                                       (600, 256, 1500)])
 def test_lm_head_random_vs_oracle(rows, H, V):
     """Row counts 1..600 cover every kernel and row grouping: one 32-row
-    group, one 64-row group, one group of 128, 256 and 512 rows of the
-    many-row kernel (ragged tails), and two 512-row groups; vocabularies
-    from 777 to 20000 cover ragged 128-row tiles."""
+    group, one 64-row group, the many-row kernel's 128 x 128 tiles (100
+    rows), 256 x 256 tiles in one row group (130 rows) and in two (257 rows:
+    a one-row second group), and three 256-row groups with ordinary weight
+    loads (600 rows); vocabularies from 777 to 20000 cover ragged 128- and
+    256-row tiles."""
     say("lm_head random", rows, H, V)
     check_random(rows, H, V, seed=rows + V)
 
@@ -99,9 +101,10 @@ def test_lm_head_qwen3_8b_random():
 @pytest.mark.parametrize("rows", [128, 512])
 def test_lm_head_qwen3_8b_random_wide_rows_sampled(rows):
     """The benchmark's B4 and B16 row counts at the Qwen3-8B head (the
-    many-row kernel: all rows in one work-group, 32-row accumulator tiles):
-    the oracle checks rows on both sides of accumulator-tile boundaries and
-    the last row."""
+    many-row kernel: 128 rows in one work-group; 512 rows in two 256-row
+    groups): the oracle checks rows on both sides of 32-row accumulator-tile
+    boundaries (every 64 rows at 512, including the groups' boundary at 256)
+    and the last row."""
     say("lm_head qwen3-8b random wide", rows)
     step = 32 if rows <= 128 else 64
     sample = sorted({0} | {m for k in range(step, rows, step) for m in (k - 1, k)} | {rows - 1})
@@ -140,19 +143,27 @@ def test_lm_head_planted_ties_resolve_to_lowest_index():
         assert tok.item() == min(winner, copy) and mx.item() == float(H), (winner, copy, tok.item())
 
 
-def test_lm_head_planted_ties_many_rows():
-    """The same ties with more than 64 hidden rows (the many-row kernel:
-    128-row key tiles, every wave's 32-row weight slice multiplied by all
-    rows): copies in the same 32-row slice, in the other lane half, in another
-    wave of the same 128-row tile, and in another tile, before or after the
-    winner.  Every row must give the lower index of the pair, exactly."""
-    say("lm_head ties, many rows")
+@pytest.mark.parametrize("rows", [96, 200, 300])
+def test_lm_head_planted_ties_many_rows(rows):
+    """The same ties with more than 64 hidden rows, in each tiling of the
+    many-row kernel: 96 rows (128-row key tiles, one weight slice per wave),
+    200 rows (256-row key tiles, two slices per wave, four vocabulary parts
+    merged in LDS) and 300 rows (256-row key tiles, four slices per wave, two
+    parts; two row groups).  Copies in the same 32-row slice, in the other
+    lane half, in another slice of the same wave, in another vocabulary part
+    of the same tile, and in another tile, before or after the winner.  Every
+    row must give the lower index of the pair, exactly."""
+    say("lm_head ties, many rows", rows)
     d = dev()
-    H, V, rows = 1024, 10000, 96
+    H, V = 1024, 10000
     _, w, _ = I.make_lm_head_inputs(1, H, V, seed=6, planted=True, device=d)
-    # 5000 and 5030 sit in different waves' 32-row slices of one 128-row tile
-    cases = [(5030, 5000), (5000, 5030), (5000, 4997), (5000, 4990), (5000, 5100), (5000, 4863), (9999, 9998),
-             (300, 44)]
+    # 128-row tiles: 5000 and 5030 sit in different waves' slices of one
+    # tile.  256-row tiles (4864 .. 5119): 5000 (slice 4) and 5030 (slice 5)
+    # share a wave; 4990 (slice 3) is in another vocabulary part; 5100
+    # (slice 7) shares the wave at four slices per wave and not at two;
+    # 4863 and 5200 are in the neighbouring tiles
+    cases = [(5030, 5000), (5000, 5030), (5000, 4997), (5000, 4990), (5000, 5100), (5000, 4863), (5000, 5200),
+             (9999, 9998), (300, 44)]
     for winner, copy in cases:
         wi = w.clone()
         wi[copy] = w[winner]
