@@ -10,9 +10,10 @@
 //
 // Three launches, no atomics, every reduction in a fixed order (run-to-run
 // bit-identical):
-//   sample_stats  one work-group per (row, 8192-logit chunk): the chunk's max
-//                 and sum of 2^((x - max) log2e / T) for both heads, 16-byte
-//                 nontemporal loads (HBM-bound: 8 bytes per logit pair);
+//   sample_stats  one work-group per (row, chunk of 4096 or 8192 logits):
+//                 the chunk's max and sum of 2^((x - max) log2e / T) for both
+//                 heads, 16-byte nontemporal loads (HBM-bound: 8 bytes per
+//                 logit pair);
 //   sample_resid  one work-group per (sequence, chunk): all 256 threads first
 //                 decide the sequence's rows (8 threads per row merge the
 //                 chunk pairs into the row normalisers; a wave ballot finds
@@ -20,7 +21,7 @@
 //                 chunk of the rejected row; chunk 0 stores the decision;
 //   sample_pick   one work-group per sequence: wave scan of the chunk sums
 //                 finds the chunk where the running sum passes
-//                 u_resample * total, a work-group scan of 32-logit runs
+//                 u_resample * total, a work-group scan of 16- or 32-logit runs
 //                 finds the run, one thread walks the run in index order.
 // The kernel boundaries order the passes; the workspace needs no
 // initialisation.
@@ -31,9 +32,14 @@ namespace orthrus {
 
 constexpr int kSampleThreads = 256;
 constexpr int kSampleWaves = kSampleThreads / kWave;
-constexpr int kSampleChunk = 8192;
+// Logits per work-group (a chunk).  A few rows (one or two sequences) take
+// 4096: twice the work-groups of 8192 on the chip, measured 24.1 -> 20.2 us
+// per call for one sequence of Qwen3 rows.  More rows take 8192, which fills
+// the chip already (16 sequences: 4096 measured the same or up to 5 %
+// slower).
+constexpr int kSmallChunk = 4096, kLargeChunk = 8192;
+static int sample_chunk(long rows) { return rows <= 64 ? kSmallChunk : kLargeChunk; }
 constexpr int kRowThreads = kSampleThreads / 32;  // threads per block row in the decision
-constexpr int kRun = kSampleChunk / kSampleThreads;
 
 struct SampleArgs {
   const float* ar;      // [B, K, V]
@@ -108,11 +114,9 @@ __device__ __forceinline__ void merge_wave(float& mp, float& sp, float& mq, floa
   dpp_merge<0x143, 0xc>(mq, sq, c);
 }
 
-constexpr int kVecPerThread = kSampleChunk / 4 / kSampleThreads;
-
 // [begin, end) of one row as a scalar head up to 16-byte alignment (< 4
-// logits), whole 16-byte vectors (at most kVecPerThread per thread) and a
-// scalar tail (< 4 logits)
+// logits), whole 16-byte vectors (at most CH / 4 / kSampleThreads per
+// thread for a chunk of CH logits) and a scalar tail (< 4 logits)
 struct Split16 {
   int head_end, nvec, tail;
 };
@@ -126,7 +130,9 @@ __device__ __forceinline__ Split16 split16(const float* x, int begin, int end) {
   return sp;
 }
 
+template <int CH>
 __global__ void __launch_bounds__(kSampleThreads) sample_stats(SampleArgs a) {
+  constexpr int kVecPerThread = CH / 4 / kSampleThreads;
   __shared__ f32x4 red[kSampleWaves];
   const int row = blockIdx.x / a.nchunks, ck = blockIdx.x % a.nchunks;
   const int tid = threadIdx.x;
@@ -316,7 +322,9 @@ __device__ __forceinline__ float chunk_mass(const SampleArgs& a, int b, int r, c
   return t[0] == -INFINITY ? 0.f : t[1] * ex2((t[0] - n[0]) * a.c) * n[1];
 }
 
+template <int CH>
 __global__ void __launch_bounds__(kSampleThreads) sample_pick(SampleArgs a) {
+  constexpr int kRun = CH / kSampleThreads;  // logits per thread
   __shared__ float wtot[kSampleWaves];
   __shared__ int wpick[kSampleWaves];
   __shared__ int chosen_s;
@@ -462,7 +470,8 @@ __global__ void __launch_bounds__(kSampleThreads) sample_pick(SampleArgs a) {
 }
 
 static size_t sample_workspace(int batch, int block_k, int vocab, int* nchunks, size_t* off) {
-  *nchunks = (vocab + kSampleChunk - 1) / kSampleChunk;
+  const int chunk = sample_chunk((long)batch * block_k);
+  *nchunks = (vocab + chunk - 1) / chunk;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   const size_t rows = (size_t)batch * block_k;
   off[0] = 0;                                             // stats
@@ -474,7 +483,7 @@ static size_t sample_workspace(int batch, int block_k, int vocab, int* nchunks, 
 
 static bool sample_shape_ok(int batch, int block_k, int vocab) {
   if (batch < 1 || block_k < 1 || block_k > 32 || vocab < 1) return false;
-  const long nchunks = (vocab + (long)kSampleChunk - 1) / kSampleChunk;
+  const long nchunks = (vocab + (long)kSmallChunk - 1) / kSmallChunk;  // at most
   return (long)batch * block_k * nchunks <= 0x7fffffffL;
 }
 
@@ -522,14 +531,20 @@ extern "C" orthrus_status orthrus_sample_accept(const float* ar_logits, const fl
   a.B = batch;
   a.K = block_k;
   a.V = vocab;
-  a.chunk = kSampleChunk;
+  a.chunk = sample_chunk((long)batch * block_k);
   a.nchunks = nchunks;
   hipStream_t s = (hipStream_t)stream;
-  hipLaunchKernelGGL(sample_stats, dim3((unsigned)((long)batch * block_k * nchunks)), dim3(kSampleThreads), 0, s,
-                     a);
+  const dim3 grid_stats((unsigned)((long)batch * block_k * nchunks));
+  if (a.chunk == kSmallChunk)
+    hipLaunchKernelGGL(sample_stats<kSmallChunk>, grid_stats, dim3(kSampleThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(sample_stats<kLargeChunk>, grid_stats, dim3(kSampleThreads), 0, s, a);
   if (hipGetLastError() != hipSuccess) return ORTHRUS_ERR_LAUNCH;
   hipLaunchKernelGGL(sample_resid, dim3((unsigned)((long)batch * nchunks)), dim3(kSampleThreads), 0, s, a);
   if (hipGetLastError() != hipSuccess) return ORTHRUS_ERR_LAUNCH;
-  hipLaunchKernelGGL(sample_pick, dim3((unsigned)batch), dim3(kSampleThreads), 0, s, a);
+  if (a.chunk == kSmallChunk)
+    hipLaunchKernelGGL(sample_pick<kSmallChunk>, dim3((unsigned)batch), dim3(kSampleThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL(sample_pick<kLargeChunk>, dim3((unsigned)batch), dim3(kSampleThreads), 0, s, a);
   return hipGetLastError() == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_LAUNCH;
 }

@@ -194,7 +194,8 @@ orthrus_status orthrus_block_attn_noalloc(const void* q, const void* k_cache, co
                                           const orthrus_attn_desc* desc, void* stream);
 
 /* Bytes of the workspace orthrus_greedy_accept needs (one 8-byte key per
- * (row, 8192-logit chunk)).  The workspace needs no initialisation. */
+ * (row, logit chunk); chunks of 4096 logits when batch * block_k <= 64,
+ * else 8192).  The workspace needs no initialisation. */
 size_t orthrus_greedy_accept_workspace_bytes(int32_t batch, int32_t block_k, int32_t vocab);
 
 /* Greedy consensus of one step (explainer §2.3).
@@ -212,9 +213,10 @@ orthrus_status orthrus_greedy_accept(const float* ar_logits, const int32_t* draf
                                      size_t workspace_bytes, void* stream);
 
 /* Bytes of the workspace orthrus_sample_accept needs (per row and
- * 8192-logit chunk one 16-byte pair of (max, sum) for each head, plus per
- * sequence the decision and one residual sum per chunk).  0 for an invalid
- * shape.  The workspace needs no initialisation. */
+ * logit chunk one 16-byte pair of (max, sum) for each head, plus per
+ * sequence the decision and one residual sum per chunk; chunks of 4096
+ * logits when batch * block_k <= 64, else 8192).  0 for an invalid shape.
+ * The workspace needs no initialisation. */
 size_t orthrus_sample_accept_workspace_bytes(int32_t batch, int32_t block_k, int32_t vocab);
 
 /* Lossless consensus at temperature T > 0: the stochastic form of the

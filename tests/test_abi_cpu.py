@@ -172,8 +172,11 @@ def test_accept_and_append_validation():
     assert lib.orthrus_greedy_accept(FAKE, FAKE, FAKE, FAKE, None, 1, 33, 100, FAKE, 1 << 20, None) == 2
     assert lib.orthrus_greedy_accept(FAKE, FAKE, FAKE, FAKE, None, 1, 32, 0, FAKE, 1 << 20, None) == 2
     need = lib.orthrus_greedy_accept_workspace_bytes(2, 32, 151936)
-    # one 8-byte key per (row, 8192-logit chunk): 64 rows x 19 chunks
-    assert need == 64 * 19 * 8
+    # one 8-byte key per (row, chunk): 64 rows take 4096-logit chunks (38),
+    # more rows 8192-logit ones (19)
+    assert need == 64 * 38 * 8
+    assert lib.orthrus_greedy_accept_workspace_bytes(16, 32, 151936) == 512 * 19 * 8
+    assert lib.orthrus_greedy_accept_workspace_bytes(1, 32, 1024) == 32 * 1 * 8
     assert lib.orthrus_greedy_accept(FAKE, FAKE, FAKE, FAKE, None, 2, 32, 151936, FAKE, need - 1, None) == 4
     assert lib.orthrus_greedy_accept(FAKE, FAKE, FAKE, FAKE, None, 2, 32, 151936, None, need, None) == 4
     d = good_desc()
@@ -211,7 +214,9 @@ def test_sample_accept_validation():
     # region rounded up to 256 bytes)
     up = lambda x: -(-x // 256) * 256
     need = lib.orthrus_sample_accept_workspace_bytes(2, 32, 151936)
-    assert need == up(64 * 19 * 16) + up(2 * 16) + up(2 * 4) + up(2 * 19 * 4)
+    assert need == up(64 * 38 * 16) + up(2 * 16) + up(2 * 4) + up(2 * 38 * 4)   # 4096-logit chunks
+    need16 = lib.orthrus_sample_accept_workspace_bytes(16, 32, 151936)          # 8192-logit chunks
+    assert need16 == up(512 * 19 * 16) + up(16 * 16) + up(16 * 4) + up(16 * 19 * 4)
     assert lib.orthrus_sample_accept_workspace_bytes(1, 33, 100) == 0
     assert call(wsb=need - 1) == 4
     assert call(ws=None, wsb=need) == 4
