@@ -4,11 +4,12 @@
 // then the longest prefix of drafts that equals those tokens.
 //
 // Two launches.  argmax_chunks: each work-group scans one contiguous chunk
-// (4096 or 8192 logits) of one logits row with 16-byte nontemporal loads (the scan is HBM-bound: 4
-// bytes per logit) and reduces (value, index) pairs across the wave with xor
-// shuffles and across waves in LDS into one 64-bit key (order-preserving
-// value bits << 32 | ~index: the larger key is the larger value, then the
-// lower index), stored to the workspace.  accept_rows: one work-group per
+// (4096 or 8192 logits) of one logits row with 16-byte nontemporal loads
+// (the scan is HBM-bound: 4 bytes per logit) and reduces its (value,
+// index) candidates, as 64-bit keys (order-preserving value bits << 32 |
+// ~index: the larger key is the larger value, then the lower index), with a
+// DPP max-scan across the wave and a max over the waves in LDS; the chunk's
+// key goes to the workspace.  accept_rows: one work-group per
 // sequence reduces each row's chunk keys to the greedy token, then compares
 // the K tokens with the drafts (wave ballot: first mismatch) and writes
 // accept_len / next_token / ar_tokens.  The kernel boundary orders the two
