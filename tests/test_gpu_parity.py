@@ -529,6 +529,36 @@ def test_accept_unaligned_vocab(V):
     check_accept(x, drafts)
 
 
+def test_accept_chunk_sizes_agree():
+    """Calls of at most 64 rows scan 4096-logit chunks, larger calls 8192-logit
+    ones.  The same rows give the same greedy tokens, accept lengths and next
+    tokens either way, equal to the oracle's, with ties planted across a
+    4096-logit boundary inside one 8192-logit chunk and across an 8192-logit
+    boundary (lowest index wins)."""
+    say("accept chunk sizes")
+    from diffusion_drafted_verification_amd import orthrus as ob
+    d = dev()
+    V = 151936
+    x = torch.randn(3, 32, V, generator=torch.Generator().manual_seed(7)) * 4
+    x[0, 0, [12288, 4096]] = 1e3        # chunk starts: 4096 wins
+    x[0, 1, [4096, 4095]] = 1e3         # across a 4096 boundary: 4095
+    x[1, 2, [8192, 8191]] = 1e3         # across an 8192 boundary: 8191
+    x[1, 3, [V - 1, 147456]] = 1e3      # in the last chunks: 147456
+    g = torch.from_numpy(O.greedy_argmax(x.numpy())).int()
+    assert g[0, 0] == 4096 and g[0, 1] == 4095 and g[1, 2] == 8191 and g[1, 3] == 147456
+    dr = g.clone()
+    dr[0, 20] += 1
+    dr[1, 3] += 1
+    dr[2, 0] += 1
+    ref = O.greedy_accept(x.numpy(), dr.numpy())
+    small = ob.greedy_accept(x[:2].to(d), dr[:2].to(d))     # 64 rows: 4096-logit chunks
+    large = ob.greedy_accept(x.to(d), dr.to(d))             # 96 rows: 8192-logit chunks
+    for out, n in ((small, 2), (large, 3)):
+        acc, nxt, tok = (t.cpu().numpy() for t in out)
+        assert np.array_equal(tok, ref[2][:n]) and np.array_equal(acc, ref[0][:n])
+        assert np.array_equal(nxt, ref[1][:n])
+
+
 def test_accept_workspace_reused_across_shapes():
     """A workspace used by a large call serves calls of other shapes, with
     any initial contents (no state survives a call)."""
