@@ -964,8 +964,15 @@ struct DmaPlan {
   }
 };
 
+// The leading scalar arguments repeat the fields the prologue's first loads
+// depend on (context lengths, page table and the work-group decomposition).
+// Scalar kernel arguments can be preloaded into SGPRs when the wave starts
+// (the build asks for the first six), so the first context-length and
+// page-id loads do not wait for a kernel-argument load.
 template <int D, int G, int MODE, bool BAL>
-__global__ void __launch_bounds__(2 * kWave * G) attn_stream(AttnArgs a) {
+__global__ void __launch_bounds__(2 * kWave * G)
+    attn_stream(const int32_t* pre_ctx, const int32_t* pre_pt, int pre_B, int pre_Hkv, int pre_split,
+                int pre_maxpages, AttnArgs a) {
   typedef StreamLayout<D> Lay;
   typedef DmaPlan<D, 2 * G> Plan;
   constexpr int NW = 2 * G;
@@ -980,17 +987,19 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_stream(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char st3[Lay::STAGE];
   __shared__ __attribute__((aligned(16))) int pages[kMaxSplit / kPage];
 
-  const int BH = a.B * a.Hkv;
+  // G = 2 measured faster reading these from the argument struct
+  const int arg_B = G == 4 ? pre_B : a.B, arg_Hkv = G == 4 ? pre_Hkv : a.Hkv;
+  const int BH = arg_B * arg_Hkv;
   const int bg = blockIdx.x % BH;
-  const int g = bg % a.Hkv;
+  const int g = bg % arg_Hkv;
   // the fixed split's unit: sequences in reverse order, so where later
   // sequences carry longer contexts (the chunks of a prompt prefill) the
   // longest work-groups start first.  Under the balanced split it is the unit
   // of a batch whose lengths all equal max_ctx: its page ids are loaded
   // before the lengths are known and kept when the guess holds.
   int s = blockIdx.x / BH;
-  int b = a.B - 1 - bg / a.Hkv;
-  int split = a.split;
+  int b = arg_B - 1 - bg / arg_Hkv;
+  int split = G == 4 ? pre_split : a.split;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave), lane = tid % kWave;
   const int i = lane & 31, hi = lane >> 5;
@@ -1006,14 +1015,15 @@ __global__ void __launch_bounds__(2 * kWave * G) attn_stream(AttnArgs a) {
   // length loads are consumed before the first DMA).
   typedef const __attribute__((address_space(4))) int cint;
   constexpr int NPRO = (kRing - 1) * kTile / kPage;  // page ids of the prologue stages
-  int L = BAL ? 0 : ((cint*)a.ctx_lens)[b];  // balanced: every length is read below
+  int L = BAL ? 0 : ((cint*)(G == 4 ? pre_ctx : a.ctx_lens))[b];  // balanced: every length is read below
   int page_base = (s * split) >> 4;
   bool ids_ok;
   int pid[NPRO];  // raw; checked where used
   auto load_ids = [&]() {
-    ids_ok = page_base + NPRO <= a.max_pages;
+    const int arg_maxpages = G == 4 ? pre_maxpages : a.max_pages;
+    ids_ok = page_base + NPRO <= arg_maxpages;
     if (ids_ok) {
-      cint* row = (cint*)(a.page_table + (size_t)b * a.max_pages + page_base);
+      cint* row = (cint*)((G == 4 ? pre_pt : a.page_table) + (size_t)b * arg_maxpages + page_base);
 #pragma unroll
       for (int j = 0; j < NPRO; ++j) pid[j] = row[j];
     } else {
@@ -1766,11 +1776,15 @@ static hipError_t launch_attn(const AttnArgs& a, int mode, hipStream_t stream) {
   if constexpr (stream_path) {
     const dim3 blk(2 * kWave * G);
     if (mode == ORTHRUS_DIFF_BIDIR) {
-      if (a.bal) hipLaunchKernelGGL((attn_stream<D, G, ORTHRUS_DIFF_BIDIR, true>), dim3(grid), blk, 0, stream, a);
-      else hipLaunchKernelGGL((attn_stream<D, G, ORTHRUS_DIFF_BIDIR, false>), dim3(grid), blk, 0, stream, a);
+      if (a.bal) hipLaunchKernelGGL((attn_stream<D, G, ORTHRUS_DIFF_BIDIR, true>), dim3(grid), blk, 0, stream, a.ctx_lens,
+                           a.page_table, a.B, a.Hkv, a.split, a.max_pages, a);
+      else hipLaunchKernelGGL((attn_stream<D, G, ORTHRUS_DIFF_BIDIR, false>), dim3(grid), blk, 0, stream, a.ctx_lens,
+                           a.page_table, a.B, a.Hkv, a.split, a.max_pages, a);
     } else {
-      if (a.bal) hipLaunchKernelGGL((attn_stream<D, G, ORTHRUS_AR_CAUSAL, true>), dim3(grid), blk, 0, stream, a);
-      else hipLaunchKernelGGL((attn_stream<D, G, ORTHRUS_AR_CAUSAL, false>), dim3(grid), blk, 0, stream, a);
+      if (a.bal) hipLaunchKernelGGL((attn_stream<D, G, ORTHRUS_AR_CAUSAL, true>), dim3(grid), blk, 0, stream, a.ctx_lens,
+                           a.page_table, a.B, a.Hkv, a.split, a.max_pages, a);
+      else hipLaunchKernelGGL((attn_stream<D, G, ORTHRUS_AR_CAUSAL, false>), dim3(grid), blk, 0, stream, a.ctx_lens,
+                           a.page_table, a.B, a.Hkv, a.split, a.max_pages, a);
     }
   } else {
     if (mode == ORTHRUS_DIFF_BIDIR)
