@@ -99,11 +99,12 @@ def build_sanitized(verbose=True, force=False):
     return SANITIZE_LIB
 
 
-# Per-source flags.  block_attn.hip: preload the streaming attention
-# kernel's six leading scalar arguments (context lengths, page table,
-# decomposition) into SGPRs at wave start, so its first loads do not wait for
-# a kernel-argument load (B1 decode call 17.9 -> 17.5 us).
-SOURCE_FLAGS = {"block_attn.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=6"]}
+# Per-source flags.  block_attn.hip: preload the leading scalar arguments of
+# the streaming attention and combine kernels (context lengths, page table,
+# partial buffers, decomposition) into SGPRs at wave start, so their first
+# loads do not wait for a kernel-argument load (B1 decode call 17.9 -> 17.4
+# us with the attention kernel's six).
+SOURCE_FLAGS = {"block_attn.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=10"]}
 
 
 def _compile(src):

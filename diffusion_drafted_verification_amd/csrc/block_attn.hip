@@ -717,19 +717,23 @@ __global__ void __launch_bounds__(256) attn_combine(AttnArgs a) {
 // 64 / (SG D/8) consecutive rows of one (b, g); block id = chunk * (B Hkv) +
 // b Hkv + g as for attn_combine.
 template <int D, int SG, int SPL, bool BAL>
-__global__ void __launch_bounds__(256) attn_combine_bf16(AttnArgs a) {
+__global__ void __launch_bounds__(256)
+    attn_combine_bf16(const int32_t* pre_ctx, const float2* pre_ml, const char* pre_p, int pre_B, int pre_Hkv,
+                      int pre_Hq, int pre_K, int pre_maxctx, int pre_split, int pre_smax, AttnArgs a) {
+  // the leading scalar arguments repeat the fields the first loads depend
+  // on, preloaded into SGPRs when the wave starts (as for attn_stream)
   constexpr int C = D / 8;               // lanes per row and split group
   constexpr int RPW = kWave / (C * SG);  // rows per wave
   constexpr int RPB = 4 * RPW;           // rows per work-group
   static_assert(RPW >= 1, "a row fits one wave");
-  const int BH = a.B * a.Hkv, G = a.Hq / a.Hkv;
+  const int BH = pre_B * pre_Hkv, G = pre_Hq / pre_Hkv;
   const int bg = blockIdx.x % BH, chunk = blockIdx.x / BH;
-  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const int b = bg / pre_Hkv, g = bg % pre_Hkv;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int rl = chunk * RPB + wave * RPW + lane / (C * SG);  // row within (b, g): w * K + i
   const int sg = (lane / C) % SG, c = lane % C;
-  const bool live = rl < G * a.K;
-  const int w = live ? rl / a.K : 0, i = live ? rl % a.K : 0;
+  const bool live = rl < G * pre_K;
+  const int w = live ? rl / pre_K : 0, i = live ? rl % pre_K : 0;
   const int h = g * G + w;
   int S_b;
   size_t base, sstride;  // row of split 0, rows between splits
@@ -741,10 +745,10 @@ __global__ void __launch_bounds__(256) attn_combine_bf16(AttnArgs a) {
     base = ((size_t)(g * a.U + P) * G + w) * kRows + i;
     sstride = (size_t)G * kRows;
   } else {
-    int L = a.ctx_lens[b];
-    L = L < 0 ? 0 : (L > a.max_ctx ? a.max_ctx : L);
-    S_b = L > 0 ? (L + a.split - 1) / a.split : 1;
-    base = (size_t)(b * a.Hq + h) * a.s_max * kRows + i;
+    int L = pre_ctx[b];
+    L = L < 0 ? 0 : (L > pre_maxctx ? pre_maxctx : L);
+    S_b = L > 0 ? (L + pre_split - 1) / pre_split : 1;
+    base = (size_t)(b * pre_Hq + h) * pre_smax * kRows + i;
     sstride = kRows;
   }
   if (S_b <= 1) return;  // uniform over the work-group
@@ -760,8 +764,8 @@ __global__ void __launch_bounds__(256) attn_combine_bf16(AttnArgs a) {
     for (int j = 0; j < SPL; ++j) {
       const int sp = s0 + SG * j;
       const size_t r = base + (size_t)(sp < S_b ? sp : 0) * sstride;
-      ml[j] = a.ws_ml[r];
-      x[j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(a.ws_p) + r * D * 2 + c * 16);
+      ml[j] = pre_ml[r];
+      x[j] = *reinterpret_cast<const u32x4*>(pre_p + r * D * 2 + c * 16);
       if (sp >= S_b) ml[j].x = -INFINITY;
     }
     float mnew = M;
@@ -807,7 +811,7 @@ __global__ void __launch_bounds__(256) attn_combine_bf16(AttnArgs a) {
     const bf16 lo = (bf16)(acc[2 * k] * inv), hi2 = (bf16)(acc[2 * k + 1] * inv);
     y[k] = (uint32_t)__builtin_bit_cast(uint16_t, lo) | ((uint32_t)__builtin_bit_cast(uint16_t, hi2) << 16);
   }
-  *reinterpret_cast<u32x4*>(a.out + ((size_t)(b * a.K + i) * a.Hq + h) * D * 2 + c * 16) = y;
+  *reinterpret_cast<u32x4*>(a.out + ((size_t)(b * pre_K + i) * pre_Hq + h) * D * 2 + c * 16) = y;
 }
 
 template <typename T, int D, bool NORM>
@@ -819,10 +823,13 @@ static hipError_t launch_combine(const AttnArgs& a, hipStream_t stream) {
       constexpr int SG = decltype(sg_tag)::value;
       constexpr int RPB = 4 * (kWave / ((D / 8) * SG));
       const int chunks = (rows + RPB - 1) / RPB;
+      const char* p = reinterpret_cast<const char*>(a.ws_p);
       if (a.bal)
-        hipLaunchKernelGGL((attn_combine_bf16<D, SG, 8, true>), dim3(chunks * a.B * a.Hkv), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((attn_combine_bf16<D, SG, 8, true>), dim3(chunks * a.B * a.Hkv), dim3(256), 0, stream,
+                           a.ctx_lens, a.ws_ml, p, a.B, a.Hkv, a.Hq, a.K, a.max_ctx, a.split, a.s_max, a);
       else
-        hipLaunchKernelGGL((attn_combine_bf16<D, SG, 8, false>), dim3(chunks * a.B * a.Hkv), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((attn_combine_bf16<D, SG, 8, false>), dim3(chunks * a.B * a.Hkv), dim3(256), 0, stream,
+                           a.ctx_lens, a.ws_ml, p, a.B, a.Hkv, a.Hq, a.K, a.max_ctx, a.split, a.s_max, a);
     };
     if (a.s_hint > 16) go2(std::integral_constant<int, 4>());
     else if (a.s_hint > 8) go2(std::integral_constant<int, 2>());
