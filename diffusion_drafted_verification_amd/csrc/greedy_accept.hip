@@ -75,15 +75,19 @@ __device__ __forceinline__ unsigned long long cand_key(float v, int i) {
   return ((unsigned long long)order_bits(v) << 32) | (unsigned long long)(0xffffffffu - (uint32_t)i);
 }
 
-__global__ void __launch_bounds__(kArgmaxThreads) argmax_chunks(AcceptArgs a) {
+// The leading scalar arguments repeat the fields the first loads depend on;
+// they are preloaded into SGPRs when a wave starts (the build asks for the
+// first four), so the scan does not wait for a kernel-argument load.
+__global__ void __launch_bounds__(kArgmaxThreads)
+    argmax_chunks(const float* pre_logits, int pre_V, int pre_chunk, int pre_nchunks, AcceptArgs a) {
   __shared__ unsigned long long wkey[kArgmaxThreads / kWave];
 
-  const int row = blockIdx.x / a.nchunks;  // b * K + i
-  const int ck = blockIdx.x % a.nchunks;
+  const int row = blockIdx.x / pre_nchunks;  // b * K + i
+  const int ck = blockIdx.x % pre_nchunks;
   const int tid = threadIdx.x;
-  const int begin = ck * a.chunk;
-  const int end = min(begin + a.chunk, a.V);
-  const float* x = a.logits + (size_t)row * a.V;
+  const int begin = ck * pre_chunk;
+  const int end = min(begin + pre_chunk, pre_V);
+  const float* x = pre_logits + (size_t)row * pre_V;
 
   float bv = -INFINITY;
   int bi = 0x7fffffff;
@@ -113,7 +117,7 @@ __global__ void __launch_bounds__(kArgmaxThreads) argmax_chunks(AcceptArgs a) {
     unsigned long long k = wkey[0];
 #pragma unroll
     for (int w = 1; w < kArgmaxThreads / kWave; ++w) k = wkey[w] > k ? wkey[w] : k;
-    a.part[(size_t)row * a.nchunks + ck] = k;
+    a.part[(size_t)row * pre_nchunks + ck] = k;
   }
 }
 
@@ -124,7 +128,8 @@ constexpr int kAcceptThreads = 256;
 constexpr int kAcceptWaves = kAcceptThreads / kWave;
 constexpr int kRowsPerWave = (32 + kAcceptWaves - 1) / kAcceptWaves;
 
-__global__ void __launch_bounds__(kAcceptThreads) accept_rows(AcceptArgs a) {
+__global__ void __launch_bounds__(kAcceptThreads)
+    accept_rows(const unsigned long long* pre_part, int pre_K, int pre_nchunks, AcceptArgs a) {
   __shared__ int32_t gtok[32];
   const int b = blockIdx.x;
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -132,14 +137,14 @@ __global__ void __launch_bounds__(kAcceptThreads) accept_rows(AcceptArgs a) {
 #pragma unroll
   for (int j = 0; j < kRowsPerWave; ++j) {
     const int i = wave + kAcceptWaves * j;
-    best[j] = (i < a.K && lane < a.nchunks) ? a.part[(size_t)(b * a.K + i) * a.nchunks + lane] : 0ull;
+    best[j] = (i < pre_K && lane < pre_nchunks) ? pre_part[(size_t)(b * pre_K + i) * pre_nchunks + lane] : 0ull;
   }
 #pragma unroll
   for (int j = 0; j < kRowsPerWave; ++j) {
     const int i = wave + kAcceptWaves * j;
-    if (i >= a.K) break;
-    const unsigned long long* keys = a.part + (size_t)(b * a.K + i) * a.nchunks;
-    for (int q = lane + kWave; q < a.nchunks; q += kWave) best[j] = keys[q] > best[j] ? keys[q] : best[j];
+    if (i >= pre_K) break;
+    const unsigned long long* keys = pre_part + (size_t)(b * pre_K + i) * pre_nchunks;
+    for (int q = lane + kWave; q < pre_nchunks; q += kWave) best[j] = keys[q] > best[j] ? keys[q] : best[j];
     const unsigned long long m = wave_max_u64(best[j]);
     if (lane == 0) gtok[i] = (int32_t)(0xffffffffu - (uint32_t)(m & 0xffffffffu));
   }
@@ -147,14 +152,14 @@ __global__ void __launch_bounds__(kAcceptThreads) accept_rows(AcceptArgs a) {
   if (wave != 0) return;
   int32_t gt = 0;
   bool miss = false;
-  if (lane < a.K) {
+  if (lane < pre_K) {
     gt = gtok[lane];
-    miss = a.drafts[b * a.K + lane] != gt;
-    if (a.ar_tokens) a.ar_tokens[b * a.K + lane] = gt;
+    miss = a.drafts[b * pre_K + lane] != gt;
+    if (a.ar_tokens) a.ar_tokens[b * pre_K + lane] = gt;
   }
   const unsigned long long mask = __ballot(miss);
-  const int acc = mask ? (__ffsll((long long)mask) - 1) : a.K;
-  const int last = acc < a.K ? acc : a.K - 1;
+  const int acc = mask ? (__ffsll((long long)mask) - 1) : pre_K;
+  const int last = acc < pre_K ? acc : pre_K - 1;
   const int nxt = __shfl(gt, last, kWave);
   if (lane == 0) {
     a.accept_len[b] = acc;
@@ -214,8 +219,9 @@ extern "C" orthrus_status orthrus_greedy_accept(const float* ar_logits, const in
   a.chunk = chunk;
   a.nchunks = nchunks;
   hipStream_t s = (hipStream_t)stream;
-  hipLaunchKernelGGL(argmax_chunks, dim3((unsigned)grid), dim3(kArgmaxThreads), 0, s, a);
+  hipLaunchKernelGGL(argmax_chunks, dim3((unsigned)grid), dim3(kArgmaxThreads), 0, s, a.logits, a.V, a.chunk,
+                     a.nchunks, a);
   if (hipGetLastError() != hipSuccess) return ORTHRUS_ERR_LAUNCH;
-  hipLaunchKernelGGL(accept_rows, dim3((unsigned)batch), dim3(kAcceptThreads), 0, s, a);
+  hipLaunchKernelGGL(accept_rows, dim3((unsigned)batch), dim3(kAcceptThreads), 0, s, a.part, a.K, a.nchunks, a);
   return hipGetLastError() == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_LAUNCH;
 }
