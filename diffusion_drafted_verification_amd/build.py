@@ -105,7 +105,8 @@ def build_sanitized(verbose=True, force=False):
 # loads do not wait for a kernel-argument load (B1 decode call 17.9 -> 17.4
 # us with the attention kernel's six).
 SOURCE_FLAGS = {"block_attn.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=10"],
-                "greedy_accept.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=4"]}
+                "greedy_accept.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=4"],
+                "sample_accept.hip": ["-mllvm", "-amdgpu-kernarg-preload-count=7"]}
 
 
 def _compile(src):

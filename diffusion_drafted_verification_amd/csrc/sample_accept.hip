@@ -130,15 +130,19 @@ __device__ __forceinline__ Split16 split16(const float* x, int begin, int end) {
   return sp;
 }
 
+// Each kernel's leading scalar arguments repeat the fields its first loads
+// depend on; they are preloaded into SGPRs when a wave starts, so the loads
+// do not wait for a kernel-argument load.
 template <int CH>
-__global__ void __launch_bounds__(kSampleThreads) sample_stats(SampleArgs a) {
+__global__ void __launch_bounds__(kSampleThreads)
+    sample_stats(const float* pre_ar, const float* pre_dr, int pre_V, int pre_nchunks, SampleArgs a) {
   constexpr int kVecPerThread = CH / 4 / kSampleThreads;
   __shared__ f32x4 red[kSampleWaves];
-  const int row = blockIdx.x / a.nchunks, ck = blockIdx.x % a.nchunks;
+  const int row = blockIdx.x / pre_nchunks, ck = blockIdx.x % pre_nchunks;
   const int tid = threadIdx.x;
-  const int begin = ck * a.chunk, end = min(begin + a.chunk, a.V);
-  const float* xp = a.ar + (size_t)row * a.V;
-  const float* xq = a.dr + (size_t)row * a.V;
+  const int begin = ck * a.chunk, end = min(begin + a.chunk, pre_V);
+  const float* xp = pre_ar + (size_t)row * pre_V;
+  const float* xq = pre_dr + (size_t)row * pre_V;
   const Split16 sp = split16(xp, begin, end), sq_ = split16(xq, begin, end);
   const f32x4* pv = reinterpret_cast<const f32x4*>(xp + sp.head_end);
   const f32x4* qv = reinterpret_cast<const f32x4*>(xq + sq_.head_end);
@@ -172,7 +176,7 @@ __global__ void __launch_bounds__(kSampleThreads) sample_stats(SampleArgs a) {
       ms_merge(mp, sp_, red[w][0], red[w][1], a.c);
       ms_merge(mq, sq, red[w][2], red[w][3], a.c);
     }
-    a.stats[(size_t)row * a.nchunks + ck] = f32x4{mp, sp_, mq, sq};
+    a.stats[(size_t)row * pre_nchunks + ck] = f32x4{mp, sp_, mq, sq};
   }
 }
 
@@ -226,35 +230,37 @@ __device__ __forceinline__ float wave_sum(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wave_scan(x, 0)), kWave - 1));
 }
 
-__global__ void __launch_bounds__(kSampleThreads) sample_resid(SampleArgs a) {
+__global__ void __launch_bounds__(kSampleThreads)
+    sample_resid(const f32x4* pre_stats, const int32_t* pre_drafts, const float* pre_ar, const float* pre_dr,
+                 int pre_K, int pre_nchunks, int pre_V, SampleArgs a) {
   __shared__ f32x4 nrm[32];
   __shared__ int ok[32];
   __shared__ int rej_s;
   __shared__ float red[kSampleWaves];
-  const int b = blockIdx.x / a.nchunks, ck = blockIdx.x % a.nchunks;
+  const int b = blockIdx.x / pre_nchunks, ck = blockIdx.x % pre_nchunks;
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
 
   // decision: kRowThreads threads per row merge its chunk pairs (chunks
   // sub, sub + 8, ...), a DPP merge over the 8 gives the normalisers
   {
     const int i = tid / kRowThreads, sub = tid % kRowThreads;
-    const bool live = i < a.K;
-    const int row = b * a.K + i;
+    const bool live = i < pre_K;
+    const int row = b * pre_K + i;
     int x = 0;
     float xa = 0.f, xd = 0.f;
     bool in = false;
     if (live && sub == 0) {
-      x = a.drafts[row];
-      in = x >= 0 && x < a.V;  // a draft outside the vocabulary is rejected
+      x = pre_drafts[row];
+      in = x >= 0 && x < pre_V;  // a draft outside the vocabulary is rejected
       if (in) {
-        xa = a.ar[(size_t)row * a.V + x];
-        xd = a.dr[(size_t)row * a.V + x];
+        xa = pre_ar[(size_t)row * pre_V + x];
+        xd = pre_dr[(size_t)row * pre_V + x];
       }
     }
     float mp = -INFINITY, sp = 0.f, mq = -INFINITY, sq = 0.f;
     if (live)
-      for (int q = sub; q < a.nchunks; q += kRowThreads) {
-        const f32x4 t = a.stats[(size_t)row * a.nchunks + q];
+      for (int q = sub; q < pre_nchunks; q += kRowThreads) {
+        const f32x4 t = pre_stats[(size_t)row * pre_nchunks + q];
         ms_merge(mp, sp, t[0], t[1], a.c);
         ms_merge(mq, sq, t[2], t[3], a.c);
       }
@@ -270,24 +276,24 @@ __global__ void __launch_bounds__(kSampleThreads) sample_resid(SampleArgs a) {
   }
   __syncthreads();
   if (wave == 0) {
-    const unsigned long long mask = __ballot(lane < a.K && !ok[lane]);
-    if (lane == 0) rej_s = mask ? (__ffsll((long long)mask) - 1) : a.K;
+    const unsigned long long mask = __ballot(lane < pre_K && !ok[lane]);
+    if (lane == 0) rej_s = mask ? (__ffsll((long long)mask) - 1) : pre_K;
   }
   __syncthreads();
   const int r = rej_s;
   if (ck == 0 && tid == 0) {
     a.accept_len[b] = r;
     a.rej[b] = r;
-    if (r == a.K) a.next_token[b] = a.drafts[b * a.K + a.K - 1];
+    if (r == pre_K) a.next_token[b] = pre_drafts[b * pre_K + pre_K - 1];
     else a.rowstat[b] = nrm[r];
   }
-  if (r == a.K) return;  // uniform: every draft accepted
+  if (r == pre_K) return;  // uniform: every draft accepted
 
   const f32x4 n = nrm[r];
-  const size_t off = (size_t)(b * a.K + r) * a.V;
-  const float* xp = a.ar + off;
-  const float* xq = a.dr + off;
-  const int begin = ck * a.chunk, end = min(begin + a.chunk, a.V);
+  const size_t off = (size_t)(b * pre_K + r) * pre_V;
+  const float* xp = pre_ar + off;
+  const float* xq = pre_dr + off;
+  const int begin = ck * a.chunk, end = min(begin + a.chunk, pre_V);
   float s = 0.f;
   if (((reinterpret_cast<uintptr_t>(xp) ^ reinterpret_cast<uintptr_t>(xq)) & 15) == 0) {
     const int mis = (int)((reinterpret_cast<uintptr_t>(xp + begin) >> 2) & 3);
@@ -309,7 +315,7 @@ __global__ void __launch_bounds__(kSampleThreads) sample_resid(SampleArgs a) {
     float t = red[0];
 #pragma unroll
     for (int w = 1; w < kSampleWaves; ++w) t += red[w];
-    a.rsum[(size_t)b * a.nchunks + ck] = t;
+    a.rsum[(size_t)b * pre_nchunks + ck] = t;
   }
 }
 
@@ -323,7 +329,9 @@ __device__ __forceinline__ float chunk_mass(const SampleArgs& a, int b, int r, c
 }
 
 template <int CH>
-__global__ void __launch_bounds__(kSampleThreads) sample_pick(SampleArgs a) {
+__global__ void __launch_bounds__(kSampleThreads)
+    sample_pick(const int32_t* pre_rej, const f32x4* pre_rowstat, const float* pre_rsum, const float* pre_ures,
+                int pre_nchunks, SampleArgs a) {
   constexpr int kRun = CH / kSampleThreads;  // logits per thread
   __shared__ float wtot[kSampleWaves];
   __shared__ int wpick[kSampleWaves];
@@ -333,22 +341,22 @@ __global__ void __launch_bounds__(kSampleThreads) sample_pick(SampleArgs a) {
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
   // the decision, the normalisers and the first 64 chunk sums are loaded
   // together (rowstat is only used when a row was rejected)
-  const int r = a.rej[b];
-  const f32x4 n = a.rowstat[b];
-  float cs0 = (wave == 0 && lane < a.nchunks) ? a.rsum[(size_t)b * a.nchunks + lane] : 0.f;
-  const float u = a.u_res[b];
+  const int r = pre_rej[b];
+  const f32x4 n = pre_rowstat[b];
+  float cs0 = (wave == 0 && lane < pre_nchunks) ? pre_rsum[(size_t)b * pre_nchunks + lane] : 0.f;
+  const float u = pre_ures[b];
   if (r >= a.K) return;  // every draft accepted: next_token is already written
 
   if (wave == 0) {
     // total residual mass (lane-strided, then a wave sum)
     float t = cs0;
-    for (int k = lane + kWave; k < a.nchunks; k += kWave) t += a.rsum[(size_t)b * a.nchunks + k];
+    for (int k = lane + kWave; k < pre_nchunks; k += kWave) t += pre_rsum[(size_t)b * pre_nchunks + k];
     t = wave_sum(t);
     const bool use_p = !(t > 0.f);
     if (use_p) {
-      cs0 = lane < a.nchunks ? chunk_mass(a, b, r, n, true, lane) : 0.f;
+      cs0 = lane < pre_nchunks ? chunk_mass(a, b, r, n, true, lane) : 0.f;
       t = cs0;
-      for (int k = lane + kWave; k < a.nchunks; k += kWave) t += chunk_mass(a, b, r, n, true, k);
+      for (int k = lane + kWave; k < pre_nchunks; k += kWave) t += chunk_mass(a, b, r, n, true, k);
       t = wave_sum(t);
     }
     const float target = u * t;
@@ -357,9 +365,9 @@ __global__ void __launch_bounds__(kSampleThreads) sample_pick(SampleArgs a) {
     float carry = 0.f;
     int ck = -1, last = -1;
     float run_ck = 0.f, run_last = 0.f;
-    for (int k0 = 0; k0 < a.nchunks && ck < 0; k0 += kWave) {
+    for (int k0 = 0; k0 < pre_nchunks && ck < 0; k0 += kWave) {
       const int k = k0 + lane;
-      const float cs = k0 == 0 ? cs0 : (k < a.nchunks ? chunk_mass(a, b, r, n, use_p, k) : 0.f);
+      const float cs = k0 == 0 ? cs0 : (k < pre_nchunks ? chunk_mass(a, b, r, n, use_p, k) : 0.f);
       const float incl = carry + wave_scan(cs, lane);
       const unsigned long long hit = __ballot(cs > 0.f && incl > target);
       const unsigned long long mass = __ballot(cs > 0.f);
@@ -536,15 +544,20 @@ extern "C" orthrus_status orthrus_sample_accept(const float* ar_logits, const fl
   hipStream_t s = (hipStream_t)stream;
   const dim3 grid_stats((unsigned)((long)batch * block_k * nchunks));
   if (a.chunk == kSmallChunk)
-    hipLaunchKernelGGL(sample_stats<kSmallChunk>, grid_stats, dim3(kSampleThreads), 0, s, a);
+    hipLaunchKernelGGL(sample_stats<kSmallChunk>, grid_stats, dim3(kSampleThreads), 0, s, a.ar, a.dr, a.V,
+                       a.nchunks, a);
   else
-    hipLaunchKernelGGL(sample_stats<kLargeChunk>, grid_stats, dim3(kSampleThreads), 0, s, a);
+    hipLaunchKernelGGL(sample_stats<kLargeChunk>, grid_stats, dim3(kSampleThreads), 0, s, a.ar, a.dr, a.V,
+                       a.nchunks, a);
   if (hipGetLastError() != hipSuccess) return ORTHRUS_ERR_LAUNCH;
-  hipLaunchKernelGGL(sample_resid, dim3((unsigned)((long)batch * nchunks)), dim3(kSampleThreads), 0, s, a);
+  hipLaunchKernelGGL(sample_resid, dim3((unsigned)((long)batch * nchunks)), dim3(kSampleThreads), 0, s, a.stats,
+                     a.drafts, a.ar, a.dr, a.K, a.nchunks, a.V, a);
   if (hipGetLastError() != hipSuccess) return ORTHRUS_ERR_LAUNCH;
   if (a.chunk == kSmallChunk)
-    hipLaunchKernelGGL(sample_pick<kSmallChunk>, dim3((unsigned)batch), dim3(kSampleThreads), 0, s, a);
+    hipLaunchKernelGGL(sample_pick<kSmallChunk>, dim3((unsigned)batch), dim3(kSampleThreads), 0, s, a.rej, a.rowstat,
+                       a.rsum, a.u_res, a.nchunks, a);
   else
-    hipLaunchKernelGGL(sample_pick<kLargeChunk>, dim3((unsigned)batch), dim3(kSampleThreads), 0, s, a);
+    hipLaunchKernelGGL(sample_pick<kLargeChunk>, dim3((unsigned)batch), dim3(kSampleThreads), 0, s, a.rej, a.rowstat,
+                       a.rsum, a.u_res, a.nchunks, a);
   return hipGetLastError() == hipSuccess ? ORTHRUS_OK : ORTHRUS_ERR_LAUNCH;
 }
